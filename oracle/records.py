@@ -1,0 +1,157 @@
+"""The int8 and q4_0 vector records (oracle).
+
+Strata page, section "三种 KV 格式横向对比": int8 (the default, 1,056 B per
+token per layer for the K and V of two KV heads, i.e. 264 B per 256-element
+vector), q4_0 (576 B, i.e. 144 B per vector, after the Walsh-Hadamard
+rotation of section "4-bit KV 缓存：先旋转，再压到 4-bit") and k8v4 (K kept in
+8 bits, V rotated and stored in 4 bits, 23% less than int8, i.e. 816 B).
+
+The pages give the sizes and the rotation, not the rounding rules. Readings
+taken here (each is a plain choice consistent with the sizes):
+
+int8 record, per group of 64 elements (4 groups, 4 fp16 scales + 256 codes):
+  a = max |x_j|;  d = fp16 round-to-nearest-even of the exact quotient a/127;
+  d == 0 -> all codes 0; else c_j = clamp(round_half_away_from_zero(x_j / d),
+  -127, 127), computed from the stored d. Dequantized value c_j * d.
+
+q4_0 record, on y = H x, per block of 32 elements (8 blocks, 8 fp16 scales +
+128 bytes of 4-bit codes), following the ggml q4_0 convention that the name
+points to:
+  m = the y_j of largest |y_j| (first index on ties);
+  d = fp16 round-to-nearest-even of the exact value -m/8;
+  d == 0 -> all codes 8; else c_j = clamp(floor(y_j / d + 1/2) + 8, 0, 15)
+  (round half up, then offset 8), computed from the stored d.
+  Dequantized (rotated-domain) value (c_j - 8) * d.
+
+Every decision is taken on exact values: the quotient x/d (or y/d) is formed
+in fp64, and it cannot land within fp64 rounding of a half-integer unless it
+is one exactly (x, y, d are multiples of 2^-28 below 2^20, so a non-tie
+quotient stays at least 2^-44 away from a tie, far above the 2^-49 error of
+an fp64 quotient below 16). The halves are detected as ``frac >= 0.5`` on
+the exact remainder, never by adding 0.5 in floating point.
+
+A d that overflows fp16 (|a| or |m| beyond what fp16 can scale) is out of the
+method's domain; the rules above still give codes (0 for int8, 8 for q4_0),
+and the dequantized values are then not finite.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .hadamard import rotate
+
+FMT_INT8, FMT_Q4_0, FMT_K8V4 = 0, 1, 2
+FORMATS = {"int8": FMT_INT8, "q4_0": FMT_Q4_0, "k8v4": FMT_K8V4}
+
+KIND_INT8, KIND_Q4 = "int8", "q4"
+
+HEAD_DIM = 256
+INT8_GROUP = 64
+Q4_BLOCK = 32
+
+
+def kinds(fmt: int):
+    """(K record kind, V record kind) of a cache format."""
+    if fmt == FMT_INT8:
+        return KIND_INT8, KIND_INT8
+    if fmt == FMT_Q4_0:
+        return KIND_Q4, KIND_Q4
+    if fmt == FMT_K8V4:
+        return KIND_INT8, KIND_Q4
+    raise ValueError(f"unknown format {fmt}")
+
+
+def rotates_query(fmt: int) -> bool:
+    """The query is rotated exactly when K is stored rotated (q4_0 only)."""
+    return kinds(fmt)[0] == KIND_Q4
+
+
+def rotates_output(fmt: int) -> bool:
+    """The output is rotated back exactly when V is stored rotated."""
+    return kinds(fmt)[1] == KIND_Q4
+
+
+def fp16_rne(v) -> np.ndarray:
+    """Round float64 values to fp16 once, to nearest, ties to even.
+
+    numpy converts a double to a half directly from its bits (one rounding,
+    overflow to +-inf), which is what is needed when the double holds the
+    exact value being rounded.
+    """
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16)
+
+
+def _round_half_away(q: np.ndarray) -> np.ndarray:
+    a = np.abs(q)
+    r = np.floor(a)
+    r = r + ((a - r) >= 0.5)
+    return np.copysign(r, q)
+
+
+def _round_half_up(q: np.ndarray) -> np.ndarray:
+    r = np.floor(q)
+    return r + ((q - r) >= 0.5)
+
+
+def quantize_int8(x) -> tuple[np.ndarray, np.ndarray]:
+    """int8 record of vectors x [..., 256] -> (codes int8 [..., 256], scales fp16 [..., 4])."""
+    x = np.asarray(x, dtype=np.float64)
+    g = x.reshape(x.shape[:-1] + (HEAD_DIM // INT8_GROUP, INT8_GROUP))
+    a = np.max(np.abs(g), axis=-1)
+    d16 = fp16_rne(a / 127.0)  # a/127 in fp64 then one rounding: see test pin
+    d = d16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d != 0, g / np.where(d != 0, d, 1.0), 0.0)
+    c = np.clip(_round_half_away(q), -127, 127)
+    return c.reshape(x.shape).astype(np.int8), d16
+
+
+def dequantize_int8(codes, scales) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.float64)
+    d = np.asarray(scales, dtype=np.float64)
+    g = c.reshape(c.shape[:-1] + (HEAD_DIM // INT8_GROUP, INT8_GROUP))
+    return (g * d[..., None]).reshape(c.shape)
+
+
+def quantize_q4_rotated(y) -> tuple[np.ndarray, np.ndarray]:
+    """q4_0 record of already-rotated vectors y [..., 256] -> (codes uint8 0..15, scales fp16 [..., 8])."""
+    y = np.asarray(y, dtype=np.float64)
+    b = y.reshape(y.shape[:-1] + (HEAD_DIM // Q4_BLOCK, Q4_BLOCK))
+    idx = np.argmax(np.abs(b), axis=-1)  # first index on ties
+    m = np.take_along_axis(b, idx[..., None], axis=-1)[..., 0]
+    d16 = fp16_rne(-m / 8.0)  # -m/8 is exact in fp64
+    d = d16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d != 0, b / np.where(d != 0, d, 1.0), 0.0)
+    c = np.clip(_round_half_up(q) + 8, 0, 15)
+    return c.reshape(y.shape).astype(np.uint8), d16
+
+
+def quantize_q4(x) -> tuple[np.ndarray, np.ndarray]:
+    """q4_0 record of vectors x [..., 256]: rotate by H, then quantize."""
+    return quantize_q4_rotated(rotate(x))
+
+
+def dequantize_q4(codes, scales) -> np.ndarray:
+    """Rotated-domain values (c - 8) * d of a q4_0 record."""
+    c = np.asarray(codes, dtype=np.float64) - 8.0
+    d = np.asarray(scales, dtype=np.float64)
+    b = c.reshape(c.shape[:-1] + (HEAD_DIM // Q4_BLOCK, Q4_BLOCK))
+    return (b * d[..., None]).reshape(c.shape)
+
+
+def encode(x, kind: str):
+    return quantize_int8(x) if kind == KIND_INT8 else quantize_q4(x)
+
+
+def decode(codes, scales, kind: str):
+    return dequantize_int8(codes, scales) if kind == KIND_INT8 else dequantize_q4(codes, scales)
+
+
+def record_bytes(kind: str) -> int:
+    """Bytes of one 256-element vector record: codes plus fp16 scales."""
+    if kind == KIND_INT8:
+        return HEAD_DIM + 2 * (HEAD_DIM // INT8_GROUP)
+    return HEAD_DIM // 2 + 2 * (HEAD_DIM // Q4_BLOCK)
