@@ -1,0 +1,260 @@
+/*
+ * kvcache.h - C ABI of the MI355X (gfx950) quantized, paged KV cache library.
+ *
+ * The library implements the decode hot path of a KV cache kept in
+ * block-quantized pages, as described on the KV-offload pages:
+ *
+ *   - Strata page: the hotelren.com article "KV 沉进内存、显存减半：Strata 让
+ *     12 GB 显卡跑满 262K 上下文", sections "KV 从显存搬进内存之后发生了什么"
+ *     (authoritative KV in pinned host memory, a residency table with CLOCK
+ *     second-chance eviction, zero-copy page-in of missing pages, identical
+ *     results), "4-bit KV 缓存：先旋转，再压到 4-bit" (256-point Walsh-Hadamard
+ *     rotation of Q, K and V, 4-bit q4_0 blocks, output restored by H) and
+ *     "三种 KV 格式横向对比" (int8, q4_0, k8v4).
+ *   - VRAM wiki page: anozoder.com wiki "qwen38-27b-quant-vram-2026", section
+ *     "一、为什么 256K 上下文的显存这么吓人" (GQA shape: 24 query heads, 4 KV
+ *     heads, head_dim 256).
+ *   - KV-offload news page: rebasdaily.com topic page on Qwen3.8-Flash-Next KV
+ *     offload, section "缓存为何不能直接搬走？" (every decoded token re-reads the
+ *     whole KV of each full-attention layer).
+ *
+ * Conventions for every entry point:
+ *   - Return 0 (KV_OK) or a negative KV_E* status. On a non-zero status
+ *     nothing has been enqueued and kv_last_error() describes the problem
+ *     (thread-local, valid until the next call on the same thread).
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t,
+ *     NULL = the default stream). Argument checks happen on the host before
+ *     anything is enqueued.
+ *   - The library allocates no device or host memory; every buffer belongs
+ *     to the caller and must stay alive until the enqueued work completes.
+ *   - Pointers named "device" must be device memory (or device-accessible
+ *     pinned host memory); pointers named "host" are read on the host during
+ *     the call. Device buffers must be 16-byte aligned (KV_EALIGN otherwise).
+ *
+ * Byte layout of a page (fixed by this library; the pages name pages, blocks
+ * and slots but no layout): a page holds 256 consecutive tokens of one
+ * sequence and one layer, for every KV head h in order, the K plane of head h
+ * then its V plane. Plane sizes: int8 67,584 B, q4 36,864 B, so a page is
+ * 540,672 B (int8), 294,912 B (q4_0) or 417,792 B (k8v4) for 4 KV heads.
+ *   K plane (token-major): 256 code rows (256 B int8 / 128 B q4) then 256 rows
+ *     of fp16 scales (4 int8 groups of 64 / 8 q4 blocks of 32). In a code row,
+ *     the bytes of the eight 32-element blocks are split into four slices and
+ *     slice-major: q4 byte 32s+4j+w = code[32j+4s+w] | code[32j+16+4s+w] << 4,
+ *     int8 byte 64s+8j+w = code[32j+8s+w] (s = 0..3, j = block 0..7).
+ *   V plane (element-major): 256 code rows, one per head element, holding that
+ *     element for the 256 tokens (int8: byte t = token t; q4: byte 16G+i =
+ *     code[token 32G+i] | code[token 32G+16+i] << 4), then one row of 256 fp16
+ *     scales per group (int8, 4 rows) or block (q4, 8 rows).
+ *
+ * Record rules (readings; the pages fix the byte sizes and the rotation):
+ *   int8 per 64 elements: d = fp16_rne(max|x| / 127), c = clamp(round half
+ *     away from zero(x / d), -127, 127), d == 0 gives c = 0; value c * d.
+ *   q4_0 per 32 elements of y = H x: m = the y of largest |y| (first index on
+ *     ties), d = fp16_rne(-m / 8), c = clamp(floor(y / d + 1/2) + 8, 0, 15),
+ *     d == 0 gives c = 8; value (c - 8) * d. H[i][j] = (-1)^popcount(i&j)/16.
+ *   k8v4: K as int8 (not rotated), V as rotated q4_0.
+ */
+#ifndef KVCACHE_H
+#define KVCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KV_OK            0
+#define KV_EINVAL       (-1)  /* an argument is out of range or inconsistent      */
+#define KV_EUNSUPPORTED (-2)  /* a shape this library does not implement          */
+#define KV_EALIGN       (-3)  /* a device buffer is not 16-byte aligned           */
+#define KV_ENOSLOTS     (-4)  /* a selection is larger than the slot pool         */
+#define KV_EHIP         (-5)  /* the HIP runtime reported an error                */
+#define KV_ESMALL       (-6)  /* a caller-provided buffer is too small            */
+
+/* Device status bits OR-ed into a status word by kernels that find bad data
+ * they cannot report synchronously (see kv_decode_attention). */
+#define KV_STATUS_BAD_PAGE_ID     1  /* a block-table entry outside the pool: page skipped */
+#define KV_STATUS_CONTEXT_CLAMPED 2  /* a context length above its bound: clamped            */
+
+/* KV formats (Strata page, section "三种 KV 格式横向对比"). */
+#define KV_FMT_INT8 0  /* K and V int8, per-64 fp16 scales, 264 B per vector        */
+#define KV_FMT_Q4_0 1  /* K and V rotated by H, q4_0 blocks, 144 B per vector       */
+#define KV_FMT_K8V4 2  /* K int8 (unrotated), V rotated q4_0: 408 B per KV head      */
+
+/* Shape of one layer's cache. Supported: head_dim == 256, page_tokens == 256,
+ * n_kv_heads >= 1, n_q_heads a multiple of n_kv_heads with at most 8 query
+ * heads per KV head. */
+typedef struct kv_shape {
+  int32_t n_q_heads;    /* e.g. 24 */
+  int32_t n_kv_heads;   /* e.g. 4  */
+  int32_t head_dim;     /* 256     */
+  int32_t page_tokens;  /* 256     */
+  int32_t format;       /* KV_FMT_* */
+} kv_shape;
+
+/* Thread-local text of the last non-zero status. Never NULL. */
+const char* kv_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* kv_version(void);
+
+/* Bytes of one page for `shape` (540672 / 294912 / 417792 for 4 KV heads),
+ * or a negative status if the shape is invalid or unsupported. */
+int64_t kv_page_bytes(const kv_shape* shape);
+
+/*
+ * kv_append_quantize - quantize-on-append (Strata page, section "4-bit KV
+ * 缓存：先旋转，再压到 4-bit": K and V are rotated and stored as q4_0 blocks as
+ * they are written; section "三种 KV 格式横向对比" for int8 and k8v4).
+ *
+ * Writes the records of tokens [start_pos, start_pos + n_tokens) of one
+ * sequence into its pages: token p goes to page block_table[p / 256], row
+ * p % 256. Every code and scale is bit-exact to the record rules above
+ * (the rotation is computed exactly, in fp64).
+ *
+ *   k, v         device fp16 [n_tokens][n_kv_heads][256], token-major.
+ *   block_table  device int32 [n_table]: physical page id of each logical
+ *                page of the sequence; n_table * 256 >= start_pos + n_tokens.
+ *   pool         device (or device-accessible pinned host) base of the page
+ *                pool, n_pool_pages pages of kv_page_bytes() each. A page id
+ *                outside [0, n_pool_pages) is skipped and, if `status` is not
+ *                NULL, KV_STATUS_BAD_PAGE_ID is OR-ed into *status (device).
+ *   status       device int32 or NULL.
+ * Only the rows of the appended tokens change (a q4 V code byte shared with
+ * another token keeps that token's nibble). Appends to the same page from
+ * several calls must be ordered on one stream.
+ */
+int kv_append_quantize(const kv_shape* shape, const void* k, const void* v,
+                       int64_t n_tokens, int64_t start_pos,
+                       const int32_t* block_table, int32_t n_table,
+                       void* pool, int64_t n_pool_pages,
+                       int32_t* status, void* stream);
+
+/*
+ * kv_decode_workspace_bytes - bytes of workspace kv_decode_attention needs
+ * for `batch` sequences of at most `max_context` tokens, with the given
+ * pages_per_split (0 = the library's choice, as in kv_decode_attention).
+ * Returns 0 for invalid arguments (see kv_last_error()).
+ */
+size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch,
+                                 int64_t max_context, int32_t pages_per_split);
+
+/*
+ * kv_decode_attention - GQA decode attention over the paged, quantized
+ * cache (KV-offload news page, section "缓存为何不能直接搬走？": a decode step
+ * reads the whole KV of the layer; Strata page, section "4-bit KV 缓存：先旋转，
+ * 再压到 4-bit": with rotated K the query is rotated by H first, and with
+ * rotated V the output is multiplied by H).
+ *
+ * For each sequence b and query head h (KV head g = h / (n_q_heads /
+ * n_kv_heads)), over its T = context_lens[b] tokens:
+ *   q' = H q if K is rotated (q4_0) else q;  s_t = softmax_scale * <q', k^_t>;
+ *   o' = sum_t softmax(s)_t v^_t;  out = H o' if V is rotated (q4_0, k8v4).
+ * k^ and v^ are the dequantized records. T == 0 gives a zero output.
+ * The work is split along the context ("split-K"): each split of
+ * pages_per_split pages writes a partial (max, sum, weighted values) that a
+ * second kernel combines with the log-sum-exp rule and rotates back.
+ * The arithmetic order depends only on logical token order, never on the
+ * physical page ids, so results do not depend on where pages are placed.
+ *
+ *   q              device fp16 [batch][n_q_heads][256].
+ *   pool           device base of n_pool_pages pages.
+ *   block_tables   device int32 [batch][max_pages]; entries past the last
+ *                  page of a sequence are not read.
+ *   context_lens   device int32 [batch]; each must be <= max_context and
+ *                  <= max_pages * 256 (larger values are clamped and flagged).
+ *   max_context    host bound on every context length (sizes the split grid).
+ *   softmax_scale  e.g. 1/16 = 1/sqrt(256).
+ *   out            device fp32 [batch][n_q_heads][256].
+ *   workspace      device, >= kv_decode_workspace_bytes() bytes. Its first
+ *                  int32 is a status word into which the kernels OR
+ *                  KV_STATUS_* bits; the caller may read and clear it.
+ *   pages_per_split  pages per split (>= 1), or 0 for the library's choice.
+ */
+int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
+                        const void* pool, int64_t n_pool_pages,
+                        const int32_t* block_tables, int32_t max_pages,
+                        const int32_t* context_lens, int64_t max_context,
+                        float softmax_scale, float* out,
+                        void* workspace, size_t workspace_bytes,
+                        int32_t pages_per_split, void* stream);
+
+/*
+ * Residency table of one layer's device page slots (Strata page, section
+ * "KV 从显存搬进内存之后发生了什么": a residency table with CLOCK second-chance
+ * eviction). Plain host memory owned by the caller:
+ *   slot_page[n_slots]  logical page held by each slot, -1 = empty
+ *   page_slot[n_pages]  slot holding each logical page, -1 = not resident
+ *   ref[n_slots]        second-chance reference bits
+ *   hand                next slot the clock hand inspects
+ */
+typedef struct kv_residency {
+  int32_t n_slots;
+  int32_t n_pages;
+  int32_t* slot_page;
+  int32_t* page_slot;
+  uint8_t* ref;
+  int32_t hand;
+} kv_residency;
+
+/* Marks every slot empty, every page non-resident, clears the reference bits
+ * and puts the hand at slot 0. */
+int kv_residency_reset(kv_residency* table);
+
+/*
+ * kv_residency_select - one step of the CLOCK table (host only, no GPU).
+ * For an ordered selection of n_sel distinct logical pages (n_sel <= n_slots,
+ * else KV_ENOSLOTS): first every resident selected page gets ref = 1 and is
+ * pinned for the step; then each missing page, in order, takes the slot the
+ * hand finds (empty; else not pinned with ref = 0, clearing ref = 1 bits on
+ * the way), is installed with ref = 1, pinned, the hand moved past it.
+ *   out_slots   host int32 [n_sel]: the slot of every selected page, in order.
+ *   miss_pages  host int32 [n_sel] (may be NULL): the missing pages in order,
+ *   miss_slots  host int32 [n_sel] (may be NULL): the slot each went to,
+ *   n_miss      host int32 (may be NULL): how many pages were missing.
+ * On error the table is unchanged.
+ */
+int kv_residency_select(kv_residency* table, const int32_t* selection, int32_t n_sel,
+                        int32_t* out_slots, int32_t* miss_pages, int32_t* miss_slots,
+                        int32_t* n_miss);
+
+/*
+ * kv_gather_pages - page-in of one layer's selected pages (Strata page,
+ * section "KV 从显存搬进内存之后发生了什么": before attention the selected
+ * blocks are looked up in the residency table and missing pages are copied
+ * zero-copy over PCIe from pinned host memory into device slots).
+ *
+ * Runs kv_residency_select on `table`, then enqueues one kernel that reads
+ * every missing page directly from `host_pool` (pinned, device-accessible:
+ * allocated with hipHostMalloc or torch pin_memory) and writes it to its slot
+ * of `slot_pool`, and writes the slot of every selected page, in selection
+ * order, to `out_block_table` (device int32 [n_sel]) - the block table that
+ * kv_decode_attention then reads. Page bytes are copied verbatim, so
+ * attention over gathered slots equals attention over the host pages.
+ *
+ *   host_pool        n_pages (= table->n_pages) pages of kv_page_bytes().
+ *   slot_pool        device, table->n_slots pages.
+ *   out_n_miss       host int32 or NULL.
+ * The host pages must not change until the enqueued copy completes.
+ */
+int kv_gather_pages(const kv_shape* shape, kv_residency* table,
+                    const int32_t* selection, int32_t n_sel,
+                    const void* host_pool, void* slot_pool,
+                    int32_t* out_block_table, int32_t* out_n_miss, void* stream);
+
+/* Host-side helpers of the record rules, exposed so the rounding can be
+ * checked without a GPU. Not part of the hot path.
+ *   kv_host_f64_to_f16: round a double to fp16 bits once, nearest-even.
+ *   kv_host_encode_vector: record of one fp16 vector x[256] (raw fp16 bits)
+ *     as the append kernel writes it: kind 0 = int8 (codes int8 x256,
+ *     scales fp16 x4), kind 1 = q4 of H x (codes 0..15 x256, scales x8). */
+uint16_t kv_host_f64_to_f16(double x);
+int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCACHE_H */

@@ -1,0 +1,17 @@
+"""MI355X-native quantized, paged, host-offloadable GQA decode attention.
+
+The hot path lives in the HIP library ``lib/libkvcache.so`` (C ABI in
+``include/kvcache.h``): quantize-on-append (int8, Walsh-Hadamard-rotated
+q4_0, k8v4), split-K decode attention with the rotation back, and a
+CLOCK-managed zero-copy page gather from pinned host memory. This package is
+the thin Python binding over it; it raises ImportError if the library has
+not been built (``python -m offloaded_kv_cache_amd.build``).
+"""
+
+from ._native import (  # noqa: F401
+    FORMATS, KV_FMT_INT8, KV_FMT_K8V4, KV_FMT_Q4_0, KV_STATUS_BAD_PAGE_ID,
+    KV_STATUS_CONTEXT_CLAMPED, KVError, KVShape, Residency, append_quantize,
+    decode_attention, decode_workspace_bytes, gather_pages, host_encode_vector,
+    host_f64_to_f16, last_error, page_bytes, shape, version,
+)
+from . import paged  # noqa: F401

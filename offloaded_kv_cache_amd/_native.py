@@ -1,0 +1,234 @@
+"""ctypes binding of ``lib/libkvcache.so`` (the C ABI in ``include/kvcache.h``).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+library. PyTorch supplies device memory, pinned host memory and the stream.
+If the library is missing, importing this module raises: there is no CPU
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libkvcache.so")
+
+KV_OK, KV_EINVAL, KV_EUNSUPPORTED, KV_EALIGN, KV_ENOSLOTS, KV_EHIP, KV_ESMALL = 0, -1, -2, -3, -4, -5, -6
+KV_STATUS_BAD_PAGE_ID, KV_STATUS_CONTEXT_CLAMPED = 1, 2
+KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4 = 0, 1, 2
+FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4}
+
+EXPORTED_SYMBOLS = (
+    "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
+    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_residency_reset",
+    "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
+)
+
+
+class KVShape(C.Structure):
+    _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("page_tokens", C.c_int32), ("format", C.c_int32)]
+
+
+class KVResidency(C.Structure):
+    _fields_ = [("n_slots", C.c_int32), ("n_pages", C.c_int32),
+                ("slot_page", C.POINTER(C.c_int32)), ("page_slot", C.POINTER(C.c_int32)),
+                ("ref", C.POINTER(C.c_uint8)), ("hand", C.c_int32)]
+
+
+class KVError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvcache error {code}: {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
+                          "(run `python -m offloaded_kv_cache_amd.build`)")
+    lib = C.CDLL(LIB_PATH)
+    P, I32, I64, SZ, F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
+    sig = {
+        "kv_last_error": (C.c_char_p, []),
+        "kv_version": (C.c_char_p, []),
+        "kv_page_bytes": (I64, [C.POINTER(KVShape)]),
+        "kv_append_quantize": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, P, I32, P, I64, P, P]),
+        "kv_decode_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I64, I32]),
+        "kv_decode_attention": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
+                                          P, P, SZ, I32, P]),
+        "kv_residency_reset": (C.c_int, [C.POINTER(KVResidency)]),
+        "kv_residency_select": (C.c_int, [C.POINTER(KVResidency), P, I32, P, P, P, P]),
+        "kv_gather_pages": (C.c_int, [C.POINTER(KVShape), C.POINTER(KVResidency), P, I32, P, P, P,
+                                      P, P]),
+        "kv_host_f64_to_f16": (C.c_uint16, [C.c_double]),
+        "kv_host_encode_vector": (C.c_int, [I32, P, P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def last_error() -> str:
+    return lib.kv_last_error().decode()
+
+
+def version() -> str:
+    return lib.kv_version().decode()
+
+
+def _check(code: int):
+    if code != KV_OK:
+        raise KVError(code, last_error())
+
+
+def shape(fmt, n_q_heads: int = 24, n_kv_heads: int = 4, head_dim: int = 256,
+          page_tokens: int = 256) -> KVShape:
+    f = FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+    return KVShape(n_q_heads, n_kv_heads, head_dim, page_tokens, f)
+
+
+def page_bytes(s: KVShape) -> int:
+    r = lib.kv_page_bytes(C.byref(s))
+    if r < 0:
+        raise KVError(int(r), last_error())
+    return int(r)
+
+
+# ------------------------------------------------------------------ torch glue
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, device=True, name="tensor"):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=None, stream=None):
+    """Quantize-on-append of tokens [start_pos, start_pos + k.shape[0]) of one sequence."""
+    torch = _torch()
+    n = k.shape[0]
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1] != s.n_kv_heads or k.shape[2] != s.head_dim:
+        raise ValueError("k and v must be [n_tokens, n_kv_heads, head_dim]")
+    pb = page_bytes(s)
+    if pool.numel() % pb:
+        raise ValueError("pool size is not a whole number of pages")
+    _check(lib.kv_append_quantize(
+        C.byref(s), _ptr(k, torch.float16, name="k"), _ptr(v, torch.float16, name="v"),
+        n, start_pos, _ptr(block_table, torch.int32, name="block_table"), block_table.numel(),
+        C.c_void_p(pool.data_ptr()), pool.numel() // pb,
+        _ptr(status, torch.int32, name="status"), _stream(stream)))
+
+
+def decode_workspace_bytes(s: KVShape, batch: int, max_context: int, pages_per_split: int = 0) -> int:
+    r = lib.kv_decode_workspace_bytes(C.byref(s), batch, max_context, pages_per_split)
+    if r == 0:
+        raise KVError(KV_EINVAL, last_error())
+    return int(r)
+
+
+def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
+                     workspace, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
+                     stream=None):
+    """GQA decode attention over the paged cache; writes fp32 ``out`` [B, Hq, 256]."""
+    torch = _torch()
+    B = q.shape[0]
+    if q.shape != (B, s.n_q_heads, s.head_dim) or out.shape != (B, s.n_q_heads, s.head_dim):
+        raise ValueError("q and out must be [batch, n_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
+    pb = page_bytes(s)
+    _check(lib.kv_decode_attention(
+        C.byref(s), _ptr(q, torch.float16, name="q"), B, C.c_void_p(pool.data_ptr()),
+        pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
+        block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
+        softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream)))
+
+
+class Residency:
+    """Host arrays of one layer's CLOCK residency table (kv_residency)."""
+
+    def __init__(self, n_slots: int, n_pages: int):
+        self.slot_page = np.full(n_slots, -1, np.int32)
+        self.page_slot = np.full(max(n_pages, 1), -1, np.int32)
+        self.ref = np.zeros(n_slots, np.uint8)
+        self.c = KVResidency(n_slots, n_pages,
+                             self.slot_page.ctypes.data_as(C.POINTER(C.c_int32)),
+                             self.page_slot.ctypes.data_as(C.POINTER(C.c_int32)),
+                             self.ref.ctypes.data_as(C.POINTER(C.c_uint8)), 0)
+        _check(lib.kv_residency_reset(C.byref(self.c)))
+
+    @property
+    def hand(self) -> int:
+        return self.c.hand
+
+    def select(self, selection):
+        sel = np.ascontiguousarray(selection, dtype=np.int32)
+        n = sel.size
+        slots = np.empty(max(n, 1), np.int32)
+        mp = np.empty(max(n, 1), np.int32)
+        ms = np.empty(max(n, 1), np.int32)
+        nm = C.c_int32(0)
+        _check(lib.kv_residency_select(C.byref(self.c), sel.ctypes.data_as(C.c_void_p), n,
+                                       slots.ctypes.data_as(C.c_void_p), mp.ctypes.data_as(C.c_void_p),
+                                       ms.ctypes.data_as(C.c_void_p), C.byref(nm)))
+        k = nm.value
+        return slots[:n].copy(), list(zip(mp[:k].tolist(), ms[:k].tolist()))
+
+
+def gather_pages(s: KVShape, table: Residency, selection, host_pool, slot_pool, out_block_table,
+                 stream=None) -> int:
+    """CLOCK step + zero-copy page-in; returns the number of pages copied."""
+    torch = _torch()
+    sel = np.ascontiguousarray(selection, dtype=np.int32)
+    if not host_pool.is_pinned():
+        raise ValueError("host_pool must be pinned host memory")
+    nm = C.c_int32(0)
+    _check(lib.kv_gather_pages(C.byref(s), C.byref(table.c), sel.ctypes.data_as(C.c_void_p), sel.size,
+                               C.c_void_p(host_pool.data_ptr()), C.c_void_p(slot_pool.data_ptr()),
+                               _ptr(out_block_table, torch.int32, name="out_block_table"),
+                               C.byref(nm), _stream(stream)))
+    return nm.value
+
+
+def host_f64_to_f16(x: float) -> int:
+    return int(lib.kv_host_f64_to_f16(float(x)))
+
+
+def host_encode_vector(kind: int, x: np.ndarray):
+    """Record of one fp16 vector by the library's host rules: (codes uint8[256], scales fp16)."""
+    xb = np.ascontiguousarray(np.asarray(x, np.float16)).view(np.uint16)
+    codes = np.zeros(256, np.uint8)
+    scales = np.zeros(8, np.uint16)
+    _check(lib.kv_host_encode_vector(kind, xb.ctypes.data_as(C.c_void_p),
+                                     codes.ctypes.data_as(C.c_void_p), scales.ctypes.data_as(C.c_void_p)))
+    n = 4 if kind == 0 else 8
+    return codes, scales[:n].view(np.float16)

@@ -1,0 +1,364 @@
+// kv_api.hip - the C ABI: argument checks, workspace layout, dispatch, and the
+// host-side CLOCK residency table.
+//
+// CLOCK table: Strata page ("KV 沉进内存、显存减半：Strata 让 12 GB 显卡跑满
+// 262K 上下文"), section "KV 从显存搬进内存之后发生了什么" - before attention
+// the selected blocks are looked up in a residency table with CLOCK (second
+// chance) eviction, and missing pages are paged in. The page names the policy;
+// the step rules (hits pinned first, misses placed in selection order, ref set
+// on insert) are the textbook algorithm and are documented in kvcache.h.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kv_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return KV_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(const kv_shape* s) {
+  if (!s) return fail(KV_EINVAL, "shape is NULL");
+  if (s->format != KV_FMT_INT8 && s->format != KV_FMT_Q4_0 && s->format != KV_FMT_K8V4)
+    return fail(KV_EINVAL, "unknown format %d", s->format);
+  if (s->head_dim != kHeadDim) return fail(KV_EUNSUPPORTED, "head_dim must be 256 (got %d)", s->head_dim);
+  if (s->page_tokens != kPageTokens)
+    return fail(KV_EUNSUPPORTED, "page_tokens must be 256 (got %d)", s->page_tokens);
+  if (s->n_kv_heads < 1 || s->n_kv_heads > 65535)
+    return fail(KV_EINVAL, "n_kv_heads out of range (%d)", s->n_kv_heads);
+  if (s->n_q_heads < s->n_kv_heads || s->n_q_heads % s->n_kv_heads)
+    return fail(KV_EINVAL, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads / s->n_kv_heads > kMaxGroup)
+    return fail(KV_EUNSUPPORTED, "at most %d query heads per KV head (got %d)", kMaxGroup,
+                s->n_q_heads / s->n_kv_heads);
+  return KV_OK;
+}
+
+int64_t page_bytes_of(const kv_shape* s) { return (int64_t)s->n_kv_heads * head_stride(s->format); }
+
+// Pages per split chosen so that the grid has about two workgroups per compute
+// unit (256 CUs) for the given batch, with every wave of a workgroup busy.
+int32_t auto_pages_per_split(const kv_shape* s, int32_t batch, int64_t max_pages_ctx) {
+  const int64_t target = 512;
+  int64_t per_seq_head = target / ((int64_t)batch * s->n_kv_heads);
+  if (per_seq_head < 1) per_seq_head = 1;
+  int64_t pps = (max_pages_ctx + per_seq_head - 1) / per_seq_head;
+  if (pps < 4) pps = 4;
+  return (int32_t)pps;
+}
+
+struct WsLayout {
+  size_t ml_off, o_off, total;
+  int32_t n_splits;
+};
+
+WsLayout workspace_layout(const kv_shape* s, int32_t batch, int64_t max_context, int32_t pps) {
+  const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
+  int64_t ns = (max_pages_ctx + pps - 1) / pps;
+  if (ns < 1) ns = 1;
+  WsLayout w;
+  w.n_splits = (int32_t)ns;
+  const size_t parts = (size_t)batch * s->n_q_heads * (size_t)ns;
+  w.ml_off = 256;
+  w.o_off = (w.ml_off + parts * 2 * sizeof(float) + 255) & ~(size_t)255;
+  w.total = w.o_off + parts * kHeadDim * sizeof(float);
+  return w;
+}
+
+
+// Checks a table and a selection without changing anything.
+int validate_selection(const kv_residency* t, const int32_t* selection, int32_t n_sel,
+                       const int32_t* out_slots) {
+  if (!t || t->n_slots < 1 || t->n_pages < 0 || !t->slot_page || !t->ref ||
+      (t->n_pages > 0 && !t->page_slot))
+    return fail(KV_EINVAL, "bad residency table");
+  if (t->hand < 0 || t->hand >= t->n_slots) return fail(KV_EINVAL, "hand out of range");
+  if (n_sel < 0) return fail(KV_EINVAL, "negative selection size");
+  if (n_sel > t->n_slots)
+    return fail(KV_ENOSLOTS, "selection of %d pages exceeds %d slots", n_sel, t->n_slots);
+  if (n_sel > 0 && (!selection || !out_slots)) return fail(KV_EINVAL, "NULL selection or out_slots");
+  std::vector<uint8_t> seen(t->n_pages, 0);
+  for (int32_t i = 0; i < n_sel; ++i) {
+    const int32_t p = selection[i];
+    if (p < 0 || p >= t->n_pages) return fail(KV_EINVAL, "page %d out of range [0, %d)", p, t->n_pages);
+    if (seen[p]) return fail(KV_EINVAL, "page %d selected twice", p);
+    seen[p] = 1;
+  }
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kv_last_error(void) { return g_error.c_str(); }
+
+const char* kv_version(void) { return "0.1.0"; }
+
+int64_t kv_page_bytes(const kv_shape* shape) {
+  if (int r = check_shape(shape)) return r;
+  ok();
+  return page_bytes_of(shape);
+}
+
+int kv_append_quantize(const kv_shape* shape, const void* k, const void* v, int64_t n_tokens,
+                       int64_t start_pos, const int32_t* block_table, int32_t n_table, void* pool,
+                       int64_t n_pool_pages, int32_t* status, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (n_tokens < 0 || start_pos < 0) return fail(KV_EINVAL, "negative n_tokens or start_pos");
+  if (n_tokens == 0) return ok();
+  if (!k || !v || !block_table || !pool) return fail(KV_EINVAL, "NULL buffer");
+  if (n_table < 1 || start_pos + n_tokens > (int64_t)n_table * kPageTokens)
+    return fail(KV_EINVAL, "tokens [%lld, %lld) do not fit %d pages of 256", (long long)start_pos,
+                (long long)(start_pos + n_tokens), n_table);
+  if (n_pool_pages < 1) return fail(KV_EINVAL, "n_pool_pages must be >= 1");
+  if (!aligned(k, 2) || !aligned(v, 2) || !aligned(block_table, 4) || !aligned(pool, 16) ||
+      (status && !aligned(status, 4)))
+    return fail(KV_EALIGN, "misaligned buffer (k, v: 2 B; block_table: 4 B; pool: 16 B)");
+  if ((start_pos + n_tokens - 1) / 32 - start_pos / 32 + 1 > (int64_t)(0x7FFFFFFF / 16))
+    return fail(KV_EINVAL, "too many tokens in one call");
+  hipError_t e = launch_append(shape->format, shape->n_kv_heads, (const uint16_t*)k,
+                               (const uint16_t*)v, n_tokens, start_pos, block_table, n_table,
+                               (uint8_t*)pool, n_pool_pages, status, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch, int64_t max_context,
+                                 int32_t pages_per_split) {
+  if (check_shape(shape)) return 0;
+  if (batch < 1 || max_context < 0 || max_context > 0x7FFFFFFF || pages_per_split < 0) {
+    fail(KV_EINVAL, "bad batch, max_context or pages_per_split");
+    return 0;
+  }
+  const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
+  const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, batch, max_pages_ctx);
+  ok();
+  return workspace_layout(shape, batch, max_context, pps).total;
+}
+
+int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch, const void* pool,
+                        int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
+                        const int32_t* context_lens, int64_t max_context, float softmax_scale,
+                        float* out, void* workspace, size_t workspace_bytes,
+                        int32_t pages_per_split, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (batch < 0 || batch > 65535) return fail(KV_EINVAL, "batch out of range (%d)", batch);
+  if (batch == 0) return ok();
+  if (!q || !pool || !block_tables || !context_lens || !out || !workspace)
+    return fail(KV_EINVAL, "NULL buffer");
+  if (max_pages < 1) return fail(KV_EINVAL, "max_pages must be >= 1");
+  if (max_context < 0 || max_context > 0x7FFFFFFF) return fail(KV_EINVAL, "max_context out of range");
+  if (n_pool_pages < 1) return fail(KV_EINVAL, "n_pool_pages must be >= 1");
+  if (pages_per_split < 0) return fail(KV_EINVAL, "pages_per_split must be >= 0");
+  if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
+  if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(KV_EALIGN, "misaligned buffer (q, pool, out: 16 B; workspace: 256 B)");
+  const int64_t bound = max_context < (int64_t)max_pages * kPageTokens ? max_context
+                                                                       : (int64_t)max_pages * kPageTokens;
+  const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
+  const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, batch, max_pages_ctx);
+  const WsLayout w = workspace_layout(shape, batch, max_context, pps);
+  if (workspace_bytes < w.total)
+    return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                w.total);
+  uint8_t* ws = (uint8_t*)workspace;
+  DecodeArgs a;
+  a.fmt = shape->format;
+  a.n_q_heads = shape->n_q_heads;
+  a.n_kv_heads = shape->n_kv_heads;
+  a.batch = batch;
+  a.q = (const uint16_t*)q;
+  a.pool = (const uint8_t*)pool;
+  a.n_pool_pages = n_pool_pages;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages;
+  a.context_lens = context_lens;
+  a.max_context = (int32_t)bound;
+  a.pages_per_split = pps;
+  a.n_splits = w.n_splits;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.status = (int32_t*)ws;
+  a.part_ml = (float*)(ws + w.ml_off);
+  a.part_o = (float*)(ws + w.o_off);
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+int kv_residency_reset(kv_residency* t) {
+  if (!t || t->n_slots < 1 || t->n_pages < 0 || !t->slot_page || !t->ref ||
+      (t->n_pages > 0 && !t->page_slot))
+    return fail(KV_EINVAL, "bad residency table");
+  for (int32_t s = 0; s < t->n_slots; ++s) {
+    t->slot_page[s] = -1;
+    t->ref[s] = 0;
+  }
+  for (int32_t p = 0; p < t->n_pages; ++p) t->page_slot[p] = -1;
+  t->hand = 0;
+  return ok();
+}
+
+int kv_residency_select(kv_residency* t, const int32_t* selection, int32_t n_sel, int32_t* out_slots,
+                        int32_t* miss_pages, int32_t* miss_slots, int32_t* n_miss) {
+  if (int r = validate_selection(t, selection, n_sel, out_slots)) return r;
+  std::vector<uint8_t> pinned(t->n_slots, 0);
+  for (int32_t i = 0; i < n_sel; ++i) {
+    const int32_t s = t->page_slot[selection[i]];
+    if (s >= 0) {
+      t->ref[s] = 1;
+      pinned[s] = 1;
+    }
+  }
+  int32_t misses = 0;
+  for (int32_t i = 0; i < n_sel; ++i) {
+    const int32_t p = selection[i];
+    if (t->page_slot[p] >= 0) continue;
+    int32_t s;
+    for (;;) {  // ends: at most n_sel - 1 slots are pinned, and a sweep clears every ref bit
+      s = t->hand;
+      t->hand = (t->hand + 1) % t->n_slots;
+      if (t->slot_page[s] < 0) break;
+      if (pinned[s]) continue;
+      if (t->ref[s]) {
+        t->ref[s] = 0;
+        continue;
+      }
+      t->page_slot[t->slot_page[s]] = -1;
+      break;
+    }
+    t->slot_page[s] = p;
+    t->page_slot[p] = s;
+    t->ref[s] = 1;
+    pinned[s] = 1;
+    if (miss_pages) miss_pages[misses] = p;
+    if (miss_slots) miss_slots[misses] = s;
+    ++misses;
+  }
+  for (int32_t i = 0; i < n_sel; ++i) out_slots[i] = t->page_slot[selection[i]];
+  if (n_miss) *n_miss = misses;
+  return ok();
+}
+
+int kv_gather_pages(const kv_shape* shape, kv_residency* t, const int32_t* selection, int32_t n_sel,
+                    const void* host_pool, void* slot_pool, int32_t* out_block_table,
+                    int32_t* out_n_miss, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (n_sel > 0 && (!host_pool || !slot_pool || !out_block_table))
+    return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(host_pool, 16) || !aligned(slot_pool, 16) || !aligned(out_block_table, 4))
+    return fail(KV_EALIGN, "misaligned buffer (pools: 16 B, block table: 4 B)");
+  {
+    int32_t dummy = 0;
+    if (int r = validate_selection(t, selection, n_sel, n_sel > 0 ? &dummy : nullptr)) return r;
+  }
+  if (n_sel > 0) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t pe = hipPointerGetAttributes(&attr, host_pool);
+    if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(KV_EINVAL, "host_pool is not pinned, device-accessible host memory");
+    }
+  }
+  std::vector<int32_t> slots(n_sel > 0 ? n_sel : 1), mp(n_sel > 0 ? n_sel : 1), ms(n_sel > 0 ? n_sel : 1);
+  int32_t misses = 0;
+  if (int r = kv_residency_select(t, selection, n_sel, slots.data(), mp.data(), ms.data(), &misses))
+    return r;
+  const int64_t pb = page_bytes_of(shape);
+  // Launch in batches that fit the kernel-argument block; each batch writes
+  // its slice of the block table and copies its share of the misses.
+  int32_t done_sel = 0, done_miss = 0;
+  while (done_sel < n_sel || done_miss < misses) {
+    GatherBatch gb;
+    gb.n_sel = n_sel - done_sel < kGatherMaxBatch ? n_sel - done_sel : kGatherMaxBatch;
+    gb.n_miss = misses - done_miss < kGatherMaxBatch ? misses - done_miss : kGatherMaxBatch;
+    for (int32_t i = 0; i < gb.n_sel; ++i) gb.slots[i] = slots[done_sel + i];
+    for (int32_t i = 0; i < gb.n_miss; ++i) {
+      gb.miss_page[i] = mp[done_miss + i];
+      gb.miss_slot[i] = ms[done_miss + i];
+    }
+    hipError_t e = launch_gather(gb, pb, (const uint8_t*)host_pool, (uint8_t*)slot_pool,
+                                 out_block_table + done_sel, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gather launch (the residency table was already updated)");
+    done_sel += gb.n_sel;
+    done_miss += gb.n_miss;
+  }
+  if (out_n_miss) *out_n_miss = misses;
+  return ok();
+}
+
+uint16_t kv_host_f64_to_f16(double x) { return f64_to_f16_rne(x); }
+
+int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales) {
+  if (!x || !codes || !scales) return fail(KV_EINVAL, "NULL buffer");
+  if (kind == kInt8) {
+    for (int g = 0; g < 4; ++g) {
+      double a = 0.0;
+      for (int e = 64 * g; e < 64 * g + 64; ++e) {
+        const double v = f16_to_f64(x[e]);
+        const double av = v < 0 ? -v : v;
+        if (av > a) a = av;
+      }
+      scales[g] = f64_to_f16_rne(a / 127.0);
+      const double d = f16_to_f64(scales[g]);
+      for (int e = 64 * g; e < 64 * g + 64; ++e)
+        codes[e] = (uint8_t)(int8_t)int8_code(f16_to_f64(x[e]), d);
+    }
+    return ok();
+  }
+  if (kind == kQ4) {
+    double y[kHeadDim];
+    for (int e = 0; e < kHeadDim; ++e) y[e] = f16_to_f64(x[e]);
+    for (int len = 1; len < kHeadDim; len <<= 1)  // Sylvester butterflies, exact in fp64
+      for (int i = 0; i < kHeadDim; i += 2 * len)
+        for (int j = i; j < i + len; ++j) {
+          const double a = y[j], b = y[j + len];
+          y[j] = a + b;
+          y[j + len] = a - b;
+        }
+    for (int e = 0; e < kHeadDim; ++e) y[e] *= 0.0625;
+    for (int blk = 0; blk < 8; ++blk) {
+      double m = y[32 * blk];
+      for (int e = 32 * blk + 1; e < 32 * blk + 32; ++e) {
+        const double am = m < 0 ? -m : m, ae = y[e] < 0 ? -y[e] : y[e];
+        if (ae > am) m = y[e];
+      }
+      scales[blk] = f64_to_f16_rne(-m * 0.125);
+      const double d = f16_to_f64(scales[blk]);
+      for (int e = 32 * blk; e < 32 * blk + 32; ++e) codes[e] = (uint8_t)q4_code(y[e], d);
+    }
+    return ok();
+  }
+  return fail(KV_EINVAL, "kind must be 0 (int8) or 1 (q4)");
+}
+
+}  // extern "C"

@@ -1,0 +1,130 @@
+// kv_internal.h - shared definitions of the HIP library (not installed).
+//
+// Record rules and page layout are those documented in include/kvcache.h; this
+// header holds their constants, the exact fp64 -> fp16 rounding and the
+// kernel launchers the C ABI dispatches to.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvcache.h"
+
+namespace kvc {
+
+constexpr int kHeadDim = 256;
+constexpr int kPageTokens = 256;
+constexpr int kMaxGroup = 8;  // query heads per KV head handled by one MFMA row tile
+
+enum RecordKind : int { kInt8 = 0, kQ4 = 1 };
+
+__host__ __device__ constexpr int code_row_bytes(int kind) { return kind == kInt8 ? 256 : 128; }
+__host__ __device__ constexpr int n_scales(int kind) { return kind == kInt8 ? 4 : 8; }
+__host__ __device__ constexpr int plane_bytes(int kind) {
+  return kPageTokens * code_row_bytes(kind) + kPageTokens * n_scales(kind) * 2;
+}
+__host__ __device__ constexpr int k_kind(int fmt) { return fmt == KV_FMT_Q4_0 ? kQ4 : kInt8; }
+__host__ __device__ constexpr int v_kind(int fmt) { return fmt == KV_FMT_INT8 ? kInt8 : kQ4; }
+__host__ __device__ constexpr int64_t head_stride(int fmt) {
+  return plane_bytes(k_kind(fmt)) + plane_bytes(v_kind(fmt));
+}
+
+// Round a double to the nearest fp16 (ties to even), once, from its bits.
+// IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; values
+// below 2^-14 are subnormal multiples of 2^-24; overflow gives infinity.
+__host__ __device__ inline uint16_t f64_to_f16_rne(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const int exp = (int)((b >> 52) & 0x7FF);
+  const uint64_t frac = b & 0xFFFFFFFFFFFFFull;
+  if (exp == 0x7FF) return (uint16_t)(sign | 0x7C00u | (frac ? 0x200u : 0u));
+  if (exp == 0) return sign;                    // |x| < 2^-1022
+  int e = exp - 1023;
+  if (e >= 16) return (uint16_t)(sign | 0x7C00u);
+  const uint64_t m = frac | (1ull << 52);       // |x| = m * 2^(e - 52)
+  const bool normal = e >= -14;
+  const int sh = normal ? 42 : 28 - e;          // target unit 2^(e-10), or 2^-24
+  if (sh >= 64) return sign;
+  uint64_t q = m >> sh;
+  const uint64_t rem = m & ((1ull << sh) - 1);
+  const uint64_t half = 1ull << (sh - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (normal) {
+    if (q == 2048) { q = 1024; ++e; }
+    if (e > 15) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | ((e + 15) << 10) | (uint16_t)(q - 1024));
+  }
+  return (uint16_t)(sign | q);                  // q == 1024 is the least normal
+}
+
+__host__ __device__ inline double f16_to_f64(uint16_t h) {
+  return (double)__builtin_bit_cast(_Float16, h);
+}
+
+// int8 code of x for the stored scale d: round half away from zero, clamp.
+// x/d is formed in fp64; it cannot fall within fp64 rounding of a half
+// integer without being one, so the decision is the exact one.
+__host__ __device__ inline int int8_code(double x, double d) {
+  if (d == 0.0) return 0;
+  const double q = x / d;
+  const double a = q < 0 ? -q : q;
+  double r = __builtin_floor(a);
+  if (a - r >= 0.5) r += 1.0;
+  int c = (int)r;
+  if (c > 127) c = 127;
+  return q < 0 ? -c : c;
+}
+
+// q4 code of y for the stored scale d: round half up, offset 8, clamp.
+__host__ __device__ inline int q4_code(double y, double d) {
+  if (d == 0.0) return 8;
+  const double q = y / d;
+  double r = __builtin_floor(q);
+  if (q - r >= 0.5) r += 1.0;
+  double c = r + 8.0;
+  if (c < 0.0) c = 0.0;
+  if (c > 15.0) c = 15.0;
+  return (int)c;
+}
+
+// Launchers (stream-ordered, arguments already validated by the C ABI).
+hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint16_t* v,
+                         int64_t n_tokens, int64_t start_pos, const int32_t* block_table,
+                         int32_t n_table, uint8_t* pool, int64_t n_pool_pages,
+                         int32_t* status, hipStream_t stream);
+
+struct DecodeArgs {
+  int fmt;
+  int n_q_heads, n_kv_heads, batch;
+  const uint16_t* q;
+  const uint8_t* pool;
+  int64_t n_pool_pages;
+  const int32_t* block_tables;
+  int32_t max_pages;
+  const int32_t* context_lens;
+  int32_t max_context;        // clamp bound, already min(max_context, max_pages * 256)
+  int32_t pages_per_split;
+  int32_t n_splits;           // grid size along the context
+  float scale_log2;           // softmax_scale * log2(e)
+  float* out;
+  int32_t* status;
+  float* part_ml;             // [batch][n_q_heads][n_splits][2]
+  float* part_o;              // [batch][n_q_heads][n_splits][256]
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+constexpr int kGatherMaxBatch = 256;  // selections per gather launch (kernel-argument size)
+
+struct GatherBatch {
+  int32_t n_sel;
+  int32_t n_miss;
+  int32_t slots[kGatherMaxBatch];       // slot of each selected page, in order
+  int32_t miss_page[kGatherMaxBatch];   // page ids to copy
+  int32_t miss_slot[kGatherMaxBatch];   // destination slots
+};
+
+hipError_t launch_gather(const GatherBatch& batch, int64_t page_bytes, const uint8_t* host_pool,
+                         uint8_t* slot_pool, int32_t* out_block_table, hipStream_t stream);
+
+}  // namespace kvc

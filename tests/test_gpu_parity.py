@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path against the fp64 oracle (through the C ABI).
+
+* quantize-on-append: pool bytes bit-exact to the oracle's records and layout;
+* decode attention on oracle-packed pools: max-abs <= 2e-3, rel-L2 <= 1e-3;
+* split-count independence, placement independence (bitwise), masking of
+  stale rows, T = 0, status flags for bad page ids and clamped contexts.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import offloaded_kv_cache_amd as K
+from oracle import layout, records
+
+from gpu_helpers import Sequence, assert_close, fmt_id, oracle_out, oracle_records, place_pages
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["int8", "q4_0", "k8v4"]
+
+
+def to_dev(a, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev)
+
+
+def special_vectors(n_kv_heads=4):
+    """fp16 token vectors that hit the rounding edge cases."""
+    vs = []
+    z = np.zeros((n_kv_heads, 256), np.float16)
+    vs.append(z)                                               # all zero: d = 0
+    t = np.zeros((n_kv_heads, 256), np.float16)
+    t[:, 0] = 127 / 16
+    t[:, 1:5] = np.array([2.5, -2.5, 0.5, -0.5], np.float16) / 16   # int8 ties
+    vs.append(t)
+    s = np.full((n_kv_heads, 256), np.float16(2.0 ** -24))     # subnormal inputs
+    s[:, ::2] *= -3
+    vs.append(s)
+    big = np.zeros((n_kv_heads, 256), np.float16)
+    big[:, 7] = 2048.0
+    big[:, 100] = -2048.0                                        # sign tie in a block
+    vs.append(big)
+    e = np.zeros((n_kv_heads, 256), np.float16)
+    e[:, :32] = np.arange(-8, 24)[:32].astype(np.float16) * 0.25   # integer multiples
+    vs.append(e)
+    return np.stack(vs)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_bitexact(gpu, fmt):
+    T = 700
+    k, v = kvsynth.kv_tokens_np(11, 0, 0, 0, T)
+    sp = special_vectors()
+    k[40:40 + len(sp)] = sp
+    v[300:300 + len(sp)] = sp
+    v[41:41 + len(sp)] = sp[::-1]
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    n_pool = 6
+    bt = np.array([4, 1, 3], np.int32)
+    rng = np.random.default_rng(5)
+    pool = to_dev(rng.integers(0, 256, n_pool * pb, dtype=np.uint8), gpu)
+    kd, vd = to_dev(k, gpu), to_dev(v, gpu)
+    btd = to_dev(bt, gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    for a, b in ((0, 1), (1, 18), (18, 300), (300, 301), (301, 512), (512, 700)):
+        K.append_quantize(s, kd[a:b].contiguous(), vd[a:b].contiguous(), a, btd, pool, status)
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    got_pages = pool.cpu().numpy().reshape(n_pool, pb)[bt]
+    kc, ks, vc, vs = oracle_records(k, v, fmt)
+    a, b_, c, d = layout.unpack_pages(got_pages, fmt_id(fmt), 4)
+    assert np.array_equal(a[:T], kc), "K codes"
+    assert np.array_equal(b_[:T].view(np.uint16), ks.view(np.uint16)), "K scales"
+    assert np.array_equal(c[:T], vc), "V codes"
+    assert np.array_equal(d[:T].view(np.uint16), vs.view(np.uint16)), "V scales"
+    # whole pages are byte-identical to the oracle's packing
+    want = layout.pack_pages(kc, ks, vc, vs, fmt_id(fmt))
+    assert np.array_equal(got_pages[:2], want[:2])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_bad_page_id_is_skipped_and_flagged(gpu, fmt):
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    k, v = kvsynth.kv_tokens_np(12, 0, 0, 0, 10)
+    pool = torch.zeros(2 * pb, dtype=torch.uint8, device=gpu)
+    status = torch.zeros(1, dtype=torch.int32, device=gpu)
+    K.append_quantize(s, to_dev(k, gpu), to_dev(v, gpu), 0, to_dev(np.array([7], np.int32), gpu), pool, status)
+    torch.cuda.synchronize()
+    assert status.item() & K.KV_STATUS_BAD_PAGE_ID
+    assert int(pool.sum().item()) == 0
+
+
+def run_decode(gpu, fmt, seqs, q, pps=0, seed=0, n_pool_extra=3):
+    s = K.shape(fmt, q.shape[1], seqs[0].k.shape[1])
+    pb = K.page_bytes(s)
+    n_pool = sum(x.n_pages for x in seqs) + n_pool_extra
+    pool_np, bt = place_pages(seqs, n_pool, seed, pb)
+    pool = to_dev(pool_np, gpu)
+    lens = np.array([x.T for x in seqs], np.int32)
+    max_ctx = int(max(lens.max(), 1))
+    ws = K.paged.DecodeWorkspace(s, len(seqs), max_ctx, pps, device=gpu)
+    out = torch.empty((len(seqs), q.shape[1], 256), dtype=torch.float32, device=gpu)
+    K.decode_attention(s, to_dev(q, gpu), pool, to_dev(bt, gpu), to_dev(lens, gpu), max_ctx, out,
+                       ws.data, pages_per_split=pps)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ws.status()
+
+
+CASES = [
+    ("T1", [1], 0), ("T2", [2], 0), ("T7", [7], 0), ("T8", [8], 0),
+    ("T255", [255], 0), ("T256", [256], 0), ("T257", [257], 0),
+    ("T1000_pps1", [1000], 1), ("T4096", [4096], 0), ("T4096_pps3", [4096], 3),
+    ("batch_mixed", [1000, 4096, 17, 0, 513], 2),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name, lens, pps", CASES, ids=[c[0] for c in CASES])
+def test_decode_matches_oracle(gpu, fmt, name, lens, pps):
+    seqs = [Sequence(21, 0, b, T, fmt) for b, T in enumerate(lens)]
+    q = kvsynth.q_np(21, 0, len(lens))
+    got, status = run_decode(gpu, fmt, seqs, q, pps, seed=len(lens) * 7 + pps)
+    assert status == 0
+    want = oracle_out(q, seqs, fmt)
+    assert_close(got, want, what=f"{fmt} {name}")
+    for b, T in enumerate(lens):
+        if T == 0:
+            assert np.array_equal(got[b], np.zeros_like(got[b]))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_split_and_placement_independence(gpu, fmt):
+    seqs = [Sequence(22, 1, 0, 3000, fmt)]
+    q = kvsynth.q_np(22, 1, 1)
+    want = oracle_out(q, seqs, fmt)
+    outs = {}
+    for pps in (1, 2, 4, 12):
+        got, _ = run_decode(gpu, fmt, seqs, q, pps, seed=1)
+        assert_close(got, want, what=f"pps {pps}")
+        outs[pps] = got
+    # same split, different physical placement: bitwise identical
+    again, _ = run_decode(gpu, fmt, seqs, q, 4, seed=99, n_pool_extra=9)
+    assert np.array_equal(again, outs[4])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_group_sizes(gpu, fmt):
+    """Other GQA groupings: 8, 1 and 3 query heads per KV head."""
+    for hq, hkv in ((16, 2), (4, 4), (6, 2)):
+        k, v = kvsynth.kv_tokens_np(23, hq, 0, 0, 600, hkv)
+        seqs = [Sequence(23, hq, 0, 600, fmt, hkv, k, v)]
+        q = kvsynth.q_np(23, hq, 1, hq)
+        got, _ = run_decode(gpu, fmt, seqs, q, 0, seed=hq)
+        assert_close(got, oracle_out(q, seqs, fmt), what=f"{hq}/{hkv}")
+
+
+def test_decode_flags_bad_page_and_clamped_context(gpu):
+    fmt = "q4_0"
+    seqs = [Sequence(24, 0, 0, 600, fmt)]
+    q = kvsynth.q_np(24, 0, 1)
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    pool_np, bt = place_pages(seqs, 5, 3, pb)
+    pool = to_dev(pool_np, gpu)
+    ws = K.paged.DecodeWorkspace(s, 1, 600, 1, device=gpu)
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+    bad = bt.copy()
+    bad[0, 1] = 1000
+    K.decode_attention(s, to_dev(q, gpu), pool, to_dev(bad, gpu), to_dev(np.array([600], np.int32), gpu),
+                       600, out, ws.data, pages_per_split=1)
+    torch.cuda.synchronize()
+    assert ws.status() & K.KV_STATUS_BAD_PAGE_ID
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    ws.clear_status()
+    # a context length above the declared bound is clamped to it and flagged
+    K.decode_attention(s, to_dev(q, gpu), pool, to_dev(bt, gpu), to_dev(np.array([650], np.int32), gpu),
+                       600, out, ws.data, pages_per_split=1)
+    torch.cuda.synchronize()
+    assert ws.status() & K.KV_STATUS_CONTEXT_CLAMPED
+    assert_close(out.cpu().numpy(), oracle_out(q, seqs, fmt))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_then_decode_end_to_end(gpu, fmt):
+    """Pool written by the append kernel (prefill chunk + decode steps), read by decode."""
+    T0, steps = 2000, 5
+    k, v = kvsynth.kv_tokens_np(25, 0, 0, 0, T0 + steps)
+    s = K.shape(fmt)
+    pool = K.paged.PagedPool(fmt, 12, device=gpu)
+    bt = to_dev(np.array([9, 2, 7, 0, 11, 5, 3, 1, 4, 6, 8, 10], np.int32), gpu)
+    kd, vd = to_dev(k, gpu), to_dev(v, gpu)
+    pool.append(kd[:T0].contiguous(), vd[:T0].contiguous(), 0, bt)
+    ws = K.paged.DecodeWorkspace(s, 1, T0 + steps, 0, device=gpu)
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+    for st in range(steps):
+        T = T0 + st + 1
+        pool.append(kd[T - 1:T].contiguous(), vd[T - 1:T].contiguous(), T - 1, bt)
+        q = kvsynth.q_np(25, 0, 1, step=st)
+        K.decode_attention(s, to_dev(q, gpu), pool.data, bt[None].contiguous(),
+                           to_dev(np.array([T], np.int32), gpu), T0 + steps, out, ws.data)
+        torch.cuda.synchronize()
+        seq = Sequence(25, 0, 0, T, fmt, k=k[:T], v=v[:T])
+        assert_close(out.cpu().numpy(), oracle_out(q, [seq], fmt), what=f"step {st}")

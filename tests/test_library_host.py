@@ -1,0 +1,160 @@
+"""CPU tests of the HIP library: it loads, exports every declared symbol, and its
+host-side logic (rounding, record rules, CLOCK table, argument checks) matches
+the oracle. No GPU work is launched here."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import offloaded_kv_cache_amd as K
+from offloaded_kv_cache_amd import _native as N
+from oracle import records
+from oracle.residency import ClockTable
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvcache.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(N.lib, n), n
+    assert set(names) == set(N.EXPORTED_SYMBOLS)
+
+
+def test_version_and_page_bytes():
+    assert re.match(r"\d+\.\d+\.\d+", K.version())
+    assert K.page_bytes(K.shape("int8")) == 540672
+    assert K.page_bytes(K.shape("q4_0")) == 294912
+    assert K.page_bytes(K.shape("k8v4")) == 417792
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(head_dim=128), N.KV_EUNSUPPORTED),
+    (dict(page_tokens=128), N.KV_EUNSUPPORTED),
+    (dict(n_q_heads=25), N.KV_EINVAL),
+    (dict(n_q_heads=40, n_kv_heads=4), N.KV_EUNSUPPORTED),
+])
+def test_shape_validation(bad, code):
+    args = dict(n_q_heads=24, n_kv_heads=4, head_dim=256, page_tokens=256)
+    args.update(bad)
+    s = N.KVShape(args["n_q_heads"], args["n_kv_heads"], args["head_dim"], args["page_tokens"], 1)
+    assert N.lib.kv_page_bytes(C.byref(s)) == code
+    assert N.last_error()
+    s.format = 7
+    s.head_dim, s.page_tokens, s.n_q_heads, s.n_kv_heads = 256, 256, 24, 4
+    assert N.lib.kv_page_bytes(C.byref(s)) == N.KV_EINVAL
+
+
+def test_f64_to_f16_matches_single_rounding():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24, 2.0 ** -25,
+         2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -12),
+         1 + 2.0 ** -11, 1 + 2.0 ** -11 + 2.0 ** -30, 1 + 3 * 2.0 ** -11, np.inf, -np.inf],
+    ])
+    want = records.fp16_rne(vals).view(np.uint16)
+    got = np.array([N.host_f64_to_f16(v) for v in vals], np.uint16)
+    assert np.array_equal(got, want)
+    assert N.host_f64_to_f16(np.nan) & 0x7C00 == 0x7C00
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_host_records_match_oracle(kind):
+    rng = np.random.default_rng(10 + kind)
+    xs = [(rng.standard_normal(256) * np.where(rng.random(256) < 0.03, 20, 1)).astype(np.float16)
+          for _ in range(150)]
+    z = np.zeros(256, np.float16)
+    xs.append(z)
+    t = np.zeros(256, np.float16)
+    t[0] = 127 / 16
+    t[1:5] = [2.5 / 16, -2.5 / 16, 0.5 / 16, -0.5 / 16]
+    xs.append(t)
+    xs.append(np.full(256, np.float16(2.0 ** -24)))
+    for x in xs:
+        codes, scales = N.host_encode_vector(kind, x)
+        if kind == 0:
+            c, d = records.quantize_int8(x.astype(np.float64))
+            assert np.array_equal(codes.view(np.int8), c)
+        else:
+            c, d = records.quantize_q4(x.astype(np.float64))
+            assert np.array_equal(codes, c)
+        assert np.array_equal(scales.view(np.uint16), d.view(np.uint16))
+
+
+def test_clock_matches_oracle_on_random_traces():
+    rng = np.random.default_rng(3)
+    for n_slots, n_pages in ((4, 10), (16, 300), (128, 4096)):
+        a, b = K.Residency(n_slots, n_pages), ClockTable(n_slots, n_pages)
+        for _ in range(200):
+            sel = rng.choice(n_pages, int(rng.integers(0, n_slots + 1)), replace=False)
+            sa, ca = a.select(sel)
+            sb, cb = b.select(sel)
+            assert list(sa) == list(sb) and ca == cb
+            assert a.hand == b.hand
+            assert list(a.slot_page) == b.slot_page and list(a.ref) == b.ref
+
+
+def test_clock_errors_leave_table_unchanged():
+    t = K.Residency(4, 10)
+    t.select([0, 1, 2])
+    snap = (t.slot_page.copy(), t.page_slot.copy(), t.ref.copy(), t.hand)
+    for sel, code in (([0, 1, 2, 3, 4], N.KV_ENOSLOTS), ([1, 1], N.KV_EINVAL), ([10], N.KV_EINVAL),
+                      ([-1], N.KV_EINVAL)):
+        with pytest.raises(K.KVError) as e:
+            t.select(sel)
+        assert e.value.code == code
+        assert np.array_equal(t.slot_page, snap[0]) and np.array_equal(t.page_slot, snap[1])
+        assert np.array_equal(t.ref, snap[2]) and t.hand == snap[3]
+
+
+def test_abi_argument_errors_enqueue_nothing():
+    s = K.shape("q4_0")
+    P = C.c_void_p
+    # NULL buffers are refused before any HIP call
+    r = N.lib.kv_decode_attention(C.byref(s), None, 1, None, 1, None, 1, None, 4096, 0.0625, None,
+                                  None, 0, 0, None)
+    assert r == N.KV_EINVAL
+    r = N.lib.kv_append_quantize(C.byref(s), None, None, 1, 0, None, 1, None, 1, None, None)
+    assert r == N.KV_EINVAL
+    # zero tokens / zero batch are no-ops
+    assert N.lib.kv_append_quantize(C.byref(s), None, None, 0, 0, None, 0, None, 0, None, None) == 0
+    assert N.lib.kv_decode_attention(C.byref(s), None, 0, None, 0, None, 0, None, 0, 0.0625, None,
+                                     None, 0, 0, None) == 0
+    # a token range past the block table
+    r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), 300, 0, P(16), 1, P(256), 4, None, None)
+    assert r == N.KV_EINVAL and "do not fit" in N.last_error()
+    # misaligned pool
+    r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), 10, 0, P(16), 1, P(258), 4, None, None)
+    assert r == N.KV_EALIGN
+    # workspace too small
+    need = K.decode_workspace_bytes(s, 1, 4096)
+    r = N.lib.kv_decode_attention(C.byref(s), P(256), 1, P(256), 16, P(256), 16, P(256), 4096, 0.0625,
+                                  P(256), P(256), need - 1, 0, None)
+    assert r == N.KV_ESMALL
+    # a gather selection larger than the slot pool
+    t = K.Residency(2, 10)
+    sel = np.array([1, 2, 3], np.int32)
+    r = N.lib.kv_gather_pages(C.byref(s), C.byref(t.c), sel.ctypes.data_as(P), 3, P(256), P(256),
+                              P(256), None, None)
+    assert r == N.KV_ENOSLOTS
+
+
+def test_workspace_grows_with_context_and_split():
+    s = K.shape("q4_0")
+    a = K.decode_workspace_bytes(s, 1, 4096, 4)
+    b = K.decode_workspace_bytes(s, 1, 131072, 4)
+    c = K.decode_workspace_bytes(s, 1, 131072, 1)
+    assert a < b < c
+    # status word + per-split (m, l) + 256 outputs, for 24 heads
+    assert b >= 256 + 24 * 128 * (2 + 256) * 4
