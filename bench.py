@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the quantized, paged KV cache on one MI355X.
+
+Default workload (the headline metric, "KV GB/s streamed in decode attention
+(% of 8 TB/s HBM) at 128K q4_0"): 16 full-attention layers, 24 query / 4 KV
+heads, head_dim 256, batch 1, q4_0 KV in 256-token pages, context growing to
+131,072 tokens. One step = for every layer, quantize-on-append of the step's
+new K/V token, then split-K decode attention (query rotation, Q.K, online
+softmax, P.V, log-sum-exp combine, rotation back) over the whole context.
+
+Inputs are synthetic (seeded; K, V ~ N(0,1) with 4 outlier channels x20 per
+head, Q ~ N(0,1)), drawn on the GPU and resident in HBM before timing.
+
+Prints one JSON line. `value` is algorithmic KV bytes read by attention per
+second over the timed steps (wall time of the whole step, appends and
+combines included). `roofline` is for the dominant kernel (the split-K
+decode kernel), timed with HIP events around each of its launches on the
+launch stream, inside the timed region. `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+
+Other workloads (parity-test shapes, not the metric line): --workload c1
+(1 layer, 4,096 tokens, q4_0), c2 (16 layers, 32,768, int8), c4 (16 layers,
+4 sequences of 262,144 / 198,000 / 65,536 / 8,192 tokens, k8v4), c5
+(16 layers, 1,048,576-token int8 host pool, 128 resident slots per layer,
+2,048-token selection per step with ~30% misses, gathered zero-copy).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PAGE = 256
+
+WORKLOADS = {
+    "c1": dict(fmt="q4_0", layers=1, lens=[4096], cfg=1),
+    "c2": dict(fmt="int8", layers=16, lens=[32768], cfg=2),
+    "c3": dict(fmt="q4_0", layers=16, lens=[131072], cfg=3),
+    "c4": dict(fmt="k8v4", layers=16, lens=[262144, 198000, 65536, 8192], cfg=4),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_token(fmt: str, n_kv_heads: int = 4) -> int:
+    rec = {"int8": (264, 264), "q4_0": (144, 144), "k8v4": (264, 144)}[fmt]
+    return n_kv_heads * sum(rec)
+
+
+def build_resident(args, wl, dev):
+    import torch
+
+    import kvsynth
+    import offloaded_kv_cache_amd as K
+
+    fmt, L, lens, cfg = wl["fmt"], wl["layers"], wl["lens"], wl["cfg"]
+    B = len(lens)
+    n_steps = args.warmup + args.steps
+    end_lens = lens
+    start_lens = [max(1, T - n_steps) for T in end_lens]
+    pages_per_seq = [-(-T // PAGE) for T in end_lens]
+    n_pool = sum(pages_per_seq)
+    max_pages = max(pages_per_seq)
+    s = K.shape(fmt)
+    pools, tables = [], []
+    append_ev = []
+    chunk = 2048
+    for layer in range(L):
+        pool = K.paged.PagedPool(fmt, n_pool, device=dev)
+        perm = torch.from_numpy(kvsynth.permutation_np(1000 * cfg + layer, n_pool)).to(dev)
+        bt = torch.zeros((B, max_pages), dtype=torch.int32, device=dev)
+        off = 0
+        for b in range(B):
+            bt[b, :pages_per_seq[b]] = perm[off:off + pages_per_seq[b]]
+            off += pages_per_seq[b]
+        gain = kvsynth.gain_torch(cfg, layer, 4, dev)
+        for b in range(B):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(kvsynth.torch_seed(cfg, layer, b))
+            row = bt[b].contiguous()
+            for t0 in range(0, start_lens[b], chunk):
+                n = min(chunk, start_lens[b] - t0)
+                k, v = kvsynth.kv_tokens_torch(gen, n, gain, dev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                pool.append(k, v, t0, row)
+                e1.record()
+                if n == chunk:
+                    append_ev.append((e0, e1))
+        pools.append(pool)
+        tables.append(bt)
+        torch.cuda.synchronize()
+        log(f"layer {layer}: prefilled {start_lens} tokens")
+    return s, pools, tables, start_lens, max_pages, append_ev
+
+
+def run_resident(args, wl, dev):
+    import torch
+
+    import kvsynth
+    import offloaded_kv_cache_amd as K
+
+    fmt, L, lens, cfg = wl["fmt"], wl["layers"], wl["lens"], wl["cfg"]
+    B = len(lens)
+    s, pools, tables, start_lens, max_pages, append_ev = build_resident(args, wl, dev)
+    torch.cuda.synchronize()
+    app_ms = [a.elapsed_time(b) for a, b in append_ev]
+    n_steps = args.warmup + args.steps
+    max_ctx = max(lens)
+    # step inputs, drawn up front and resident in HBM
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(kvsynth.torch_seed(cfg, 99))
+    q_all = torch.randn((n_steps, L, B, 24, 256), generator=gen, device=dev).to(torch.float16)
+    knew = torch.randn((n_steps, L, B, 1, 4, 256), generator=gen, device=dev).to(torch.float16)
+    vnew = torch.randn((n_steps, L, B, 1, 4, 256), generator=gen, device=dev).to(torch.float16)
+    ctx = torch.tensor([[start_lens[b] + st + 1 for b in range(B)] for st in range(n_steps)],
+                       dtype=torch.int32, device=dev)
+    ws = K.paged.DecodeWorkspace(s, B, max_ctx, args.pages_per_split, device=dev)
+    out = torch.empty((B, 24, 256), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    per_tok = kv_bytes_per_token(fmt)
+    timed_split = []
+
+    def step(st, timing):
+        for layer in range(L):
+            for b in range(B):
+                T = start_lens[b] + st + 1
+                pools[layer].append(knew[st, layer, b], vnew[st, layer, b], T - 1,
+                                    tables[layer][b].contiguous() if B > 1 else tables[layer][0])
+            if timing:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
+                               out, ws.data, pages_per_split=args.pages_per_split, phase="split")
+            if timing:
+                e1.record(stream)
+                timed_split.append((e0, e1, sum(start_lens[b] + st + 1 for b in range(B)) * per_tok))
+            K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
+                               out, ws.data, pages_per_split=args.pages_per_split, phase="combine")
+
+    for st in range(args.warmup):
+        step(st, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.warmup, n_steps):
+        step(st, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"decode status word {ws.status()}")
+    kv_bytes = sum(sum(start_lens[b] + st + 1 for b in range(B)) * per_tok * L
+                   for st in range(args.warmup, n_steps))
+    split_ms = [a.elapsed_time(b) for a, b, _ in timed_split]
+    split_bytes = [x for _, _, x in timed_split]
+    achieved = sum(split_bytes) / (sum(split_ms) * 1e-3) / 1e9
+    res = dict(
+        value=kv_bytes / wall / 1e9,
+        ms_per_step=wall / args.steps * 1e3,
+        split_us=sum(split_ms) / len(split_ms) * 1e3,
+        split_bytes=sum(split_bytes) / len(split_bytes),
+        achieved=achieved,
+        append_chunk_us=(sum(app_ms) / len(app_ms) * 1e3) if app_ms else None,
+        n_append_chunks=len(app_ms),
+        pages_per_split=args.pages_per_split,
+    )
+    return res, (s, pools, tables, start_lens)
+
+
+def cpu_baseline(args, wl, dev, state):
+    """Time the fp64 oracle (as it stands) on one layer's records of the same inputs."""
+    import numpy as np
+    import torch
+
+    import kvsynth
+    from oracle import attention, records
+
+    fmt, cfg = wl["fmt"], wl["cfg"]
+    fmt_id = records.FORMATS[fmt]
+    kk, vk = records.kinds(fmt_id)
+    T = min(args.cpu_tokens, wl["lens"][0])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(kvsynth.torch_seed(cfg, 0, 0))
+    gain = kvsynth.gain_torch(cfg, 0, 4, dev)
+    ks, vs = [], []
+    for t0 in range(0, T, 2048):
+        k, v = kvsynth.kv_tokens_torch(gen, min(2048, T - t0), gain, dev)
+        ks.append(k.cpu().numpy())
+        vs.append(v.cpu().numpy())
+    k = np.concatenate(ks)
+    v = np.concatenate(vs)
+    q = torch.randn((1, 24, 256), generator=gen, device=dev).to(torch.float16).cpu().numpy()[0]
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = None
+    # records (the append side), then the timed attention sample: dequantize + attention
+    t0 = time.perf_counter()
+    kc, ksc = records.encode(k[:2048].astype(np.float64), kk)
+    vc, vsc = records.encode(v[:2048].astype(np.float64), vk)
+    quant_s = time.perf_counter() - t0
+    kc, ksc = records.encode(k.astype(np.float64), kk)
+    vc, vsc = records.encode(v.astype(np.float64), vk)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        def get_kv(a, b):
+            return records.decode(kc[a:b], ksc[a:b], kk), records.decode(vc[a:b], vsc[a:b], vk)
+        attention.decode_attention_chunked(q, get_kv, T, 4, fmt_id)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or reps >= 8:
+            break
+    gbs = T * kv_bytes_per_token(fmt) * reps / el / 1e9
+    return dict(value=gbs, unit="GB/s", cores=threads or os.cpu_count(), kind="oracle",
+                sample=f"1 layer x {T} tokens of the same workload, fp64 dequantize + attention, "
+                       f"{reps} pass(es) in {el:.1f} s; oracle quantizer on a 2,048-token chunk "
+                       f"(4 KV heads, K and V): {quant_s:.2f} s",
+                host_cpus=len(os.sched_getaffinity(0)))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--pages-per-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures the single-GPU decode path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    res, state = run_resident(args, wl, dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, wl, dev, state)
+    fmt = wl["fmt"]
+    line = {
+        "metric": "KV GB/s streamed in decode attention (% of 8 TB/s HBM) at 128K q4_0",
+        "value": round(res["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"q4_0": "q4_0 KV, fp32 accumulate", "int8": "int8 KV, fp32 accumulate",
+                  "k8v4": "int8 K / q4_0 V, fp32 accumulate"}[fmt],
+        "data": "synthetic",
+        "config": {"workload": {"c1": "1 layer, 4,096-token q4_0 context",
+                                "c2": "16 layers, 32,768-token int8 context",
+                                "c3": "16 layers, 131,072-token q4_0 context (append 1 token + decode per layer)",
+                                "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4"}[args.workload],
+                   "layers": wl["layers"], "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256,
+                   "page_tokens": 256, "batch": len(wl["lens"]), "context": wl["lens"],
+                   "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto"},
+        "pct_of_hbm_peak": round(100 * res["value"] / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(res["achieved"], 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(res["split_us"], 3),
+                     "bytes_per_launch": int(res["split_bytes"])},
+        "append_2048_chunk_us": round(res["append_chunk_us"], 3) if res["append_chunk_us"] else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -182,6 +182,29 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
                         int32_t pages_per_split, void* stream);
 
 /*
+ * The two phases of kv_decode_attention, for callers that schedule them
+ * separately (e.g. to time or overlap them). Same arguments and checks as
+ * kv_decode_attention; kv_decode_split enqueues only the split-K kernel
+ * (partials into the workspace), kv_decode_combine only the log-sum-exp
+ * combine and rotation back (partials to `out`). Calling them in this order
+ * on one stream with identical arguments is exactly kv_decode_attention.
+ */
+int kv_decode_split(const kv_shape* shape, const void* q, int32_t batch,
+                    const void* pool, int64_t n_pool_pages,
+                    const int32_t* block_tables, int32_t max_pages,
+                    const int32_t* context_lens, int64_t max_context,
+                    float softmax_scale, float* out,
+                    void* workspace, size_t workspace_bytes,
+                    int32_t pages_per_split, void* stream);
+int kv_decode_combine(const kv_shape* shape, const void* q, int32_t batch,
+                      const void* pool, int64_t n_pool_pages,
+                      const int32_t* block_tables, int32_t max_pages,
+                      const int32_t* context_lens, int64_t max_context,
+                      float softmax_scale, float* out,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t pages_per_split, void* stream);
+
+/*
  * Residency table of one layer's device page slots (Strata page, section
  * "KV 从显存搬进内存之后发生了什么": a residency table with CLOCK second-chance
  * eviction). Plain host memory owned by the caller:

@@ -5,7 +5,7 @@ The hot path lives in the HIP library ``lib/libkvcache.so`` (C ABI in
 q4_0, k8v4), split-K decode attention with the rotation back, and a
 CLOCK-managed zero-copy page gather from pinned host memory. This package is
 the thin Python binding over it; it raises ImportError if the library has
-not been built (``python -m offloaded_kv_cache_amd.build``).
+not been built (``python offloaded_kv_cache_amd/build.py``).
 """
 
 from ._native import (  # noqa: F401

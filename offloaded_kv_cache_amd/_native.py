@@ -23,7 +23,8 @@ FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4}
 
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
-    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_residency_reset",
+    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_decode_split", "kv_decode_combine",
+    "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
 )
 
@@ -48,7 +49,7 @@ class KVError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
-                          "(run `python -m offloaded_kv_cache_amd.build`)")
+                          "(run `python offloaded_kv_cache_amd/build.py`)")
     lib = C.CDLL(LIB_PATH)
     P, I32, I64, SZ, F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
     sig = {
@@ -59,6 +60,10 @@ def _load():
         "kv_decode_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I64, I32]),
         "kv_decode_attention": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                           P, P, SZ, I32, P]),
+        "kv_decode_split": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
+                                      P, P, SZ, I32, P]),
+        "kv_decode_combine": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
+                                        P, P, SZ, I32, P]),
         "kv_residency_reset": (C.c_int, [C.POINTER(KVResidency)]),
         "kv_residency_select": (C.c_int, [C.POINTER(KVResidency), P, I32, P, P, P, P]),
         "kv_gather_pages": (C.c_int, [C.POINTER(KVShape), C.POINTER(KVResidency), P, I32, P, P, P,
@@ -154,18 +159,24 @@ def decode_workspace_bytes(s: KVShape, batch: int, max_context: int, pages_per_s
     return int(r)
 
 
+_PHASES = {"all": "kv_decode_attention", "split": "kv_decode_split", "combine": "kv_decode_combine"}
+
+
 def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
                      workspace, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
-                     stream=None):
-    """GQA decode attention over the paged cache; writes fp32 ``out`` [B, Hq, 256]."""
+                     stream=None, phase: str = "all"):
+    """GQA decode attention over the paged cache; writes fp32 ``out`` [B, Hq, 256].
+
+    ``phase`` = "split" or "combine" enqueues only that kernel (see kvcache.h)."""
     torch = _torch()
+    fn = getattr(lib, _PHASES[phase])
     B = q.shape[0]
     if q.shape != (B, s.n_q_heads, s.head_dim) or out.shape != (B, s.n_q_heads, s.head_dim):
         raise ValueError("q and out must be [batch, n_q_heads, head_dim]")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
     pb = page_bytes(s)
-    _check(lib.kv_decode_attention(
+    _check(fn(
         C.byref(s), _ptr(q, torch.float16, name="q"), B, C.c_void_p(pool.data_ptr()),
         pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,

@@ -10,33 +10,47 @@
 // dequantized records, then H for rotated V.
 //
 // Kernel 1 (decode_split): one workgroup of four wavefronts per (split, KV
-// head, sequence). A split is `pages_per_split` consecutive logical pages;
-// wave w takes pages w, w+4, ... of it, one whole 256-token page at a time:
-//   - Q.K on MFMA 16x16x32 f16. A = the rotated query of the group's heads,
-//     each head as two fp16 rows (hi, lo) so the fp32 query is carried to
-//     ~22 bits; B = 16 tokens x 32 elements of exact integer codes (q4: c-8,
-//     int8: c), unpacked with bit tricks (1024 + c as fp16, then a packed
-//     fp16 subtract). One MFMA covers one 32-element block, so the block (q4)
-//     or group (int8) scale is applied to the fp32 accumulators afterwards.
-//   - online softmax over the page in the log2 domain, with the wave's
-//     running max and sum; probabilities are scaled by 2^14 and split into
-//     fp16 hi/lo parts, kept in LDS.
-//   - P.V on MFMA 16x16x32 f16 with the contraction over tokens. The V plane
-//     is element-major, so a lane's 8 k-slots are 8 tokens of one element:
-//     one dword of q4 codes (two 4-token runs) or two dwords of int8 codes.
-//     The per-token scale d varies along the contraction, so it goes into B
-//     exactly: d is split into parts with few enough bits that every
-//     (code x part) product is exact in fp16 (q4: two parts of <= 8 and 3
-//     bits; int8: three parts of <= 4 bits), one MFMA per part.
-//   - the four waves merge their (max, sum, output) in LDS and the workgroup
-//     writes one partial per query head.
+// head, sequence). A split is `pages_per_split` consecutive logical pages,
+// processed one 256-token page at a time by the whole workgroup: wave w
+// computes the scores of tokens 64w..64w+63 and the outputs of head elements
+// 64w..64w+63. Each wave holds its share of the next page in registers while
+// it works on the current one, so HBM latency is hidden behind the math.
+//
+//   Q.K on MFMA 16x16x32 f16. A = the query of the group's heads (rotated by H
+//   for q4 K), each head as two fp16 rows (hi, lo) carrying ~22 bits. B = 16
+//   tokens x 32 elements of raw codes taken as fp16 subnormals: a 4-bit code c
+//   sits in the low bits of a half and is worth c * 2^-24 (a nibble at bits
+//   4..7 is worth 16c * 2^-24, so its A slot holds q/16); int8 codes are
+//   offset to c + 128 and placed the same way. One MFMA is one 32-element
+//   block, scaled afterwards by that block's (q4) or group's (int8) fp16 scale.
+//   The offsets (8 for q4, 128 for int8) are removed with one more MFMA per
+//   tile that forms sum_j d_j * Q_j, Q_j the block sums of the query.
+//
+//   Online softmax in the log2 domain with a workgroup-wide maximum per page
+//   (wave maxima exchanged through LDS). Probabilities are scaled by 2^14,
+//   split into fp16 hi/lo and written straight into the A-fragment layout of
+//   the P.V MFMA.
+//
+//   P.V on MFMA 16x16x32 f16, contraction over tokens. The V plane is
+//   element-major, so a lane's 8 k-slots are 8 tokens of one element (two
+//   4-token runs of q4 nibbles, or 8 int8 bytes). The per-token scale d varies
+//   along the contraction, so it is folded into B exactly: d is split into
+//   parts with few enough bits that every code x part product is exact in
+//   fp16, and each part is applied with one packed fp16 fma on a "1024 + code"
+//   half (q4: B = (1024 + 16c) * (p/16) - 72p = (c - 8) p, parts of <= 7 and
+//   4 bits; int8: B = (1024 + c + 128) * p - 1152p = c p, three parts of <= 4
+//   bits). One MFMA per part. Scales too large for these constants (|d| >= 896
+//   for q4, >= 56 for int8) take a slower exact path for that page.
+//
+//   The four waves then share the page maximum and sum; each writes its
+//   elements of the split's partial (max, sum, unnormalised output).
+//
 // Kernel 2 (decode_combine): per (query head, sequence), the log-sum-exp
-// merge of the partials, then the rotation back by H (fp32 butterflies) when
-// V is stored rotated.
+// merge of the partials, then the rotation back by H when V is rotated.
 //
 // Tokens past the context length are masked (score -inf, scale 0), so stale
-// or uninitialised rows of a last, partly filled page never contribute.
-// Nothing depends on the physical page ids except the addresses read.
+// or uninitialised rows of a partly filled page never contribute. Nothing
+// depends on the physical page ids except the addresses read.
 #include "kv_internal.h"
 
 namespace kvc {
@@ -51,36 +65,24 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr float kPScale = 16384.0f;  // probabilities are kept as p * 2^14 in fp16 hi/lo
 constexpr float kPScaleInv = 1.0f / 16384.0f;
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kQ4FastMax = 896.0f;   // |d| below this: -72 * d_hi is exact and finite
+constexpr float kI8FastMax = 56.0f;    // |d| below this: -1152 * d_part is exact and finite
+constexpr int kWaves = 4;
 
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
-
-// Eight 4-bit codes (bytes b0..b3, low and high nibbles) -> c - 8 as fp16,
-// slot order [lo0, lo1, lo2, lo3, hi0, hi1, hi2, hi3].
-__device__ inline h8 unpack_q4(uint32_t x) {
-  const uint32_t t01 = (x & 0xFFu) | ((x << 8) & 0xFF0000u);          // halves (b0, b1)
-  const uint32_t t23 = ((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u);  // halves (b2, b3)
-  const h2 lo01 = as_h2((t01 & 0x000F000Fu) | 0x64006400u) - (h2){1032, 1032};
-  const h2 lo23 = as_h2((t23 & 0x000F000Fu) | 0x64006400u) - (h2){1032, 1032};
-  // high nibble sits at bits 4..7: 1024 + 16c, scaled by 1/16 and shifted: c - 8
-  const h2 hi01 = __builtin_elementwise_fma(as_h2((t01 & 0x00F000F0u) | 0x64006400u),
-                                            (h2){0.0625, 0.0625}, (h2){-72, -72});
-  const h2 hi23 = __builtin_elementwise_fma(as_h2((t23 & 0x00F000F0u) | 0x64006400u),
-                                            (h2){0.0625, 0.0625}, (h2){-72, -72});
-  return (h8){lo01[0], lo01[1], lo23[0], lo23[1], hi01[0], hi01[1], hi23[0], hi23[1]};
-}
-
-// Eight int8 codes (x0 bytes 0..3, x1 bytes 4..7) -> fp16, natural order.
-__device__ inline h8 unpack_i8(uint32_t x0, uint32_t x1) {
-  const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;  // c + 128
-  const h2 a = as_h2((u0 & 0xFFu) | ((u0 << 8) & 0xFF0000u) | 0x64006400u) - (h2){1152, 1152};
-  const h2 b = as_h2(((u0 >> 16) & 0xFFu) | ((u0 >> 8) & 0xFF0000u) | 0x64006400u) - (h2){1152, 1152};
-  const h2 c = as_h2((u1 & 0xFFu) | ((u1 << 8) & 0xFF0000u) | 0x64006400u) - (h2){1152, 1152};
-  const h2 d = as_h2(((u1 >> 16) & 0xFFu) | ((u1 >> 8) & 0xFF0000u) | 0x64006400u) - (h2){1152, 1152};
-  return (h8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
+__device__ inline uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 
 __device__ inline f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// A value kept in a VGPR, opaque to constant folding, so that (x & m) | v
+// becomes one v_and_or_b32 inside the hot loops.
+__device__ inline uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
 }
 
 __device__ inline float half_max(float v) {  // max over the 16 lanes of a lane group
@@ -98,34 +100,26 @@ __device__ inline float half_sum(float v) {
   return v;
 }
 
-// LDS of one wave while it works on a page.
-//   sp:     first the page's scores (fp32 bits, log2 domain), then in place
-//           p * 2^14 as two fp16 halves (hi | lo << 16), per head and token
-//   dsplit: the page's V scales split into exact fp16 parts, per 4-token run:
-//           q4   [8 blocks][64 runs][8]  = {hi x 4 tokens, lo x 4 tokens}
-//           int8 [4 groups][64 runs][16] = {a x 4, b x 4, c x 4, pad x 4}
-struct WaveLds {
-  uint32_t sp[kMaxGroup][kPageTokens];
-  _Float16 dsplit[4096];
-};
-__device__ inline int dsplit_q4(int blk, int run) { return (blk * 64 + run) * 8; }
-__device__ inline int dsplit_i8(int grp, int run) { return (grp * 64 + run) * 16; }
-static_assert(sizeof(WaveLds) == 16384, "wave LDS");
+// ---- Q.K operands --------------------------------------------------------
 
-struct MergeLds {
-  float m[4][kMaxGroup];
-  float l[4][kMaxGroup];
-  float o[4][kMaxGroup][kHeadDim];
-};
-
-constexpr int kWaves = 4;
-constexpr size_t kSplitLds = (sizeof(WaveLds) * kWaves > sizeof(MergeLds) ? sizeof(WaveLds) * kWaves
-                                                                         : sizeof(MergeLds));
+// Eight 4-bit codes of one dword (bytes w = 0..3, low nibble = element 4s+w,
+// high nibble = element 16+4s+w of a block) as fp16 subnormals; slot order
+// [lo0, lo2, hi0, hi2, lo1, lo3, hi1, hi3], high nibbles worth 16c.
+__device__ inline h8 k_codes_q4(uint32_t x) {
+  const uint32_t y = x >> 8;
+  return __builtin_bit_cast(h8, (u4){x & 0x000F000Fu, x & 0x00F000F0u, y & 0x000F000Fu, y & 0x00F000F0u});
+}
+// Eight int8 codes (x0 bytes 0..3, x1 bytes 4..7) as fp16 subnormals of c + 128, in order.
+__device__ inline h8 k_codes_i8(uint32_t x0, uint32_t x1) {
+  const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
+  return __builtin_bit_cast(h8, (u4){__builtin_amdgcn_perm(0u, u0, 0x0c010c00u), __builtin_amdgcn_perm(0u, u0, 0x0c030c02u),
+                                     __builtin_amdgcn_perm(0u, u1, 0x0c010c00u), __builtin_amdgcn_perm(0u, u1, 0x0c030c02u)});
+}
 
 // One 16-token tile of a K plane, as loaded by one lane (token = its column).
 struct KTile {
   u4 c0, c1, c2, c3;  // code bytes of the lane's slice (q4: c0, c1; int8: all four)
-  u4 d;               // the token's scales (q4: 8 fp16; int8: 4 fp16 in d.xy)
+  u4 d;               // the token's scales (q4: 8 fp16; int8: 4 fp16 in d.xy, d.zw = 0)
 };
 
 template <int KK>
@@ -154,39 +148,113 @@ __device__ inline float scale_at(u4 d, int j) {  // fp16 scale j of a packed row
   return (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
-// Raw scores of one tile for the lane's two heads (rows 4grp..4grp+3 = head 2grp hi, lo,
-// head 2grp+1 hi, lo).
+// Scores of one tile for the lane's two heads (rows 4grp..4grp+3 = head 2grp
+// hi, lo, head 2grp+1 hi, lo), in units of q.k (before the softmax scale).
 template <int KK>
-__device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], float& s0, float& s1) {
-  s0 = 0.f;
-  s1 = 0.f;
+__device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], h8 qc, float& s0, float& s1) {
+  float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;  // hi and lo rows, units of 2^-24
   if (KK == kQ4) {
     const uint32_t w[8] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3]};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const f4 acc = mfma(qa[j], unpack_q4(w[j]), (f4){0.f, 0.f, 0.f, 0.f});
+      const f4 acc = mfma(qa[j], k_codes_q4(w[j]), (f4){0.f, 0.f, 0.f, 0.f});
       const float d = scale_at(t.d, j);
-      s0 = fmaf(d, acc[0] + acc[1], s0);
-      s1 = fmaf(d, acc[2] + acc[3], s1);
+      a0 = fmaf(d, acc[0], a0);
+      b0 = fmaf(d, acc[1], b0);
+      a1 = fmaf(d, acc[2], a1);
+      b1 = fmaf(d, acc[3], b1);
     }
   } else {
     const uint32_t w[16] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3],
                             t.c2[0], t.c2[1], t.c2[2], t.c2[3], t.c3[0], t.c3[1], t.c3[2], t.c3[3]};
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
-      f4 acc = mfma(qa[2 * gg], unpack_i8(w[4 * gg], w[4 * gg + 1]), (f4){0.f, 0.f, 0.f, 0.f});
-      acc = mfma(qa[2 * gg + 1], unpack_i8(w[4 * gg + 2], w[4 * gg + 3]), acc);
+      f4 acc = mfma(qa[2 * gg], k_codes_i8(w[4 * gg], w[4 * gg + 1]), (f4){0.f, 0.f, 0.f, 0.f});
+      acc = mfma(qa[2 * gg + 1], k_codes_i8(w[4 * gg + 2], w[4 * gg + 3]), acc);
       const float d = scale_at(t.d, gg);
-      s0 = fmaf(d, acc[0] + acc[1], s0);
-      s1 = fmaf(d, acc[2] + acc[3], s1);
+      a0 = fmaf(d, acc[0], a0);
+      b0 = fmaf(d, acc[1], b0);
+      a1 = fmaf(d, acc[2], a1);
+      b1 = fmaf(d, acc[3], b1);
     }
+  }
+  // sum_j d_j * Q_j per head (hi, lo rows), for the code offsets
+  const f4 corr = mfma(qc, __builtin_bit_cast(h8, t.d), (f4){0.f, 0.f, 0.f, 0.f});
+  const float off = KK == kQ4 ? 8.0f : 128.0f;
+  s0 = fmaf(a0 + b0, kTwo24, -off * (corr[0] + corr[1]));
+  s1 = fmaf(a1 + b1, kTwo24, -off * (corr[2] + corr[3]));
+}
+
+// ---- V share and P.V operands ---------------------------------------------
+
+// The wave's share of a page's V plane: head elements 64w..64w+63 (four MFMA
+// column tiles), all 256 tokens, plus the scales the wave turns into B parts.
+template <int VK>
+struct VShare {
+  u4 c[4][VK == kQ4 ? 2 : 4];  // per column tile: the lane's 32 (q4) / 64 (int8) code bytes
+  u2 s0, s1;                   // q4: 4 + 4 token scales; int8: s0, s1 = 8 consecutive scales
+};
+
+template <int VK>
+__device__ inline void load_vshare(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
+  const int grp = lane >> 4, col = lane & 15;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    const int e = 64 * wave + 16 * nt + col;
+    const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)e * code_row_bytes(VK) +
+                                                (VK == kQ4 ? 32 : 64) * grp);
+#pragma unroll
+    for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = src[u];
+  }
+  const uint16_t* vs = reinterpret_cast<const uint16_t*>(vpl + kHeadDim * code_row_bytes(VK));
+  if (VK == kQ4) {
+    // B-part entry (block 2w + bb, MFMA i, lane group gq): tokens t_lo..+3 and t_lo+16..+19
+    const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
+    const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
+    const uint16_t* row = vs + (2 * wave + bb) * kPageTokens;
+    v.s0 = *reinterpret_cast<const u2*>(row + t_lo);
+    v.s1 = *reinterpret_cast<const u2*>(row + t_lo + 16);
+  } else {
+    // entry (MFMA i, lane group gq) = tokens 64gq + 8i .. +7 of group w (lanes 0..31)
+    const int i = (lane >> 2) & 7, gq = lane & 3;
+    const u4 d = *reinterpret_cast<const u4*>(vs + wave * kPageTokens + 64 * gq + 8 * i);
+    v.s0 = (u2){d[0], d[1]};
+    v.s1 = (u2){d[2], d[3]};
   }
 }
 
-// Two packed (hi | lo << 16) probabilities -> the two fp16 of one part.
-__device__ inline uint32_t pick_part(uint32_t w0, uint32_t w1, int shift) {
-  return ((w0 >> shift) & 0xFFFFu) | (((w1 >> shift) & 0xFFFFu) << 16);
+// Eight q4 codes of one dword (byte w: low nibble token t+w, high nibble token
+// t+16+w) as halves "1024 + 16c", slot order [t..t+3, t+16..t+19].
+__device__ inline u4 v_magic_q4(uint32_t x, uint32_t vmask, uint32_t vmagic) {
+  const uint32_t t01 = __builtin_amdgcn_perm(0u, x, 0x0c010c00u);  // (b0, b1)
+  const uint32_t t23 = __builtin_amdgcn_perm(0u, x, 0x0c030c02u);  // (b2, b3)
+  return (u4){((t01 << 4) & vmask) | vmagic, ((t23 << 4) & vmask) | vmagic,
+              (t01 & vmask) | vmagic, (t23 & vmask) | vmagic};
 }
+// Eight int8 codes as halves "1024 + c + 128", in order.
+__device__ inline u4 v_magic_i8(uint32_t x0, uint32_t x1, uint32_t vmagic) {
+  const uint32_t u0 = x0 ^ 0x80808080u, u1 = x1 ^ 0x80808080u;
+  // selector byte 5 = byte 1 of vmagic = 0x64, the high byte of each half
+  return (u4){__builtin_amdgcn_perm(vmagic, u0, 0x05010500u), __builtin_amdgcn_perm(vmagic, u0, 0x05030502u),
+              __builtin_amdgcn_perm(vmagic, u1, 0x05010500u), __builtin_amdgcn_perm(vmagic, u1, 0x05030502u)};
+}
+__device__ inline h8 pk_fma8(u4 x, h8 m, h8 a) {
+  return __builtin_elementwise_fma(__builtin_bit_cast(h8, x), m, a);
+}
+
+// LDS of a workgroup.
+//   afrag:  the page's probabilities in P.V A-fragment layout, [MFMA i][lane] x 8 fp16
+//   dpart:  per wave, the B parts of its V scales: q4 [block 2][i 8][lane group 4][4 parts],
+//           int8 [i 8][lane group 4][6 parts], each an h8 in B slot order
+//   wmax:   each wave's maximum score per head;  lsum: each wave's probability sums
+struct SplitLds {
+  h8 afrag[8][64];
+  h8 dpart[kWaves][64 * 4];
+  float wmax[kWaves][kMaxGroup];
+  float lsum[kWaves][kMaxGroup];
+  float qs[kMaxGroup][kHeadDim];
+  float bsum[kMaxGroup][8];
+};
 
 template <int KK, int VK>
 __global__ __launch_bounds__(256, 2) void decode_split(
@@ -195,8 +263,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t* __restrict__ status) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[kSplitLds];
-  __shared__ float qs[kMaxGroup][kHeadDim];
+  __shared__ __attribute__((aligned(16))) SplitLds lds;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, col = lane & 15;  // MFMA lane group and column
@@ -213,335 +280,376 @@ __global__ __launch_bounds__(256, 2) void decode_split(
   const int p_end = min(n_pages, p_begin + pages_per_split);
   if (p_begin >= p_end) return;  // uniform over the workgroup
 
-  // ---- query of the group's heads, rotated by H when K is stored rotated
-  for (int hh = 0; hh < G; ++hh)
-    qs[hh][tid] = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hh) * kHeadDim + tid]);
-  __syncthreads();
+  const int64_t head_bytes = plane_bytes(KK) + plane_bytes(VK);
+  const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
+  const int32_t* bt = block_tables + (size_t)b * max_pages;
+
+  // Page base of logical page pg for this KV head (nullptr for an id outside the pool).
+  auto page_base = [&](int pg) -> const uint8_t* {
+    const int32_t phys = bt[pg];
+    if (phys < 0 || phys >= n_pool_pages) return nullptr;
+    return pool + (int64_t)phys * page_bytes + (int64_t)g * head_bytes;
+  };
+
+  // prefetch the first page's share: 4 K tiles (tokens 64w..64w+63) and the V share
+  KTile kt[4];
+  VShare<VK> vsh;
+  const uint8_t* base = page_base(p_begin);
+  {
+    const uint8_t* src = base ? base : pool;  // a bad page is read from page 0 and then ignored
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(src, 64 * wave + 16 * t + col, grp);
+    load_vshare<VK>(vsh, src + plane_bytes(KK), wave, lane);
+  }
+
+  // ---- query of the group's heads (element tid), rotated by H when K is stored rotated
+  float qv[kMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh)
+    qv[hh] = hh < G ? (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hh) * kHeadDim + tid]) : 0.f;
   if (KK == kQ4) {
-    for (int bit = 0; bit < 8; ++bit) {
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
       const int m = 1 << bit;
-      float vals[kMaxGroup];
-      for (int hh = 0; hh < G; ++hh) {
-        const float mine = qs[hh][tid], other = qs[hh][tid ^ m];
-        vals[hh] = (tid & m) ? (other - mine) : (mine + other);
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh) {
+        const float o = __shfl_xor(qv[hh], m);
+        qv[hh] = (lane & m) ? (o - qv[hh]) : (qv[hh] + o);
       }
-      __syncthreads();
-      for (int hh = 0; hh < G; ++hh) qs[hh][tid] = vals[hh];
-      __syncthreads();
     }
-    for (int hh = 0; hh < G; ++hh) qs[hh][tid] *= 0.0625f;
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+    __syncthreads();
+    const int e0 = tid & 63, k = tid >> 6;  // bits 6 and 7: a 4-point transform across waves
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
+                  x3 = lds.qs[hh][e0 + 192];
+      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
+      qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
+    }
     __syncthreads();
   }
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    lds.qs[hh][tid] = qv[hh];
+    // block sums of the (rotated) query: 32 elements (q4 blocks) or 64 (int8 groups)
+    float sum = qv[hh];
+#pragma unroll
+    for (int o = 1; o < (KK == kQ4 ? 32 : 64); o <<= 1) sum += __shfl_xor(sum, o);
+    if ((tid & (KK == kQ4 ? 31 : 63)) == 0) lds.bsum[hh][tid >> (KK == kQ4 ? 5 : 6)] = sum;
+  }
+  __syncthreads();
 
   // A operands of Q.K: row r = 2*head + part; MFMA j covers block j (elements 32j..32j+31)
   const int a_head = col >> 1, a_part = col & 1;
+  const bool a_live = a_head < G;
   h8 qa[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       int e;
-      if (KK == kQ4) e = 32 * j + (s < 4 ? 4 * grp + s : 16 + 4 * grp + (s - 4));
-      else e = 32 * j + 8 * grp + s;
-      const float f = qs[a_head < G ? a_head : 0][e];
+      float f;
+      if (KK == kQ4) {
+        const int off4[8] = {0, 2, 16, 18, 1, 3, 17, 19};
+        e = 32 * j + 4 * grp + off4[s];
+        f = lds.qs[a_head][e] * ((s & 2) ? 0.0625f : 1.0f);  // high-nibble slots hold q/16
+      } else {
+        e = 32 * j + 8 * grp + s;
+        f = lds.qs[a_head][e];
+      }
       const _Float16 hi = (_Float16)f;
       const _Float16 lo = (_Float16)(f - (float)hi);
-      qa[j][s] = a_head < G ? (a_part ? lo : hi) : (_Float16)0;
+      qa[j][s] = a_live ? (a_part ? lo : hi) : (_Float16)0;
     }
   }
+  // A operand of the offset correction: row 2*head + part, k-slot j (lane group 0) = block sum j
+  h8 qc;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const float f = (s < (KK == kQ4 ? 8 : 4)) ? lds.bsum[a_head][s] : 0.f;
+    const _Float16 hi = (_Float16)f;
+    const _Float16 lo = (_Float16)(f - (float)hi);
+    qc[s] = (a_live && grp == 0) ? (a_part ? lo : hi) : (_Float16)0;
+  }
+  // heads >= G never get probabilities: their fragment rows stay zero
+  for (int idx = tid; idx < 8 * 64; idx += 256) lds.afrag[idx >> 6][idx & 63] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
 
-  WaveLds& wl = reinterpret_cast<WaveLds*>(lds_raw)[wave];
-
+  const uint32_t vmask = vgpr_const(0x00F000F0u), vmagic = vgpr_const(0x64006400u);
+  const int h0 = 2 * grp, h1 = 2 * grp + 1;
   // per-lane running state for the two heads of its row group (rows 4grp..4grp+3)
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-  f4 oacc[16];
+  f4 oacc[4];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 4; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
 
-  const int64_t page_bytes = (int64_t)n_kv_heads * (plane_bytes(KK) + plane_bytes(VK));
-  const int32_t* bt = block_tables + (size_t)b * max_pages;
-  const int h0 = 2 * grp, h1 = 2 * grp + 1;
+  for (int pg = p_begin; pg < p_end; ++pg) {
+    const bool page_ok = base != nullptr;
+    if (!page_ok && tid == 0) atomicOr(status, KV_STATUS_BAD_PAGE_ID);
+    const int valid = page_ok ? min(kPageTokens, T - pg * kPageTokens) : 0;  // tokens in context
+    const uint8_t* next = pg + 1 < p_end ? page_base(pg + 1) : nullptr;
 
-  for (int pg = p_begin + wave; pg < p_end; pg += kWaves) {
-    const int32_t phys = bt[pg];
-    if (phys < 0 || phys >= n_pool_pages) {
-      if (lane == 0) atomicOr(status, KV_STATUS_BAD_PAGE_ID);
-      continue;
-    }
-    const uint8_t* kpl = pool + (int64_t)phys * page_bytes + (int64_t)g * (plane_bytes(KK) + plane_bytes(VK));
-    const uint8_t* vpl = kpl + plane_bytes(KK);
-    const int valid = min(kPageTokens, T - pg * kPageTokens);  // tokens of this page in context
-
-    // ---------------- Q.K: 16 tiles of 16 tokens, one tile of loads ahead
+    // ---------------- Q.K of the wave's 64 tokens, wave maximum per head
+    float xs[4][2];
     float mx0 = -INFINITY, mx1 = -INFINITY;
-    KTile cur = load_ktile<KK>(kpl, col, grp);
-#pragma unroll 1
-    for (int tile = 0; tile < 16; ++tile) {
-      const int row = tile * 16 + col;
-      const KTile nxt = load_ktile<KK>(kpl, min(tile + 1, 15) * 16 + col, grp);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = 64 * wave + 16 * t + col;
       float s0, s1;
-      qk_tile<KK>(cur, qa, s0, s1);
+      qk_tile<KK>(kt[t], qa, qc, s0, s1);
       const bool ok = row < valid;
-      const float x0 = ok ? s0 * scale_log2 : -INFINITY;
-      const float x1 = ok ? s1 * scale_log2 : -INFINITY;
-      mx0 = fmaxf(mx0, x0);
-      mx1 = fmaxf(mx1, x1);
-      wl.sp[h0][row] = __builtin_bit_cast(uint32_t, x0);
-      wl.sp[h1][row] = __builtin_bit_cast(uint32_t, x1);
-      cur = nxt;
+      xs[t][0] = ok ? s0 * scale_log2 : -INFINITY;
+      xs[t][1] = ok ? s1 * scale_log2 : -INFINITY;
+      mx0 = fmaxf(mx0, xs[t][0]);
+      mx1 = fmaxf(mx1, xs[t][1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // ---------------- online softmax over the page (log2 domain)
     mx0 = half_max(mx0);
     mx1 = half_max(mx1);
-    const float mn0 = fmaxf(m_run[0], mx0), mn1 = fmaxf(m_run[1], mx1);
-    const float al0 = exp2f(m_run[0] - mn0), al1 = exp2f(m_run[1] - mn1);
+    if (col == 0) {
+      lds.wmax[wave][h0] = mx0;
+      lds.wmax[wave][h1] = mx1;
+    }
+    // next page's K share, into the registers just consumed. Issued without a
+    // branch (the last page re-reads a valid page) so that the wait counters
+    // before the next uses stay exact and these loads overlap with the work below.
+    {
+      const uint8_t* src = next ? next : (base ? base : pool);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(src, 64 * wave + 16 * t + col, grp);
+    }
+
+    // ---------------- B parts of the wave's V scales (0 past the context)
+    bool fast;
+    {
+      h8* dp = lds.dpart[wave];
+      if (VK == kQ4) {
+        const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
+        const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
+        h8 dh16, nh, dl16, nl;
+        float amax = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int tt = t_lo + (u & 3) + 16 * (u >> 2);
+          const uint32_t word = (u < 4 ? vsh.s0 : vsh.s1)[(u & 3) >> 1];
+          uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
+          if (tt >= valid) bits = 0;
+          const _Float16 d = __builtin_bit_cast(_Float16, bits);
+          const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF0u));  // <= 7 bits
+          const _Float16 dl = d - dh;                                                     // <= 4 bits
+          dh16[u] = dh * (_Float16)0.0625f;
+          dl16[u] = dl * (_Float16)0.0625f;
+          nh[u] = dh * (_Float16)(-72.0f);
+          nl[u] = dl * (_Float16)(-72.0f);
+          amax = fmaxf(amax, fabsf((float)d));
+        }
+        h8* e = dp + ((bb * 8 + i) * 4 + gq) * 4;
+        e[0] = dh16;
+        e[1] = nh;
+        e[2] = dl16;
+        e[3] = nl;
+        fast = !__any(!(amax < kQ4FastMax));
+      } else {
+        const int i = (lane >> 2) & 7, gq = lane & 3;
+        const int t0 = 64 * gq + 8 * i;
+        h8 pa_, pb_, pc_, na, nb, nc;
+        float amax = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t word = (u < 4 ? vsh.s0 : vsh.s1)[(u & 3) >> 1];
+          uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
+          if (t0 + u >= valid) bits = 0;
+          const _Float16 d = __builtin_bit_cast(_Float16, bits);
+          const _Float16 da = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFF80u));   // <= 4 bits
+          const _Float16 db8 = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF8u));
+          pa_[u] = da;
+          pb_[u] = db8 - da;                                                             // <= 4 bits
+          pc_[u] = d - db8;                                                              // <= 3 bits
+          na[u] = pa_[u] * (_Float16)(-1152.0f);
+          nb[u] = pb_[u] * (_Float16)(-1152.0f);
+          nc[u] = pc_[u] * (_Float16)(-1152.0f);
+          amax = fmaxf(amax, fabsf((float)d));
+        }
+        if (lane < 32) {
+          h8* e = dp + (i * 4 + gq) * 6;
+          e[0] = pa_;
+          e[1] = na;
+          e[2] = pb_;
+          e[3] = nb;
+          e[4] = pc_;
+          e[5] = nc;
+        }
+        fast = !__any(lane < 32 && !(amax < kI8FastMax));
+      }
+    }
+    __syncthreads();  // (A) wave maxima visible
+
+    // ---------------- online softmax: page maximum over the four waves, p of the wave's tokens
+    float pm0 = lds.wmax[0][h0], pm1 = lds.wmax[0][h1];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      pm0 = fmaxf(pm0, lds.wmax[w][h0]);
+      pm1 = fmaxf(pm1, lds.wmax[w][h1]);
+    }
+    const float mn0 = fmaxf(m_run[0], pm0), mn1 = fmaxf(m_run[1], pm1);
+    // a page with no token in context leaves the state unchanged (max stays -inf)
+    const float al0 = mn0 == -INFINITY ? 1.f : exp2f(m_run[0] - mn0);
+    const float al1 = mn1 == -INFINITY ? 1.f : exp2f(m_run[1] - mn1);
     m_run[0] = mn0;
     m_run[1] = mn1;
     float sum0 = 0.f, sum1 = 0.f;
-#pragma unroll 4
-    for (int tile = 0; tile < 16; ++tile) {
-      const int row = tile * 16 + col;
-      const float p0 = exp2f(__builtin_bit_cast(float, wl.sp[h0][row]) - mn0);
-      const float p1 = exp2f(__builtin_bit_cast(float, wl.sp[h1][row]) - mn1);
+    _Float16* af = reinterpret_cast<_Float16*>(&lds.afrag[0][0]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float p0 = xs[t][0] == -INFINITY ? 0.f : exp2f(xs[t][0] - mn0);
+      const float p1 = xs[t][1] == -INFINITY ? 0.f : exp2f(xs[t][1] - mn1);
       sum0 += p0;
       sum1 += p1;
+      // fragment position of token 64w + 16t + col for P.V MFMA i, lane (w, 2h + part), slot
+      int i, slot;
+      if (VK == kQ4) {
+        i = 4 * (t >> 1) + (col >> 2);
+        slot = 4 * (t & 1) + (col & 3);
+      } else {
+        i = 2 * t + (col >> 3);
+        slot = col & 7;
+      }
+      const int base_idx = (i * 64 + 16 * wave) * 8 + slot;
       const float ps0 = p0 * kPScale, ps1 = p1 * kPScale;
       const _Float16 hi0 = (_Float16)ps0, hi1 = (_Float16)ps1;
       const _Float16 lo0 = (_Float16)(ps0 - (float)hi0), lo1 = (_Float16)(ps1 - (float)hi1);
-      wl.sp[h0][row] = (uint32_t)__builtin_bit_cast(uint16_t, hi0) | ((uint32_t)__builtin_bit_cast(uint16_t, lo0) << 16);
-      wl.sp[h1][row] = (uint32_t)__builtin_bit_cast(uint16_t, hi1) | ((uint32_t)__builtin_bit_cast(uint16_t, lo1) << 16);
+      if (h0 < G) {
+        af[base_idx + (2 * h0) * 8] = hi0;
+        af[base_idx + (2 * h0 + 1) * 8] = lo0;
+      }
+      if (h1 < G) {
+        af[base_idx + (2 * h1) * 8] = hi1;
+        af[base_idx + (2 * h1 + 1) * 8] = lo1;
+      }
     }
     l_run[0] = l_run[0] * al0 + sum0;
     l_run[1] = l_run[1] * al1 + sum1;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < 4; ++t) {
       oacc[t][0] *= al0;
       oacc[t][1] *= al0;
       oacc[t][2] *= al1;
       oacc[t][3] *= al1;
     }
+    __syncthreads();  // (B) probabilities of all 256 tokens visible
 
-    // ---------------- V scales of the page, split into exact fp16 parts (0 past the context)
-    {
-      const uint16_t* vs = reinterpret_cast<const uint16_t*>(vpl + kHeadDim * code_row_bytes(VK));
-      if (VK == kQ4) {
-        const int blk = lane >> 3, t0 = (lane & 7) * 32;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u4 raw = *reinterpret_cast<const u4*>(vs + blk * kPageTokens + t0 + 8 * c);
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int tt = t0 + 8 * c + 4 * half;  // first token of this 4-token run
-            h8 parts;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t word = raw[2 * half + (u >> 1)];
-              uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
-              if (tt + u >= valid) bits = 0;
-              const _Float16 d = __builtin_bit_cast(_Float16, bits);
-              const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF8u));
-              parts[u] = dh;
-              parts[4 + u] = d - dh;
-            }
-            *reinterpret_cast<h8*>(&wl.dsplit[dsplit_q4(blk, tt >> 2)]) = parts;
-          }
-        }
-      } else {
-        const int grp4 = lane >> 4, t0 = (lane & 15) * 16;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u4 raw = *reinterpret_cast<const u4*>(vs + grp4 * kPageTokens + t0 + 8 * c);
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int tt = t0 + 8 * c + 4 * half;
-            _Float16 parts[12];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t word = raw[2 * half + (u >> 1)];
-              uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
-              if (tt + u >= valid) bits = 0;
-              const _Float16 d = __builtin_bit_cast(_Float16, bits);
-              const _Float16 da = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFF80u));
-              const _Float16 db8 = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF8u));
-              parts[u] = da;
-              parts[4 + u] = db8 - da;
-              parts[8 + u] = d - db8;
-            }
-            _Float16* dst = &wl.dsplit[dsplit_i8(grp4, tt >> 2)];
-            *reinterpret_cast<h8*>(dst) = (h8){parts[0], parts[1], parts[2], parts[3],
-                                               parts[4], parts[5], parts[6], parts[7]};
-            *reinterpret_cast<h4*>(dst + 8) = (h4){parts[8], parts[9], parts[10], parts[11]};
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---------------- A operands of P.V (rows 2*head + part, k-slots = 8 tokens), built once
-    // per page and parked in LDS over the consumed scores: afrag[i][lane]
-    {
-      u4 frag[8];
-      const int shift = 16 * a_part;
+    // ---------------- P.V for the wave's 64 head elements (4 column tiles)
+    const h8* dp = lds.dpart[wave];
+    if (fast) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        u4 w0, w1;
+        const h8 pa = lds.afrag[i][lane];
         if (VK == kQ4) {
-          const int t_lo = 32 * (2 * grp + (i >> 2)) + 4 * (i & 3);
-          w0 = *reinterpret_cast<const u4*>(&wl.sp[a_head][t_lo]);
-          w1 = *reinterpret_cast<const u4*>(&wl.sp[a_head][t_lo + 16]);
+#pragma unroll
+          for (int bb = 0; bb < 2; ++bb) {
+            const h8* e = dp + ((bb * 8 + i) * 4 + grp) * 4;
+            const h8 dh16 = e[0], nh = e[1], dl16 = e[2], nl = e[3];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int nt = 2 * bb + u;
+              const u4 xm = v_magic_q4(vsh.c[nt][i >> 2][i & 3], vmask, vmagic);
+              oacc[nt] = mfma(pa, pk_fma8(xm, dh16, nh), oacc[nt]);
+              oacc[nt] = mfma(pa, pk_fma8(xm, dl16, nl), oacc[nt]);
+            }
+          }
         } else {
-          w0 = *reinterpret_cast<const u4*>(&wl.sp[a_head][64 * grp + 8 * i]);
-          w1 = *reinterpret_cast<const u4*>(&wl.sp[a_head][64 * grp + 8 * i + 4]);
-        }
-        const u4 packed = (u4){pick_part(w0[0], w0[1], shift), pick_part(w0[2], w0[3], shift),
-                               pick_part(w1[0], w1[1], shift), pick_part(w1[2], w1[3], shift)};
-        frag[i] = a_head < G ? packed : (u4){0, 0, 0, 0};
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      u4* af = reinterpret_cast<u4*>(&wl.sp[0][0]);
+          const h8* e = dp + (i * 4 + grp) * 6;
+          const h8 pa_ = e[0], na = e[1], pb_ = e[2], nb = e[3], pc_ = e[4], nc = e[5];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) af[i * 64 + lane] = frag[i];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    const u4* afrag = reinterpret_cast<const u4*>(&wl.sp[0][0]);
-
-    // ---------------- P.V
-    if (VK == kQ4) {
-      // lane column = head element 16*(2*blk + t) + col; its 32 code bytes hold 64 tokens
-      u4 vc[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)(16 * t + col) * 128 + 32 * grp);
-        vc[t][0] = src[0];
-        vc[t][1] = src[1];
-      }
-#pragma unroll
-      for (int blk = 0; blk < 8; ++blk) {
-        u4 vn[2][2];
-        const int nb = blk < 7 ? blk + 1 : 7;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)(16 * (2 * nb + t) + col) * 128 + 32 * grp);
-          vn[t][0] = src[0];
-          vn[t][1] = src[1];
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int run = (32 * (2 * grp + (i >> 2)) + 4 * (i & 3)) >> 2;
-          const h8 r0 = *reinterpret_cast<const h8*>(&wl.dsplit[dsplit_q4(blk, run)]);      // hi x4, lo x4
-          const h8 r1 = *reinterpret_cast<const h8*>(&wl.dsplit[dsplit_q4(blk, run + 4)]);  // +16 tokens
-          const h8 d1 = (h8){r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-          const h8 d2 = (h8){r0[4], r0[5], r0[6], r0[7], r1[4], r1[5], r1[6], r1[7]};
-          const h8 pa = __builtin_bit_cast(h8, afrag[i * 64 + lane]);
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const h8 c = unpack_q4(vc[t][i >> 2][i & 3]);
-            oacc[2 * blk + t] = mfma(pa, c * d1, oacc[2 * blk + t]);
-            oacc[2 * blk + t] = mfma(pa, c * d2, oacc[2 * blk + t]);
+          for (int nt = 0; nt < 4; ++nt) {
+            const u4 words = vsh.c[nt][i >> 1];
+            const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
+            oacc[nt] = mfma(pa, pk_fma8(xm, pa_, na), oacc[nt]);
+            oacc[nt] = mfma(pa, pk_fma8(xm, pb_, nb), oacc[nt]);
+            oacc[nt] = mfma(pa, pk_fma8(xm, pc_, nc), oacc[nt]);
           }
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          vc[t][0] = vn[t][0];
-          vc[t][1] = vn[t][1];
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands short-lived
       }
     } else {
-      u4 vc[4];
-      {
-        const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)col * 256 + 64 * grp);
-        vc[0] = src[0]; vc[1] = src[1]; vc[2] = src[2]; vc[3] = src[3];
-      }
+      // scales too large for the folded constants: exact codes first, then the parts
 #pragma unroll
-      for (int nt = 0; nt < 16; ++nt) {
-        const int gg = nt >> 2;
-        const int nn = nt < 15 ? nt + 1 : 15;
-        u4 vn[4];
-        {
-          const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)(16 * nn + col) * 256 + 64 * grp);
-          vn[0] = src[0]; vn[1] = src[1]; vn[2] = src[2]; vn[3] = src[3];
-        }
-        const uint32_t w[16] = {vc[0][0], vc[0][1], vc[0][2], vc[0][3], vc[1][0], vc[1][1], vc[1][2], vc[1][3],
-                                vc[2][0], vc[2][1], vc[2][2], vc[2][3], vc[3][0], vc[3][1], vc[3][2], vc[3][3]};
+      for (int i = 0; i < 8; ++i) {
+        const h8 pa = lds.afrag[i][lane];
+        if (VK == kQ4) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int run = (64 * grp + 8 * i) >> 2;
-          const _Float16* r0 = &wl.dsplit[dsplit_i8(gg, run)];
-          const _Float16* r1 = &wl.dsplit[dsplit_i8(gg, run + 1)];
-          const h8 a0 = *reinterpret_cast<const h8*>(r0);
-          const h4 a1 = *reinterpret_cast<const h4*>(r0 + 8);
-          const h8 b0 = *reinterpret_cast<const h8*>(r1);
-          const h4 b1 = *reinterpret_cast<const h4*>(r1 + 8);
-          const h8 da = (h8){a0[0], a0[1], a0[2], a0[3], b0[0], b0[1], b0[2], b0[3]};
-          const h8 db = (h8){a0[4], a0[5], a0[6], a0[7], b0[4], b0[5], b0[6], b0[7]};
-          const h8 dc = (h8){a1[0], a1[1], a1[2], a1[3], b1[0], b1[1], b1[2], b1[3]};
-          const h8 c = unpack_i8(w[2 * i], w[2 * i + 1]);
-          const h8 pa = __builtin_bit_cast(h8, afrag[i * 64 + lane]);
-          oacc[nt] = mfma(pa, c * da, oacc[nt]);
-          oacc[nt] = mfma(pa, c * db, oacc[nt]);
-          oacc[nt] = mfma(pa, c * dc, oacc[nt]);
+          for (int bb = 0; bb < 2; ++bb) {
+            const h8* e = dp + ((bb * 8 + i) * 4 + grp) * 4;
+            const h8 dh = e[0] * (_Float16)16.0f, dl = e[2] * (_Float16)16.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int nt = 2 * bb + u;
+              const u4 xm = v_magic_q4(vsh.c[nt][i >> 2][i & 3], vmask, vmagic);
+              const h8 c8 = __builtin_elementwise_fma(__builtin_bit_cast(h8, xm), (h8)(_Float16)0.0625f,
+                                                      (h8)(_Float16)(-72.0f));  // c - 8, exact
+              oacc[nt] = mfma(pa, c8 * dh, oacc[nt]);
+              oacc[nt] = mfma(pa, c8 * dl, oacc[nt]);
+            }
+          }
+        } else {
+          const h8* e = dp + (i * 4 + grp) * 6;
+          const h8 pa_ = e[0], pb_ = e[2], pc_ = e[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const u4 words = vsh.c[nt][i >> 1];
+            const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
+            const h8 c8 = __builtin_bit_cast(h8, xm) - (h8)(_Float16)1152.0f;  // c, exact
+            oacc[nt] = mfma(pa, c8 * pa_, oacc[nt]);
+            oacc[nt] = mfma(pa, c8 * pb_, oacc[nt]);
+            oacc[nt] = mfma(pa, c8 * pc_, oacc[nt]);
+          }
         }
-        vc[0] = vn[0]; vc[1] = vn[1]; vc[2] = vn[2]; vc[3] = vn[3];
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // next page's V share, into the registers just consumed (unconditional, as above)
+    load_vshare<VK>(vsh, (next ? next : (base ? base : pool)) + plane_bytes(KK), wave, lane);
+    base = next;
   }
 
-  // ---------------- merge the four waves and write this split's partials
-  __syncthreads();
-  MergeLds& ml = *reinterpret_cast<MergeLds*>(lds_raw);
+  // ---------------- this split's partials: common max, summed weights, each wave's elements
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int hh = 2 * grp + r;
     const float lsum = half_sum(l_run[r]);
-    if (col == 0) {
-      ml.m[wave][hh] = m_run[r];
-      ml.l[wave][hh] = lsum;
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) ml.o[wave][hh][16 * t + col] = oacc[t][2 * r] + oacc[t][2 * r + 1];
+    if (col == 0) lds.lsum[wave][2 * grp + r] = lsum;
   }
   __syncthreads();
   const size_t S = (size_t)n_splits;
-  for (int hh = 0; hh < G; ++hh) {
-    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml.m[w][hh]);
-    float L = 0.f, O = 0.f;
+  for (int r = 0; r < 2; ++r) {
+    const int hh = 2 * grp + r;
+    if (hh < G) {
+      const size_t idx = ((size_t)b * n_q_heads + g * G + hh) * S + split;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = ml.m[w][hh];
-      const float wt = mw == -INFINITY ? 0.f : exp2f(mw - M);
-      L += wt * ml.l[w][hh];
-      O += wt * ml.o[w][hh][tid];
-    }
-    const size_t idx = ((size_t)b * n_q_heads + g * G + hh) * S + split;
-    part_o[idx * kHeadDim + tid] = O * kPScaleInv;
-    if (tid == 0) {
-      part_ml[2 * idx] = M;
-      part_ml[2 * idx + 1] = L;
+      for (int t = 0; t < 4; ++t)
+        part_o[idx * kHeadDim + 64 * wave + 16 * t + col] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
+      if (wave == 0 && col == 0) {
+        part_ml[2 * idx] = m_run[r];
+        part_ml[2 * idx + 1] = lds.lsum[0][hh] + lds.lsum[1][hh] + lds.lsum[2][hh] + lds.lsum[3][hh];
+      }
     }
   }
 }
 
+// Log-sum-exp merge of the partials of one (query head, sequence), then the
+// rotation back by H. The split weights are staged in LDS so that the loop
+// over splits issues independent loads.
 template <bool ROTATE>
 __global__ __launch_bounds__(256) void decode_combine(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ context_lens, int max_context, int n_q_heads,
     int pages_per_split, int n_splits, float* __restrict__ out) {
   __shared__ float buf[kHeadDim];
+  __shared__ float wts[1024];
+  __shared__ float red[2][4];
   const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
   int T = context_lens[b];
   T = T < 0 ? 0 : (T > max_context ? max_context : T);
@@ -551,15 +659,40 @@ __global__ __launch_bounds__(256) void decode_combine(
   float o = 0.f;
   if (ns > 0) {
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, part_ml[2 * (base + s)]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = part_ml[2 * (base + s)];
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L += w * part_ml[2 * (base + s) + 1];
-      acc += w * part_o[(base + s) * kHeadDim + tid];
+    for (int s = tid; s < ns; s += 256) M = fmaxf(M, part_ml[2 * (base + s)]);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((tid & 63) == 0) red[0][tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float L = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 1024) {
+      const int cnt = min(1024, ns - s0);
+      __syncthreads();
+      for (int s = tid; s < cnt; s += 256) {
+        const float ms = part_ml[2 * (base + s0 + s)];
+        const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
+        wts[s] = w;
+        L += w * part_ml[2 * (base + s0 + s) + 1];
+      }
+      __syncthreads();
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      int s = 0;
+      for (; s + 4 <= cnt; s += 4) {
+        const float* po = part_o + (base + s0 + s) * kHeadDim + tid;
+        a0 += wts[s] * po[0];
+        a1 += wts[s + 1] * po[kHeadDim];
+        a2 += wts[s + 2] * po[2 * kHeadDim];
+        a3 += wts[s + 3] * po[3 * kHeadDim];
+      }
+      for (; s < cnt; ++s) a0 += wts[s] * part_o[(base + s0 + s) * kHeadDim + tid];
+      o += (a0 + a1) + (a2 + a3);
     }
-    o = L > 0.f ? acc / L : 0.f;  // L == 0 only if every page of the sequence was skipped
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    __syncthreads();
+    if ((tid & 63) == 0) red[1][tid >> 6] = L;
+    __syncthreads();
+    L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    o = L > 0.f ? o / L : 0.f;  // L == 0 only if every page of the sequence was skipped
   }
   if (ROTATE) {
     buf[tid] = o;
@@ -589,24 +722,29 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e;
-  switch (a.fmt) {
-    case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream); break;
-    case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream); break;
-    default: e = launch_split<kInt8, kQ4>(a, stream); break;
+hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream) {
+  if (phase & 1) {
+    hipError_t e;
+    switch (a.fmt) {
+      case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream); break;
+      case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream); break;
+      default: e = launch_split<kInt8, kQ4>(a, stream); break;
+    }
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch), block(256);
-  if (a.fmt == KV_FMT_INT8)
-    hipLaunchKernelGGL((decode_combine<false>), grid, block, 0, stream, a.part_ml, a.part_o,
-                       a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
-                       a.out);
-  else
-    hipLaunchKernelGGL((decode_combine<true>), grid, block, 0, stream, a.part_ml, a.part_o,
-                       a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
-                       a.out);
-  return hipGetLastError();
+  if (phase & 2) {
+    dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch), block(256);
+    if (a.fmt == KV_FMT_INT8)
+      hipLaunchKernelGGL((decode_combine<false>), grid, block, 0, stream, a.part_ml, a.part_o,
+                         a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
+                         a.out);
+    else
+      hipLaunchKernelGGL((decode_combine<true>), grid, block, 0, stream, a.part_ml, a.part_o,
+                         a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
+                         a.out);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace kvc

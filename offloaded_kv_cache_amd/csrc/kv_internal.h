@@ -112,7 +112,8 @@ struct DecodeArgs {
   float* part_o;              // [batch][n_q_heads][n_splits][256]
 };
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// phase: 1 = split kernel only, 2 = combine only, 3 = both
+hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream);
 
 constexpr int kGatherMaxBatch = 256;  // selections per gather launch (kernel-argument size)
 
