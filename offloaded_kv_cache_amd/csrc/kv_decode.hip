@@ -69,6 +69,7 @@ constexpr float kTwo24 = 16777216.0f;
 constexpr float kQ4FastMax = 896.0f;   // |d| below this: -72 * d_hi is exact and finite
 constexpr float kI8FastMax = 56.0f;    // |d| below this: -1152 * d_part is exact and finite
 constexpr int kWaves = 4;
+constexpr int kQsStride = kHeadDim + 4;  // padded rows of the query in LDS (bank spread)
 
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 __device__ inline uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
@@ -195,17 +196,20 @@ struct VShare {
   u2 s0, s1;                   // q4: 4 + 4 token scales; int8: s0, s1 = 8 consecutive scales
 };
 
+// Column tile nt of the wave's V share: the lane's 32 (q4) / 64 (int8) code bytes of head
+// element 64w + 16nt + col.
 template <int VK>
-__device__ inline void load_vshare(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
+__device__ inline void load_vcodes(VShare<VK>& v, const uint8_t* vpl, int wave, int lane, int nt) {
   const int grp = lane >> 4, col = lane & 15;
+  const int e = 64 * wave + 16 * nt + col;
+  const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)e * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    const int e = 64 * wave + 16 * nt + col;
-    const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)e * code_row_bytes(VK) +
-                                                (VK == kQ4 ? 32 : 64) * grp);
-#pragma unroll
-    for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = src[u];
-  }
+  for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = src[u];
+}
+
+// The scales the lane turns into B parts.
+template <int VK>
+__device__ inline void load_vscales(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
   const uint16_t* vs = reinterpret_cast<const uint16_t*>(vpl + kHeadDim * code_row_bytes(VK));
   if (VK == kQ4) {
     // B-part entry (block 2w + bb, MFMA i, lane group gq): tokens t_lo..+3 and t_lo+16..+19
@@ -221,6 +225,13 @@ __device__ inline void load_vshare(VShare<VK>& v, const uint8_t* vpl, int wave, 
     v.s0 = (u2){d[0], d[1]};
     v.s1 = (u2){d[2], d[3]};
   }
+}
+
+template <int VK>
+__device__ inline void load_vshare(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) load_vcodes<VK>(v, vpl, wave, lane, nt);
+  load_vscales<VK>(v, vpl, wave, lane);
 }
 
 // Eight q4 codes of one dword (byte w: low nibble token t+w, high nibble token
@@ -244,15 +255,16 @@ __device__ inline h8 pk_fma8(u4 x, h8 m, h8 a) {
 
 // LDS of a workgroup.
 //   afrag:  the page's probabilities in P.V A-fragment layout, [MFMA i][lane] x 8 fp16
-//   dpart:  per wave, the B parts of its V scales: q4 [block 2][i 8][lane group 4][4 parts],
-//           int8 [i 8][lane group 4][6 parts], each an h8 in B slot order
+//   dpart:  per wave, the B parts of its V scales, part-major so that lanes write and read
+//           consecutive 16 B: q4 [4 parts][block 2][i 8][lane group 4], int8 [6 parts][i 8]
+//           [lane group 4], each an h8 in B slot order
 //   wmax:   each wave's maximum score per head;  lsum: each wave's probability sums
 struct SplitLds {
   h8 afrag[8][64];
-  h8 dpart[kWaves][64 * 4];
+  h8 dpart[kWaves][64 * 6];
   float wmax[kWaves][kMaxGroup];
   float lsum[kWaves][kMaxGroup];
-  float qs[kMaxGroup][kHeadDim];
+  float qs[kMaxGroup][kQsStride];
   float bsum[kMaxGroup][8];
 };
 
@@ -309,58 +321,67 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     qv[hh] = hh < G ? (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hh) * kHeadDim + tid]) : 0.f;
   if (KK == kQ4) {
 #pragma unroll
-    for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
-      const int m = 1 << bit;
+    for (int hh = 0; hh < kMaxGroup; ++hh) {
+      if (hh < G) {  // uniform
 #pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) {
-        const float o = __shfl_xor(qv[hh], m);
-        qv[hh] = (lane & m) ? (o - qv[hh]) : (qv[hh] + o);
+        for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
+          const int m = 1 << bit;
+          const float o = __shfl_xor(qv[hh], m);
+          qv[hh] = (lane & m) ? (o - qv[hh]) : (qv[hh] + o);
+        }
+        lds.qs[hh][tid] = qv[hh];
       }
     }
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
     __syncthreads();
     const int e0 = tid & 63, k = tid >> 6;  // bits 6 and 7: a 4-point transform across waves
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh) {
-      const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
-                  x3 = lds.qs[hh][e0 + 192];
-      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
-      qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
+      if (hh < G) {
+        const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
+                    x3 = lds.qs[hh][e0 + 192];
+        const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
+        qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
+      }
     }
     __syncthreads();
   }
 #pragma unroll
   for (int hh = 0; hh < kMaxGroup; ++hh) {
     lds.qs[hh][tid] = qv[hh];
-    // block sums of the (rotated) query: 32 elements (q4 blocks) or 64 (int8 groups)
-    float sum = qv[hh];
+    if (hh < G) {
+      // block sums of the (rotated) query: 32 elements (q4 blocks) or 64 (int8 groups)
+      float sum = qv[hh];
 #pragma unroll
-    for (int o = 1; o < (KK == kQ4 ? 32 : 64); o <<= 1) sum += __shfl_xor(sum, o);
-    if ((tid & (KK == kQ4 ? 31 : 63)) == 0) lds.bsum[hh][tid >> (KK == kQ4 ? 5 : 6)] = sum;
+      for (int o = 1; o < (KK == kQ4 ? 32 : 64); o <<= 1) sum += __shfl_xor(sum, o);
+      if ((tid & (KK == kQ4 ? 31 : 63)) == 0) lds.bsum[hh][tid >> (KK == kQ4 ? 5 : 6)] = sum;
+    }
   }
   __syncthreads();
 
   // A operands of Q.K: row r = 2*head + part; MFMA j covers block j (elements 32j..32j+31)
   const int a_head = col >> 1, a_part = col & 1;
   const bool a_live = a_head < G;
+  const float* qrow = lds.qs[a_head];
   h8 qa[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    float f[8];
+    if (KK == kQ4) {
+      // slots [e, e+2, e+16, e+18, e+1, e+3, e+17, e+19] with e = 32j + 4grp; high-nibble slots hold q/16
+      const f4 lo4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp);
+      const f4 hi4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp + 16) * 0.0625f;
+      f[0] = lo4[0]; f[1] = lo4[2]; f[2] = hi4[0]; f[3] = hi4[2];
+      f[4] = lo4[1]; f[5] = lo4[3]; f[6] = hi4[1]; f[7] = hi4[3];
+    } else {
+      const f4 a4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 8 * grp);
+      const f4 b4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 8 * grp + 4);
+      f[0] = a4[0]; f[1] = a4[1]; f[2] = a4[2]; f[3] = a4[3];
+      f[4] = b4[0]; f[5] = b4[1]; f[6] = b4[2]; f[7] = b4[3];
+    }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      int e;
-      float f;
-      if (KK == kQ4) {
-        const int off4[8] = {0, 2, 16, 18, 1, 3, 17, 19};
-        e = 32 * j + 4 * grp + off4[s];
-        f = lds.qs[a_head][e] * ((s & 2) ? 0.0625f : 1.0f);  // high-nibble slots hold q/16
-      } else {
-        e = 32 * j + 8 * grp + s;
-        f = lds.qs[a_head][e];
-      }
-      const _Float16 hi = (_Float16)f;
-      const _Float16 lo = (_Float16)(f - (float)hi);
+      const _Float16 hi = (_Float16)f[s];
+      const _Float16 lo = (_Float16)(f[s] - (float)hi);
       qa[j][s] = a_live ? (a_part ? lo : hi) : (_Float16)0;
     }
   }
@@ -392,6 +413,11 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     const int valid = page_ok ? min(kPageTokens, T - pg * kPageTokens) : 0;  // tokens in context
     const uint8_t* next = pg + 1 < p_end ? page_base(pg + 1) : nullptr;
 
+    // Next page's loads are issued without a branch (the last page re-reads a
+    // valid page) so that the wait counters before each use stay exact, and each
+    // part is issued as soon as its registers are consumed, to overlap the math.
+    const uint8_t* nsrc = next ? next : (base ? base : pool);
+
     // ---------------- Q.K of the wave's 64 tokens, wave maximum per head
     float xs[4][2];
     float mx0 = -INFINITY, mx1 = -INFINITY;
@@ -405,6 +431,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       xs[t][1] = ok ? s1 * scale_log2 : -INFINITY;
       mx0 = fmaxf(mx0, xs[t][0]);
       mx1 = fmaxf(mx1, xs[t][1]);
+      kt[t] = load_ktile<KK>(nsrc, 64 * wave + 16 * t + col, grp);  // next page's tile t
       __builtin_amdgcn_sched_barrier(0);
     }
     mx0 = half_max(mx0);
@@ -412,14 +439,6 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     if (col == 0) {
       lds.wmax[wave][h0] = mx0;
       lds.wmax[wave][h1] = mx1;
-    }
-    // next page's K share, into the registers just consumed. Issued without a
-    // branch (the last page re-reads a valid page) so that the wait counters
-    // before the next uses stay exact and these loads overlap with the work below.
-    {
-      const uint8_t* src = next ? next : (base ? base : pool);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(src, 64 * wave + 16 * t + col, grp);
     }
 
     // ---------------- B parts of the wave's V scales (0 past the context)
@@ -446,11 +465,11 @@ __global__ __launch_bounds__(256, 2) void decode_split(
           nl[u] = dl * (_Float16)(-72.0f);
           amax = fmaxf(amax, fabsf((float)d));
         }
-        h8* e = dp + ((bb * 8 + i) * 4 + gq) * 4;
+        h8* e = dp + ((bb * 8 + i) * 4 + gq);  // = dp + lane
         e[0] = dh16;
-        e[1] = nh;
-        e[2] = dl16;
-        e[3] = nl;
+        e[64] = nh;
+        e[128] = dl16;
+        e[192] = nl;
         fast = !__any(!(amax < kQ4FastMax));
       } else {
         const int i = (lane >> 2) & 7, gq = lane & 3;
@@ -474,17 +493,18 @@ __global__ __launch_bounds__(256, 2) void decode_split(
           amax = fmaxf(amax, fabsf((float)d));
         }
         if (lane < 32) {
-          h8* e = dp + (i * 4 + gq) * 6;
+          h8* e = dp + (i * 4 + gq);  // = dp + lane
           e[0] = pa_;
-          e[1] = na;
-          e[2] = pb_;
-          e[3] = nb;
-          e[4] = pc_;
-          e[5] = nc;
+          e[32] = na;
+          e[64] = pb_;
+          e[96] = nb;
+          e[128] = pc_;
+          e[160] = nc;
         }
         fast = !__any(lane < 32 && !(amax < kI8FastMax));
       }
     }
+    load_vscales<VK>(vsh, nsrc + plane_bytes(KK), wave, lane);  // next page's scales
     __syncthreads();  // (A) wave maxima visible
 
     // ---------------- online softmax: page maximum over the four waves, p of the wave's tokens
@@ -541,77 +561,79 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     }
     __syncthreads();  // (B) probabilities of all 256 tokens visible
 
-    // ---------------- P.V for the wave's 64 head elements (4 column tiles)
+    // ---------------- P.V for the wave's 64 head elements (4 column tiles), in two halves
+    // of two column tiles (one q4 block each); after a half, its code registers take the
+    // next page's codes.
     const h8* dp = lds.dpart[wave];
-    if (fast) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const h8 pa = lds.afrag[i][lane];
-        if (VK == kQ4) {
+    for (int hf = 0; hf < 2; ++hf) {
+      if (fast) {
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const h8* e = dp + ((bb * 8 + i) * 4 + grp) * 4;
-            const h8 dh16 = e[0], nh = e[1], dl16 = e[2], nl = e[3];
+        for (int i = 0; i < 8; ++i) {
+          const h8 pa = lds.afrag[i][lane];
+          if (VK == kQ4) {
+            const h8* e = dp + ((hf * 8 + i) * 4 + grp);
+            const h8 dh16 = e[0], nh = e[64], dl16 = e[128], nl = e[192];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const int nt = 2 * bb + u;
+              const int nt = 2 * hf + u;
               const u4 xm = v_magic_q4(vsh.c[nt][i >> 2][i & 3], vmask, vmagic);
               oacc[nt] = mfma(pa, pk_fma8(xm, dh16, nh), oacc[nt]);
               oacc[nt] = mfma(pa, pk_fma8(xm, dl16, nl), oacc[nt]);
             }
-          }
-        } else {
-          const h8* e = dp + (i * 4 + grp) * 6;
-          const h8 pa_ = e[0], na = e[1], pb_ = e[2], nb = e[3], pc_ = e[4], nc = e[5];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const u4 words = vsh.c[nt][i >> 1];
-            const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
-            oacc[nt] = mfma(pa, pk_fma8(xm, pa_, na), oacc[nt]);
-            oacc[nt] = mfma(pa, pk_fma8(xm, pb_, nb), oacc[nt]);
-            oacc[nt] = mfma(pa, pk_fma8(xm, pc_, nc), oacc[nt]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands short-lived
-      }
-    } else {
-      // scales too large for the folded constants: exact codes first, then the parts
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const h8 pa = lds.afrag[i][lane];
-        if (VK == kQ4) {
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const h8* e = dp + ((bb * 8 + i) * 4 + grp) * 4;
-            const h8 dh = e[0] * (_Float16)16.0f, dl = e[2] * (_Float16)16.0f;
+          } else {
+            const h8* e = dp + (i * 4 + grp);
+            const h8 pa_ = e[0], na = e[32], pb_ = e[64], nb = e[96], pc_ = e[128], nc = e[160];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const int nt = 2 * bb + u;
+              const int nt = 2 * hf + u;
+              const u4 words = vsh.c[nt][i >> 1];
+              const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
+              oacc[nt] = mfma(pa, pk_fma8(xm, pa_, na), oacc[nt]);
+              oacc[nt] = mfma(pa, pk_fma8(xm, pb_, nb), oacc[nt]);
+              oacc[nt] = mfma(pa, pk_fma8(xm, pc_, nc), oacc[nt]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands short-lived
+        }
+      } else {
+        // scales too large for the folded constants: exact codes first, then the parts
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const h8 pa = lds.afrag[i][lane];
+          if (VK == kQ4) {
+            const h8* e = dp + ((hf * 8 + i) * 4 + grp);
+            const h8 dh = e[0] * (_Float16)16.0f, dl = e[128] * (_Float16)16.0f;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int nt = 2 * hf + u;
               const u4 xm = v_magic_q4(vsh.c[nt][i >> 2][i & 3], vmask, vmagic);
               const h8 c8 = __builtin_elementwise_fma(__builtin_bit_cast(h8, xm), (h8)(_Float16)0.0625f,
                                                       (h8)(_Float16)(-72.0f));  // c - 8, exact
               oacc[nt] = mfma(pa, c8 * dh, oacc[nt]);
               oacc[nt] = mfma(pa, c8 * dl, oacc[nt]);
             }
-          }
-        } else {
-          const h8* e = dp + (i * 4 + grp) * 6;
-          const h8 pa_ = e[0], pb_ = e[2], pc_ = e[4];
+          } else {
+            const h8* e = dp + (i * 4 + grp);
+            const h8 pa_ = e[0], pb_ = e[64], pc_ = e[128];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const u4 words = vsh.c[nt][i >> 1];
-            const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
-            const h8 c8 = __builtin_bit_cast(h8, xm) - (h8)(_Float16)1152.0f;  // c, exact
-            oacc[nt] = mfma(pa, c8 * pa_, oacc[nt]);
-            oacc[nt] = mfma(pa, c8 * pb_, oacc[nt]);
-            oacc[nt] = mfma(pa, c8 * pc_, oacc[nt]);
+            for (int u = 0; u < 2; ++u) {
+              const int nt = 2 * hf + u;
+              const u4 words = vsh.c[nt][i >> 1];
+              const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
+              const h8 c8 = __builtin_bit_cast(h8, xm) - (h8)(_Float16)1152.0f;  // c, exact
+              oacc[nt] = mfma(pa, c8 * pa_, oacc[nt]);
+              oacc[nt] = mfma(pa, c8 * pb_, oacc[nt]);
+              oacc[nt] = mfma(pa, c8 * pc_, oacc[nt]);
+            }
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
+      // this half's code registers now take the next page's codes
+      load_vcodes<VK>(vsh, nsrc + plane_bytes(KK), wave, lane, 2 * hf);
+      load_vcodes<VK>(vsh, nsrc + plane_bytes(KK), wave, lane, 2 * hf + 1);
     }
-    // next page's V share, into the registers just consumed (unconditional, as above)
-    load_vshare<VK>(vsh, (next ? next : (base ? base : pool)) + plane_bytes(KK), wave, lane);
     base = next;
   }
 
@@ -675,17 +697,22 @@ __global__ __launch_bounds__(256) void decode_combine(
         L += w * part_ml[2 * (base + s0 + s) + 1];
       }
       __syncthreads();
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      float acc[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc[u] = 0.f;
       int s = 0;
-      for (; s + 4 <= cnt; s += 4) {
+      for (; s + 16 <= cnt; s += 16) {  // 16 independent loads in flight per thread
         const float* po = part_o + (base + s0 + s) * kHeadDim + tid;
-        a0 += wts[s] * po[0];
-        a1 += wts[s + 1] * po[kHeadDim];
-        a2 += wts[s + 2] * po[2 * kHeadDim];
-        a3 += wts[s + 3] * po[3 * kHeadDim];
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = po[u * kHeadDim];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] += wts[s + u] * v[u];
       }
-      for (; s < cnt; ++s) a0 += wts[s] * part_o[(base + s0 + s) * kHeadDim + tid];
-      o += (a0 + a1) + (a2 + a3);
+      for (; s < cnt; ++s) acc[0] += wts[s] * part_o[(base + s0 + s) * kHeadDim + tid];
+#pragma unroll
+      for (int u = 1; u < 16; ++u) acc[0] += acc[u];
+      o += acc[0];
     }
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
     __syncthreads();
