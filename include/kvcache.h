@@ -114,7 +114,8 @@ int64_t kv_page_bytes(const kv_shape* shape);
  * p % 256. Every code and scale is bit-exact to the record rules above
  * (the rotation is computed exactly, in fp64).
  *
- *   k, v         device fp16 [n_tokens][n_kv_heads][256], token-major.
+ *   k, v         device fp16 [n_tokens][n_kv_heads][256], token-major, finite
+ *                (codes of a vector holding Inf or NaN are unspecified).
  *   block_table  device int32 [n_table]: physical page id of each logical
  *                page of the sequence; n_table * 256 >= start_pos + n_tokens.
  *   pool         device (or device-accessible pinned host) base of the page

@@ -6,10 +6,12 @@
 // section "三种 KV 格式横向对比": int8 (per-64 scales) and k8v4 (int8 K,
 // rotated q4_0 V). The rounding rules are those of include/kvcache.h.
 //
-// One wavefront handles one token pair (32G+i, 32G+16+i) of one KV head: the
-// two tokens whose 4-bit V codes share a byte of the element-major V plane.
-// Computing both records in one wave makes every V byte single-writer, so a
-// chunk of any length and alignment is appended without atomics.
+// One workgroup of four waves handles one token pair (32G+i, 32G+16+i) of one
+// KV head: the two tokens whose 4-bit V codes share a byte of the element-major
+// V plane. Waves 0 and 1 encode the K vectors of the two tokens, waves 2 and 3
+// their V vectors; the V codes of the upper token pass through LDS and wave 2
+// writes the shared bytes, so that every V byte has a single writer and a chunk
+// of any length and alignment is appended without atomics.
 //
 // Lane l holds elements e = l + 64k (k = 0..3) of a vector. The rotation is
 // done in fp64, where it is exact for fp16 inputs (partial sums are multiples
@@ -20,10 +22,17 @@
 namespace kvc {
 namespace {
 
-__device__ inline double wave_max(double v) {
+// Maximum over the wave of each of the lane's four values (exchanges of the four
+// values are issued together).
+__device__ inline void wave_max4(double (&v)[4]) {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
+  for (int o = 1; o < 64; o <<= 1) {
+    double t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = __shfl_xor(v[k], o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], t[k]);
+  }
 }
 
 // Exact y = H x on the lane's four elements.
@@ -57,26 +66,36 @@ __device__ inline void encode(const uint16_t* __restrict__ src, int lane, int (&
 #pragma unroll
   for (int k = 0; k < 4; ++k) x[k] = f16_to_f64(src[lane + 64 * k]);
   if (KIND == kInt8) {
+    double a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
+    wave_max4(a);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const double a = wave_max(fabs(x[k]));
-      scale[k] = f64_to_f16_rne(a / 127.0);
+      scale[k] = f64_to_f16_rne(a[k] / 127.0);
       code[k] = int8_code(x[k], f16_to_f64(scale[k]));
     }
   } else {
     wht256(x, lane);
+    // per block (the 32 lanes of a half-wave, register k): largest |y|, then the
+    // first element holding it, then its signed value
+    double m[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+      double t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = __shfl_xor(m[k], o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m[k] = fmax(m[k], t[k]);
+    }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // largest |y| over the 32 lanes of this half-wave, first element on ties
-      double best = x[k];
-      int idx = lane & 31;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        const double ob = __shfl_xor(best, o);
-        const int oi = __shfl_xor(idx, o);
-        const double fa = fabs(best), fo = fabs(ob);
-        if (fo > fa || (fo == fa && oi < idx)) { best = ob; idx = oi; }
-      }
+      const uint64_t hit = __ballot(fabs(x[k]) == m[k]);
+      const uint32_t half = (lane & 32) ? (uint32_t)(hit >> 32) : (uint32_t)hit;
+      // (no hit only for NaN inputs, whose codes are unspecified)
+      const double best = __shfl(x[k], (lane & 32) + (half ? __builtin_ctz(half) : (lane & 31)));
       scale[k] = f64_to_f16_rne(-best * 0.125);  // -m/8 is exact in fp64
       code[k] = q4_code(x[k], f16_to_f64(scale[k]));
     }
@@ -131,22 +150,23 @@ __device__ inline void write_v_scales(uint8_t* __restrict__ plane, int row, int 
 }
 
 template <int KK, int VK>
-__global__ __launch_bounds__(64) void append_kernel(
+__global__ __launch_bounds__(256) void append_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int64_t n_tokens,
     int64_t start, const int32_t* __restrict__ block_table, int64_t group0, uint8_t* pool,
     int64_t n_pool_pages, int64_t page_bytes, int n_kv_heads, int32_t* status) {
-  const int lane = threadIdx.x;
+  __shared__ uint8_t vcode_hi[kHeadDim];  // V codes of the upper token (4-bit V)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.y;
   const int64_t grp = group0 + blockIdx.x / 16;
   const int i = blockIdx.x % 16;
   const int64_t t_lo = 32 * grp + i, t_hi = t_lo + 16;
   const bool in_lo = t_lo >= start && t_lo < start + n_tokens;
   const bool in_hi = t_hi >= start && t_hi < start + n_tokens;
-  if (!in_lo && !in_hi) return;
+  if (!in_lo && !in_hi) return;  // uniform over the workgroup
   const int64_t page = t_lo / kPageTokens;
   const int32_t phys = block_table[page];
   if (phys < 0 || phys >= n_pool_pages) {
-    if (status && lane == 0) atomicOr(status, KV_STATUS_BAD_PAGE_ID);
+    if (status && threadIdx.x == 0) atomicOr(status, KV_STATUS_BAD_PAGE_ID);
     return;
   }
   uint8_t* head = pool + (int64_t)phys * page_bytes + (int64_t)h * (plane_bytes(KK) + plane_bytes(VK));
@@ -155,41 +175,50 @@ __global__ __launch_bounds__(64) void append_kernel(
   const int row_lo = (int)(t_lo % kPageTokens), row_hi = row_lo + 16;
   const size_t stride = (size_t)n_kv_heads * kHeadDim;
 
-  int code[4];
-  uint16_t scale[4];
-  // K records, one token at a time
-  if (in_lo) {
-    encode<KK>(k + (size_t)(t_lo - start) * stride + (size_t)h * kHeadDim, lane, code, scale);
-    write_k_row<KK>(kplane, row_lo, lane, code, scale);
-  }
-  if (in_hi) {
-    encode<KK>(k + (size_t)(t_hi - start) * stride + (size_t)h * kHeadDim, lane, code, scale);
-    write_k_row<KK>(kplane, row_hi, lane, code, scale);
-  }
-  // V records of both tokens, then their shared element-major bytes
-  int vlo[4] = {0, 0, 0, 0}, vhi[4] = {0, 0, 0, 0};
-  if (in_lo) {
-    encode<VK>(v + (size_t)(t_lo - start) * stride + (size_t)h * kHeadDim, lane, vlo, scale);
-    write_v_scales<VK>(vplane, row_lo, lane, scale);
-  }
-  if (in_hi) {
-    encode<VK>(v + (size_t)(t_hi - start) * stride + (size_t)h * kHeadDim, lane, vhi, scale);
-    write_v_scales<VK>(vplane, row_hi, lane, scale);
-  }
+  const bool upper = wave & 1, is_v = wave >= 2;
+  const bool in = upper ? in_hi : in_lo;
+  const int64_t t = upper ? t_hi : t_lo;
+  const int row = upper ? row_hi : row_lo;
+  // 4-bit V bytes of lane elements (rows e, column of the pair)
+  uint8_t* vbyte[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int e = lane + 64 * kk;
-    uint8_t* row = vplane + (size_t)e * code_row_bytes(VK);
-    if (VK == kInt8) {
-      if (in_lo) row[row_lo] = (uint8_t)(int8_t)vlo[kk];
-      if (in_hi) row[row_hi] = (uint8_t)(int8_t)vhi[kk];
+  for (int kk = 0; kk < 4; ++kk)
+    vbyte[kk] = vplane + (size_t)(lane + 64 * kk) * code_row_bytes(VK) + 16 * (row_lo >> 5) + (row_lo & 15);
+  // with one token of the pair outside the chunk, wave 2 keeps the other nibble
+  uint8_t old[4] = {0, 0, 0, 0};
+  if (VK == kQ4 && wave == 2 && !(in_lo && in_hi)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) old[kk] = *vbyte[kk];
+  }
+
+  int code[4] = {0, 0, 0, 0};
+  uint16_t scale[4];
+  if (in) {
+    const size_t src = (size_t)(t - start) * stride + (size_t)h * kHeadDim;
+    if (!is_v) {
+      encode<KK>(k + src, lane, code, scale);
+      write_k_row<KK>(kplane, row, lane, code, scale);
     } else {
-      uint8_t* byte = row + 16 * (row_lo >> 5) + (row_lo & 15);
-      uint8_t val;
-      if (in_lo && in_hi) val = (uint8_t)(vlo[kk] | (vhi[kk] << 4));
-      else if (in_lo) val = (uint8_t)((*byte & 0xF0) | vlo[kk]);
-      else val = (uint8_t)((*byte & 0x0F) | (vhi[kk] << 4));
-      *byte = val;
+      encode<VK>(v + src, lane, code, scale);
+      write_v_scales<VK>(vplane, row, lane, scale);
+      if (VK == kInt8) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) vplane[(size_t)(lane + 64 * kk) * code_row_bytes(VK) + row] = (uint8_t)(int8_t)code[kk];
+      } else if (upper) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) vcode_hi[lane + 64 * kk] = (uint8_t)code[kk];
+      }
+    }
+  }
+  if (VK == kQ4) {
+    __syncthreads();
+    if (wave == 2) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int lo = in_lo ? code[kk] : (old[kk] & 0x0F);
+        const int hi = in_hi ? vcode_hi[lane + 64 * kk] : (old[kk] >> 4);
+        *vbyte[kk] = (uint8_t)(lo | (hi << 4));
+      }
     }
   }
 }
@@ -204,7 +233,7 @@ hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint1
   const int64_t g0 = start_pos / 32, g1 = (start_pos + n_tokens - 1) / 32;
   const int64_t pairs = (g1 - g0 + 1) * 16;
   const int64_t page_bytes = (int64_t)n_kv_heads * head_stride(fmt);
-  dim3 grid((unsigned)pairs, (unsigned)n_kv_heads), block(64);
+  dim3 grid((unsigned)pairs, (unsigned)n_kv_heads), block(256);
   switch (fmt) {
     case KV_FMT_INT8:
       hipLaunchKernelGGL((append_kernel<kInt8, kInt8>), grid, block, 0, stream, k, v, n_tokens,

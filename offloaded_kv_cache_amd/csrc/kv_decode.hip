@@ -127,18 +127,18 @@ template <int KK>
 __device__ inline KTile load_ktile(const uint8_t* kpl, int row, int grp) {
   KTile t;
   if (KK == kQ4) {
-    const u4* cp = reinterpret_cast<const u4*>(kpl + (size_t)row * 128 + 32 * grp);
+    const u4* cp = reinterpret_cast<const u4*>(kpl + (uint32_t)(row * 128 + 32 * grp));
     t.c0 = cp[0];
     t.c1 = cp[1];
     t.c2 = t.c3 = (u4){0, 0, 0, 0};
-    t.d = *reinterpret_cast<const u4*>(kpl + 256 * 128 + (size_t)row * 16);
+    t.d = *reinterpret_cast<const u4*>(kpl + (uint32_t)(256 * 128 + row * 16));
   } else {
-    const u4* cp = reinterpret_cast<const u4*>(kpl + (size_t)row * 256 + 64 * grp);
+    const u4* cp = reinterpret_cast<const u4*>(kpl + (uint32_t)(row * 256 + 64 * grp));
     t.c0 = cp[0];
     t.c1 = cp[1];
     t.c2 = cp[2];
     t.c3 = cp[3];
-    const u2 dd = *reinterpret_cast<const u2*>(kpl + 256 * 256 + (size_t)row * 8);
+    const u2 dd = *reinterpret_cast<const u2*>(kpl + (uint32_t)(256 * 256 + row * 8));
     t.d = (u4){dd[0], dd[1], 0, 0};
   }
   return t;
@@ -202,7 +202,7 @@ template <int VK>
 __device__ inline void load_vcodes(VShare<VK>& v, const uint8_t* vpl, int wave, int lane, int nt) {
   const int grp = lane >> 4, col = lane & 15;
   const int e = 64 * wave + 16 * nt + col;
-  const u4* src = reinterpret_cast<const u4*>(vpl + (size_t)e * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
+  const u4* src = reinterpret_cast<const u4*>(vpl + (uint32_t)(e * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp));
 #pragma unroll
   for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = src[u];
 }
@@ -210,18 +210,18 @@ __device__ inline void load_vcodes(VShare<VK>& v, const uint8_t* vpl, int wave, 
 // The scales the lane turns into B parts.
 template <int VK>
 __device__ inline void load_vscales(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
-  const uint16_t* vs = reinterpret_cast<const uint16_t*>(vpl + kHeadDim * code_row_bytes(VK));
+  const uint32_t vs = kHeadDim * code_row_bytes(VK);  // byte offset of the scales
   if (VK == kQ4) {
     // B-part entry (block 2w + bb, MFMA i, lane group gq): tokens t_lo..+3 and t_lo+16..+19
     const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
     const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
-    const uint16_t* row = vs + (2 * wave + bb) * kPageTokens;
-    v.s0 = *reinterpret_cast<const u2*>(row + t_lo);
-    v.s1 = *reinterpret_cast<const u2*>(row + t_lo + 16);
+    const uint32_t row = vs + (uint32_t)(((2 * wave + bb) * kPageTokens + t_lo) * 2);
+    v.s0 = *reinterpret_cast<const u2*>(vpl + row);
+    v.s1 = *reinterpret_cast<const u2*>(vpl + row + 32);
   } else {
     // entry (MFMA i, lane group gq) = tokens 64gq + 8i .. +7 of group w (lanes 0..31)
     const int i = (lane >> 2) & 7, gq = lane & 3;
-    const u4 d = *reinterpret_cast<const u4*>(vs + wave * kPageTokens + 64 * gq + 8 * i);
+    const u4 d = *reinterpret_cast<const u4*>(vpl + vs + (uint32_t)((wave * kPageTokens + 64 * gq + 8 * i) * 2));
     v.s0 = (u2){d[0], d[1]};
     v.s1 = (u2){d[2], d[3]};
   }
@@ -303,7 +303,18 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     return pool + (int64_t)phys * page_bytes + (int64_t)g * head_bytes;
   };
 
-  // prefetch the first page's share: 4 K tiles (tokens 64w..64w+63) and the V share
+  // ---- query of the group's heads (element tid), rotated by H when K is stored rotated
+  // (unconditional loads of a clamped head, so that all eight are in flight together)
+  float qv[kMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    const int hc = min(hh, G - 1);
+    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + tid]);
+    qv[hh] = hh < G ? x : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // then the first page's share: 4 K tiles (tokens 64w..64w+63) and the V share, issued
+  // after the query so that the wait for the query does not also wait for the page
   KTile kt[4];
   VShare<VK> vsh;
   const uint8_t* base = page_base(p_begin);
@@ -314,46 +325,44 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     load_vshare<VK>(vsh, src + plane_bytes(KK), wave, lane);
   }
 
-  // ---- query of the group's heads (element tid), rotated by H when K is stored rotated
-  float qv[kMaxGroup];
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh)
-    qv[hh] = hh < G ? (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hh) * kHeadDim + tid]) : 0.f;
+  // (all eight head slots are transformed, unused ones hold zeros, so that each step's
+  // exchanges are in flight together)
   if (KK == kQ4) {
 #pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      if (hh < G) {  // uniform
+    for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
+      const int m = 1 << bit;
+      float o[kMaxGroup];
 #pragma unroll
-        for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
-          const int m = 1 << bit;
-          const float o = __shfl_xor(qv[hh], m);
-          qv[hh] = (lane & m) ? (o - qv[hh]) : (qv[hh] + o);
-        }
-        lds.qs[hh][tid] = qv[hh];
-      }
+      for (int hh = 0; hh < kMaxGroup; ++hh) o[hh] = __shfl_xor(qv[hh], m);
+#pragma unroll
+      for (int hh = 0; hh < kMaxGroup; ++hh) qv[hh] = (lane & m) ? (o[hh] - qv[hh]) : (qv[hh] + o[hh]);
     }
+#pragma unroll
+    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
     __syncthreads();
     const int e0 = tid & 63, k = tid >> 6;  // bits 6 and 7: a 4-point transform across waves
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh) {
-      if (hh < G) {
-        const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
-                    x3 = lds.qs[hh][e0 + 192];
-        const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
-        qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
-      }
+      const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
+                  x3 = lds.qs[hh][e0 + 192];
+      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
+      qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    lds.qs[hh][tid] = qv[hh];
-    if (hh < G) {
-      // block sums of the (rotated) query: 32 elements (q4 blocks) or 64 (int8 groups)
-      float sum = qv[hh];
+  for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+  __syncthreads();
+  {
+    // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8)
+    constexpr int nb = KK == kQ4 ? 8 : 4, bl = kHeadDim / nb;
+    if (tid < kMaxGroup * nb) {
+      const int hh = tid / nb, j = tid % nb;
+      const f4* src = reinterpret_cast<const f4*>(&lds.qs[hh][j * bl]);
+      f4 acc = src[0];
 #pragma unroll
-      for (int o = 1; o < (KK == kQ4 ? 32 : 64); o <<= 1) sum += __shfl_xor(sum, o);
-      if ((tid & (KK == kQ4 ? 31 : 63)) == 0) lds.bsum[hh][tid >> (KK == kQ4 ? 5 : 6)] = sum;
+      for (int u = 1; u < bl / 4; ++u) acc += src[u];
+      lds.bsum[hh][j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     }
   }
   __syncthreads();
