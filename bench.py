@@ -129,6 +129,11 @@ def run_resident(args, wl, dev):
     stream = torch.cuda.current_stream()
     per_tok = kv_bytes_per_token(fmt)
     timed_split = []
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(n_steps)]
+    for pair in (p for row in events for p in row):
+        for e in pair:
+            e.record(stream)  # creates the events before the timed region
 
     def step(st, timing):
         for layer in range(L):
@@ -136,17 +141,17 @@ def run_resident(args, wl, dev):
                 T = start_lens[b] + st + 1
                 pools[layer].append(knew[st, layer, b], vnew[st, layer, b], T - 1,
                                     tables[layer][b].contiguous() if B > 1 else tables[layer][0])
-            if timing:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
+            # the split kernel's own start and end are recorded on its stream (kernel duration
+            # without the queueing gap in front of it)
+            evs = events[st][layer] if timing else None
             K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
-                               out, ws.data, pages_per_split=args.pages_per_split, phase="split")
+                               out, ws.data, pages_per_split=args.pages_per_split, phase="split",
+                               stream=stream, events=evs)
             if timing:
-                e1.record(stream)
-                timed_split.append((e0, e1, sum(start_lens[b] + st + 1 for b in range(B)) * per_tok))
+                timed_split.append((evs[0], evs[1], sum(start_lens[b] + st + 1 for b in range(B)) * per_tok))
             K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
-                               out, ws.data, pages_per_split=args.pages_per_split, phase="combine")
+                               out, ws.data, pages_per_split=args.pages_per_split, phase="combine",
+                               stream=stream)
 
     for st in range(args.warmup):
         step(st, False)
@@ -229,6 +234,26 @@ def cpu_baseline(args, wl, dev, state):
                 host_cpus=len(os.sched_getaffinity(0)))
 
 
+def copy_calibration(args, dev):
+    """A plain copy of known size: its counter readings scale the decode kernel's."""
+    import torch
+    n = args.copy_calibration << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    print(json.dumps({"copy_bytes": n, "copies": args.steps, "us_per_copy": round(us, 3),
+                      "read_plus_write_GBs": round(2 * n / us / 1e3, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +264,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB --steps times "
+                         "(reference kernel for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the single-GPU decode path "
@@ -249,6 +277,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(args, dev)
+        return
     wl = WORKLOADS[args.workload]
     res, state = run_resident(args, wl, dev)
     cpu = None

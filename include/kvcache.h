@@ -206,6 +206,23 @@ int kv_decode_combine(const kv_shape* shape, const void* q, int32_t batch,
                       int32_t pages_per_split, void* stream);
 
 /*
+ * kv_decode_split with measurement events: identical work and checks, and the
+ * kernel is launched with hipExtLaunchKernelGGL so that `start_event` and
+ * `stop_event` (hipEvent_t created by the caller, may be NULL) are recorded
+ * when the split-K kernel itself starts and ends on `stream`. The elapsed time
+ * between them is the kernel's duration without the queueing gap in front of
+ * it, which is what a kernel trace reports.
+ */
+int kv_decode_split_timed(const kv_shape* shape, const void* q, int32_t batch,
+                          const void* pool, int64_t n_pool_pages,
+                          const int32_t* block_tables, int32_t max_pages,
+                          const int32_t* context_lens, int64_t max_context,
+                          float softmax_scale, float* out,
+                          void* workspace, size_t workspace_bytes,
+                          int32_t pages_per_split, void* stream,
+                          void* start_event, void* stop_event);
+
+/*
  * Residency table of one layer's device page slots (Strata page, section
  * "KV 从显存搬进内存之后发生了什么": a residency table with CLOCK second-chance
  * eviction). Plain host memory owned by the caller:

@@ -23,7 +23,8 @@ FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4}
 
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
-    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_decode_split", "kv_decode_combine",
+    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_decode_split", "kv_decode_split_timed",
+    "kv_decode_combine",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
 )
@@ -64,6 +65,8 @@ def _load():
                                       P, P, SZ, I32, P]),
         "kv_decode_combine": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                         P, P, SZ, I32, P]),
+        "kv_decode_split_timed": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
+                                            P, P, SZ, I32, P, P, P]),
         "kv_residency_reset": (C.c_int, [C.POINTER(KVResidency)]),
         "kv_residency_select": (C.c_int, [C.POINTER(KVResidency), P, I32, P, P, P, P]),
         "kv_gather_pages": (C.c_int, [C.POINTER(KVShape), C.POINTER(KVResidency), P, I32, P, P, P,
@@ -164,12 +167,25 @@ _PHASES = {"all": "kv_decode_attention", "split": "kv_decode_split", "combine": 
 
 def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
                      workspace, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
-                     stream=None, phase: str = "all"):
+                     stream=None, phase: str = "all", events=None):
     """GQA decode attention over the paged cache; writes fp32 ``out`` [B, Hq, 256].
 
-    ``phase`` = "split" or "combine" enqueues only that kernel (see kvcache.h)."""
+    ``phase`` = "split" or "combine" enqueues only that kernel (see kvcache.h).
+    ``events`` = (start, stop) torch.cuda.Event pair, with phase "split" only:
+    recorded at the split kernel's own start and end (kv_decode_split_timed)."""
     torch = _torch()
     fn = getattr(lib, _PHASES[phase])
+    extra = ()
+    if events is not None:
+        if phase != "split":
+            raise ValueError("events are recorded around the split kernel only (phase='split')")
+        ev = []
+        for e in events:
+            if not e.cuda_event:
+                e.record()  # creates the underlying event
+            ev.append(C.c_void_p(e.cuda_event))
+        fn = lib.kv_decode_split_timed
+        extra = tuple(ev)
     B = q.shape[0]
     if q.shape != (B, s.n_q_heads, s.head_dim) or out.shape != (B, s.n_q_heads, s.head_dim):
         raise ValueError("q and out must be [batch, n_q_heads, head_dim]")
@@ -181,7 +197,7 @@ def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_contex
         pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
         softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream)))
+        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream), *extra))
 
 
 class Residency:

@@ -170,7 +170,8 @@ namespace {
 int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch, const void* pool,
                  int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
                  const int32_t* context_lens, int64_t max_context, float softmax_scale, float* out,
-                 void* workspace, size_t workspace_bytes, int32_t pages_per_split, void* stream) {
+                 void* workspace, size_t workspace_bytes, int32_t pages_per_split, void* stream,
+                 void* start_event = nullptr, void* stop_event = nullptr) {
   if (int r = check_shape(shape)) return r;
   if (batch < 0 || batch > 65535) return fail(KV_EINVAL, "batch out of range (%d)", batch);
   if (batch == 0) return ok();
@@ -212,7 +213,7 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.status = (int32_t*)ws;
   a.part_ml = (float*)(ws + w.ml_off);
   a.part_o = (float*)(ws + w.o_off);
-  hipError_t e = launch_decode(a, phase, (hipStream_t)stream);
+  hipError_t e = launch_decode(a, phase, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
 }
@@ -239,6 +240,17 @@ int kv_decode_split(const kv_shape* shape, const void* q, int32_t batch, const v
   return decode_phase(1, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
                       max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
                       stream);
+}
+
+int kv_decode_split_timed(const kv_shape* shape, const void* q, int32_t batch, const void* pool,
+                          int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
+                          const int32_t* context_lens, int64_t max_context, float softmax_scale,
+                          float* out, void* workspace, size_t workspace_bytes,
+                          int32_t pages_per_split, void* stream, void* start_event,
+                          void* stop_event) {
+  return decode_phase(1, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
+                      max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
+                      stream, start_event, stop_event);
 }
 
 int kv_decode_combine(const kv_shape* shape, const void* q, int32_t batch, const void* pool,

@@ -51,6 +51,8 @@
 // Tokens past the context length are masked (score -inf, scale 0), so stale
 // or uninitialised rows of a partly filled page never contribute. Nothing
 // depends on the physical page ids except the addresses read.
+#include <hip/hip_ext.h>
+
 #include "kv_internal.h"
 
 namespace kvc {
@@ -747,24 +749,25 @@ __global__ __launch_bounds__(256) void decode_combine(
 }
 
 template <int KK, int VK>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch), block(256);
-  hipLaunchKernelGGL((decode_split<KK, VK>), grid, block, 0, stream, a.q, a.pool, a.n_pool_pages,
-                     a.block_tables, a.max_pages, a.context_lens, a.max_context, a.n_q_heads,
-                     a.n_kv_heads, a.pages_per_split, a.n_splits, a.scale_log2, a.part_ml,
-                     a.part_o, a.status);
+  hipExtLaunchKernelGGL((decode_split<KK, VK>), grid, block, 0, stream, start, stop, 0, a.q, a.pool,
+                        a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens, a.max_context,
+                        a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits, a.scale_log2,
+                        a.part_ml, a.part_o, a.status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop) {
   if (phase & 1) {
     hipError_t e;
     switch (a.fmt) {
-      case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream); break;
-      case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream); break;
-      default: e = launch_split<kInt8, kQ4>(a, stream); break;
+      case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream, start, stop); break;
+      case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream, start, stop); break;
+      default: e = launch_split<kInt8, kQ4>(a, stream, start, stop); break;
     }
     if (e != hipSuccess) return e;
   }

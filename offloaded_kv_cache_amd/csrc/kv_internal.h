@@ -112,8 +112,10 @@ struct DecodeArgs {
   float* part_o;              // [batch][n_q_heads][n_splits][256]
 };
 
-// phase: 1 = split kernel only, 2 = combine only, 3 = both
-hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream);
+// phase: 1 = split kernel only, 2 = combine only, 3 = both. start/stop (may be
+// null) are recorded at the split kernel's own start and end.
+hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 constexpr int kGatherMaxBatch = 256;  // selections per gather launch (kernel-argument size)
 

@@ -207,3 +207,28 @@ def test_append_then_decode_end_to_end(gpu, fmt):
         torch.cuda.synchronize()
         seq = Sequence(25, 0, 0, T, fmt, k=k[:T], v=v[:T])
         assert_close(out.cpu().numpy(), oracle_out(q, [seq], fmt), what=f"step {st}")
+
+
+def test_decode_split_timed_matches_split(gpu):
+    """kv_decode_split_timed does the same work as kv_decode_split and records its events."""
+    fmt = "q4_0"
+    seqs = [Sequence(26, 0, 0, 2500, fmt)]
+    q = kvsynth.q_np(26, 0, 1)
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    pool_np, bt = place_pages(seqs, 12, 7, pb)
+    pool, btd = to_dev(pool_np, gpu), to_dev(bt, gpu)
+    qd, ctx = to_dev(q, gpu), to_dev(np.array([2500], np.int32), gpu)
+    outs = []
+    for timed in (False, True):
+        ws = K.paged.DecodeWorkspace(s, 1, 2500, 0, device=gpu)
+        out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+        K.decode_attention(s, qd, pool, btd, ctx, 2500, out, ws.data, phase="split", events=ev)
+        K.decode_attention(s, qd, pool, btd, ctx, 2500, out, ws.data, phase="combine")
+        torch.cuda.synchronize()
+        if timed:
+            assert ev[0].elapsed_time(ev[1]) > 0
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    assert_close(outs[1], oracle_out(q, seqs, fmt))
