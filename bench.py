@@ -234,6 +234,26 @@ def cpu_baseline(args, wl, dev, state):
                 host_cpus=len(os.sched_getaffinity(0)))
 
 
+def counter_traffic(workload: str):
+    """HBM bytes per decode_split launch from the committed counter summary, or None.
+
+    The summary records the sha256 of the kernel source its counters were taken
+    with; a kernel changed since then gives None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_q4_0_128k_hbm_bytes.txt")
+    if workload != "c3" or not os.path.exists(path):
+        return None
+    sha = traffic = None
+    for line in open(path):
+        if line.startswith("kernel source sha256"):
+            sha = line.rsplit(":", 1)[1].strip()
+        elif line.startswith("decode_split traffic bytes per launch:"):
+            traffic = int(float(line.rsplit(":", 1)[1]))
+    src = os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", "kv_decode.hip")
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return traffic if sha == cur else None
+
+
 def copy_calibration(args, dev):
     """A plain copy of known size: its counter readings scale the decode kernel's."""
     import torch
@@ -310,7 +330,7 @@ def main():
         "pct_of_hbm_peak": round(100 * res["value"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(res["achieved"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(res["split_us"], 3),
+                     "traffic": counter_traffic(args.workload), "avg_launch_us": round(res["split_us"], 3),
                      "bytes_per_launch": int(res["split_bytes"])},
         "append_2048_chunk_us": round(res["append_chunk_us"], 3) if res["append_chunk_us"] else None,
         "cpu_baseline": cpu,
