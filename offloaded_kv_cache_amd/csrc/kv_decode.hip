@@ -673,79 +673,110 @@ __global__ __launch_bounds__(256, 2) void decode_split(
 }
 
 // Log-sum-exp merge of the partials of one (query head, sequence), then the
-// rotation back by H. The split weights are staged in LDS so that the loop
-// over splits issues independent loads.
+// rotation back by H. 1,024 threads: four groups of 256 (one thread per head
+// element) each merge a quarter of the splits. A thread's 32 partial values of
+// a pass are loaded together with the split maxima, before the weights are
+// known; the group sums are added in a fixed order.
+constexpr int kCombineThreads = 1024;
+constexpr int kCombineGroups = kCombineThreads / kHeadDim;
+constexpr int kCombineRun = 32;                                // splits per thread per pass
+constexpr int kCombinePass = kCombineGroups * kCombineRun;     // splits per pass
+
 template <bool ROTATE>
-__global__ __launch_bounds__(256) void decode_combine(
+__global__ __launch_bounds__(kCombineThreads) void decode_combine(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ context_lens, int max_context, int n_q_heads,
     int pages_per_split, int n_splits, float* __restrict__ out) {
-  __shared__ float buf[kHeadDim];
-  __shared__ float wts[1024];
-  __shared__ float red[2][4];
-  const int tid = threadIdx.x, h = blockIdx.x, b = blockIdx.y;
+  __shared__ float wts[kCombineThreads];
+  __shared__ float part[kCombineGroups][kHeadDim];
+  __shared__ float red[2][kCombineThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = tid & (kHeadDim - 1), sg = tid / kHeadDim;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const size_t base = ((size_t)b * n_q_heads + h) * (size_t)n_splits;
+  // issued before the context length is known: split tid's maximum and the first
+  // pass of partials (indices clamped to the grid's splits)
+  const float m_first = part_ml[2 * (base + min(tid, n_splits - 1))];
+  float v[kCombineRun];
+#pragma unroll
+  for (int u = 0; u < kCombineRun; ++u)
+    v[u] = part_o[(base + min(sg * kCombineRun + u, n_splits - 1)) * kHeadDim + e];
   int T = context_lens[b];
   T = T < 0 ? 0 : (T > max_context ? max_context : T);
   const int n_pages = (T + kPageTokens - 1) / kPageTokens;
-  const int ns = (n_pages + pages_per_split - 1) / pages_per_split;
-  const size_t base = ((size_t)b * n_q_heads + h) * (size_t)n_splits;
-  float o = 0.f;
-  if (ns > 0) {
-    float M = -INFINITY;
-    for (int s = tid; s < ns; s += 256) M = fmaxf(M, part_ml[2 * (base + s)]);
+  const int ns = min(n_splits, (n_pages + pages_per_split - 1) / pages_per_split);
+  float o = 0.f, L = 0.f;
+  if (ns > 0) {  // uniform over the workgroup
+    float M = tid < ns ? m_first : -INFINITY;
+    for (int s = tid + kCombineThreads; s < ns; s += kCombineThreads) M = fmaxf(M, part_ml[2 * (base + s)]);
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((tid & 63) == 0) red[0][tid >> 6] = M;
+    if (lane == 0) red[0][wave] = M;
     __syncthreads();
-    M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    float L = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += 1024) {
-      const int cnt = min(1024, ns - s0);
+    M = red[0][0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[0][w]);
+    float acc = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += kCombineThreads) {  // chunks of splits whose weights fit in LDS
+      const int cnt = min(kCombineThreads, ns - s0);
       __syncthreads();
-      for (int s = tid; s < cnt; s += 256) {
-        const float ms = part_ml[2 * (base + s0 + s)];
+      if (tid < cnt) {
+        const float ms = s0 == 0 ? m_first : part_ml[2 * (base + s0 + tid)];
         const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        wts[s] = w;
-        L += w * part_ml[2 * (base + s0 + s) + 1];
+        wts[tid] = w;
+        L += w * part_ml[2 * (base + s0 + tid) + 1];
       }
       __syncthreads();
-      float acc[16];
+      for (int p0 = 0; p0 < cnt; p0 += kCombinePass) {
+        const int first = p0 + sg * kCombineRun;  // this group's run of the pass
+        if (s0 + p0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-      int s = 0;
-      for (; s + 16 <= cnt; s += 16) {  // 16 independent loads in flight per thread
-        const float* po = part_o + (base + s0 + s) * kHeadDim + tid;
-        float v[16];
+          for (int u = 0; u < kCombineRun; ++u)
+            v[u] = part_o[(base + min(s0 + first + u, ns - 1)) * kHeadDim + e];
+        }
+        float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = po[u * kHeadDim];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] += wts[s + u] * v[u];
+        for (int u = 0; u < kCombineRun; ++u) {
+          const int s = first + u;
+          a += s < cnt ? wts[min(s, kCombineThreads - 1)] * v[u] : 0.f;  // splits past ns add nothing
+        }
+        acc += a;
       }
-      for (; s < cnt; ++s) acc[0] += wts[s] * part_o[(base + s0 + s) * kHeadDim + tid];
-#pragma unroll
-      for (int u = 1; u < 16; ++u) acc[0] += acc[u];
-      o += acc[0];
     }
+    part[sg][e] = acc;
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
-    __syncthreads();
-    if ((tid & 63) == 0) red[1][tid >> 6] = L;
-    __syncthreads();
-    L = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    if (lane == 0) red[1][wave] = L;
+  }
+  __syncthreads();
+  if (ns > 0 && sg == 0) {
+    o = part[0][e];
+#pragma unroll
+    for (int g = 1; g < kCombineGroups; ++g) o += part[g][e];
+    L = red[1][0];
+#pragma unroll
+    for (int w = 1; w < kCombineThreads / 64; ++w) L += red[1][w];
     o = L > 0.f ? o / L : 0.f;  // L == 0 only if every page of the sequence was skipped
   }
   if (ROTATE) {
-    buf[tid] = o;
-    __syncthreads();
+    // bits 0..5 of the element index inside the wave, bits 6 and 7 through LDS
+    if (sg == 0) {
 #pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-      const int m = 1 << bit;
-      const float mine = buf[tid], other = buf[tid ^ m];
-      __syncthreads();
-      buf[tid] = (tid & m) ? (other - mine) : (mine + other);
-      __syncthreads();
+      for (int bit = 0; bit < 6; ++bit) {
+        const int m = 1 << bit;
+        const float other = __shfl_xor(o, m);
+        o = (lane & m) ? (other - o) : (o + other);
+      }
     }
-    o = buf[tid] * 0.0625f;
+    __syncthreads();
+    if (sg == 0) part[0][e] = o;
+    __syncthreads();
+    if (sg == 0) {
+      const int e0 = e & 63, k = e >> 6;
+      const float x0 = part[0][e0], x1 = part[0][e0 + 64], x2 = part[0][e0 + 128], x3 = part[0][e0 + 192];
+      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
+      o = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
+    }
   }
-  out[((size_t)b * n_q_heads + h) * kHeadDim + tid] = o;
+  if (sg == 0) out[((size_t)b * n_q_heads + h) * kHeadDim + e] = o;
 }
 
 template <int KK, int VK>
@@ -772,7 +803,7 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hip
     if (e != hipSuccess) return e;
   }
   if (phase & 2) {
-    dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch), block(256);
+    dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch), block(kCombineThreads);
     if (a.fmt == KV_FMT_INT8)
       hipLaunchKernelGGL((decode_combine<false>), grid, block, 0, stream, a.part_ml, a.part_o,
                          a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
