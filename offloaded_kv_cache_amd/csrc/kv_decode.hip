@@ -39,8 +39,11 @@
 //   fp16, and each part is applied with one packed fp16 fma on a "1024 + code"
 //   half (q4: B = (1024 + 16c) * (p/16) - 72p = (c - 8) p, parts of <= 7 and
 //   4 bits; int8: B = (1024 + c + 128) * p - 1152p = c p, three parts of <= 4
-//   bits). One MFMA per part. Scales too large for these constants (|d| >= 896
-//   for q4, >= 56 for int8) take a slower exact path for that page.
+//   bits). One MFMA per part. A page with a scale outside the range where these
+//   constants are exact (q4: |d| >= 896, or 0 < |d| < 2^-10 where p/16 would
+//   lose bits; int8: |d| >= 56) takes a slower path that forms (c - 8) or c
+//   exactly and multiplies it by the parts (exact while |8 d| stays below the
+//   fp16 maximum, i.e. rotated V elements below about 2^16 / 8 in magnitude).
 //
 //   The four waves then share the page maximum and sum; each writes its
 //   elements of the split's partial (max, sum, unnormalised output).
@@ -68,8 +71,9 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr float kPScale = 16384.0f;  // probabilities are kept as p * 2^14 in fp16 hi/lo
 constexpr float kPScaleInv = 1.0f / 16384.0f;
 constexpr float kTwo24 = 16777216.0f;
-constexpr float kQ4FastMax = 896.0f;   // |d| below this: -72 * d_hi is exact and finite
-constexpr float kI8FastMax = 56.0f;    // |d| below this: -1152 * d_part is exact and finite
+constexpr uint32_t kQ4FastBits = 0x6300;  // fp16 896: |d| below this, -72 * d_hi is exact and finite
+constexpr uint32_t kQ4FastMinM1 = 0x13FF;  // fp16 2^-10 minus one: |d| from here up, d_lo / 16 is exact
+constexpr uint32_t kI8FastBits = 0x5300;  // fp16 56: |d| below this, -1152 * d_part is exact and finite
 constexpr int kWaves = 4;
 constexpr int kQsStride = kHeadDim + 4;  // padded rows of the query in LDS (bank spread)
 
@@ -86,6 +90,27 @@ __device__ inline uint32_t vgpr_const(uint32_t c) {
   uint32_t r;
   asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
   return r;
+}
+
+// Largest |d| of eight fp16 scales, as the bit pattern of |d| (NaN patterns compare
+// above every finite value).
+__device__ inline uint32_t max_abs_bits(u4 w) {
+  typedef uint16_t us2 __attribute__((ext_vector_type(2)));
+  const us2 a = __builtin_elementwise_max(__builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu), __builtin_bit_cast(us2, w[1] & 0x7FFF7FFFu));
+  const us2 b = __builtin_elementwise_max(__builtin_bit_cast(us2, w[2] & 0x7FFF7FFFu), __builtin_bit_cast(us2, w[3] & 0x7FFF7FFFu));
+  const us2 m = __builtin_elementwise_max(a, b);
+  return m[0] > m[1] ? m[0] : m[1];
+}
+
+// Smallest (|d| bits - 1) of eight fp16 scales, with 0 wrapping to 0xFFFF (so a zero
+// scale never counts as small).
+__device__ inline uint32_t min_abs_bits_m1(u4 w) {
+  typedef uint16_t us2 __attribute__((ext_vector_type(2)));
+  const us2 one = {1, 1};
+  const us2 a = __builtin_elementwise_min(__builtin_bit_cast(us2, w[0] & 0x7FFF7FFFu) - one, __builtin_bit_cast(us2, w[1] & 0x7FFF7FFFu) - one);
+  const us2 b = __builtin_elementwise_min(__builtin_bit_cast(us2, w[2] & 0x7FFF7FFFu) - one, __builtin_bit_cast(us2, w[3] & 0x7FFF7FFFu) - one);
+  const us2 m = __builtin_elementwise_min(a, b);
+  return m[0] < m[1] ? m[0] : m[1];
 }
 
 __device__ inline float half_max(float v) {  // max over the 16 lanes of a lane group
@@ -405,8 +430,6 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     const _Float16 lo = (_Float16)(f - (float)hi);
     qc[s] = (a_live && grp == 0) ? (a_part ? lo : hi) : (_Float16)0;
   }
-  // heads >= G never get probabilities: their fragment rows stay zero
-  for (int idx = tid; idx < 8 * 64; idx += 256) lds.afrag[idx >> 6][idx & 63] = (h8){0, 0, 0, 0, 0, 0, 0, 0};
 
   const uint32_t vmask = vgpr_const(0x00F000F0u), vmagic = vgpr_const(0x64006400u);
   const int h0 = 2 * grp, h1 = 2 * grp + 1;
@@ -459,60 +482,54 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       if (VK == kQ4) {
         const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
         const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
-        h8 dh16, nh, dl16, nl;
-        float amax = 0.f;
+        // slot u = scale of token t_lo + (u & 3) + 16 (u >> 2): half (u & 1) of word u >> 1
+        u4 wv = {vsh.s0[0], vsh.s0[1], vsh.s1[0], vsh.s1[1]};
+        if (valid < kPageTokens) {  // a partial page: scales of rows past the context are 0
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int tt = t_lo + (u & 3) + 16 * (u >> 2);
-          const uint32_t word = (u < 4 ? vsh.s0 : vsh.s1)[(u & 3) >> 1];
-          uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
-          if (tt >= valid) bits = 0;
-          const _Float16 d = __builtin_bit_cast(_Float16, bits);
-          const _Float16 dh = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF0u));  // <= 7 bits
-          const _Float16 dl = d - dh;                                                     // <= 4 bits
-          dh16[u] = dh * (_Float16)0.0625f;
-          dl16[u] = dl * (_Float16)0.0625f;
-          nh[u] = dh * (_Float16)(-72.0f);
-          nl[u] = dl * (_Float16)(-72.0f);
-          amax = fmaxf(amax, fabsf((float)d));
+          for (int u = 0; u < 8; ++u)
+            if (t_lo + (u & 3) + 16 * (u >> 2) >= valid) wv[u >> 1] &= (u & 1) ? 0x0000FFFFu : 0xFFFF0000u;
         }
+        const h8 d = __builtin_bit_cast(h8, wv);
+        const h8 dh = __builtin_bit_cast(h8, wv & 0xFFF0FFF0u);  // <= 7 significant bits
+        const h8 dl = d - dh;                                    // <= 4 significant bits
+        // folded constants exact and finite: every |d| in [2^-10, 896) or 0
+        fast = !__any(!(max_abs_bits(wv) < kQ4FastBits && min_abs_bits_m1(wv) >= kQ4FastMinM1));
         h8* e = dp + ((bb * 8 + i) * 4 + gq);  // = dp + lane
-        e[0] = dh16;
-        e[64] = nh;
-        e[128] = dl16;
-        e[192] = nl;
-        fast = !__any(!(amax < kQ4FastMax));
+        if (fast) {
+          e[0] = dh * (_Float16)0.0625f;
+          e[64] = dh * (_Float16)(-72.0f);
+          e[128] = dl * (_Float16)0.0625f;
+          e[192] = dl * (_Float16)(-72.0f);
+        } else {  // the parts themselves, for exact (c - 8) * part products
+          e[0] = dh;
+          e[128] = dl;
+        }
       } else {
         const int i = (lane >> 2) & 7, gq = lane & 3;
         const int t0 = 64 * gq + 8 * i;
-        h8 pa_, pb_, pc_, na, nb, nc;
-        float amax = 0.f;
+        // slot u = scale of token t0 + u: half (u & 1) of word u >> 1
+        u4 wv = {vsh.s0[0], vsh.s0[1], vsh.s1[0], vsh.s1[1]};
+        if (valid < kPageTokens) {  // a partial page: scales of rows past the context are 0
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t word = (u < 4 ? vsh.s0 : vsh.s1)[(u & 3) >> 1];
-          uint16_t bits = (uint16_t)((u & 1) ? (word >> 16) : (word & 0xFFFFu));
-          if (t0 + u >= valid) bits = 0;
-          const _Float16 d = __builtin_bit_cast(_Float16, bits);
-          const _Float16 da = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFF80u));   // <= 4 bits
-          const _Float16 db8 = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFF8u));
-          pa_[u] = da;
-          pb_[u] = db8 - da;                                                             // <= 4 bits
-          pc_[u] = d - db8;                                                              // <= 3 bits
-          na[u] = pa_[u] * (_Float16)(-1152.0f);
-          nb[u] = pb_[u] * (_Float16)(-1152.0f);
-          nc[u] = pc_[u] * (_Float16)(-1152.0f);
-          amax = fmaxf(amax, fabsf((float)d));
+          for (int u = 0; u < 8; ++u)
+            if (t0 + u >= valid) wv[u >> 1] &= (u & 1) ? 0x0000FFFFu : 0xFFFF0000u;
         }
+        const h8 d = __builtin_bit_cast(h8, wv);
+        const h8 pa_ = __builtin_bit_cast(h8, wv & 0xFF80FF80u);   // <= 4 significant bits
+        const h8 db8 = __builtin_bit_cast(h8, wv & 0xFFF8FFF8u);
+        const h8 pb_ = db8 - pa_;                                  // <= 4 significant bits
+        const h8 pc_ = d - db8;                                    // <= 3 significant bits
         if (lane < 32) {
           h8* e = dp + (i * 4 + gq);  // = dp + lane
           e[0] = pa_;
-          e[32] = na;
+          e[32] = pa_ * (_Float16)(-1152.0f);
           e[64] = pb_;
-          e[96] = nb;
+          e[96] = pb_ * (_Float16)(-1152.0f);
           e[128] = pc_;
-          e[160] = nc;
+          e[160] = pc_ * (_Float16)(-1152.0f);
         }
-        fast = !__any(lane < 32 && !(amax < kI8FastMax));
+        const uint32_t amax_bits = lane < 32 ? max_abs_bits(wv) : 0u;
+        fast = !__any(!(amax_bits < kI8FastBits));
       }
     }
     load_vscales<VK>(vsh, nsrc + plane_bytes(KK), wave, lane);  // next page's scales
@@ -526,17 +543,20 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       pm1 = fmaxf(pm1, lds.wmax[w][h1]);
     }
     const float mn0 = fmaxf(m_run[0], pm0), mn1 = fmaxf(m_run[1], pm1);
-    // a page with no token in context leaves the state unchanged (max stays -inf)
-    const float al0 = mn0 == -INFINITY ? 1.f : exp2f(m_run[0] - mn0);
-    const float al1 = mn1 == -INFINITY ? 1.f : exp2f(m_run[1] - mn1);
+    // reference point of the exponentials: the new maximum, or 0 while no token of
+    // the split is in context (then every score and the old maximum are -inf, and
+    // 2^(-inf) = 0 leaves the zero state unchanged)
+    const float r0 = mn0 == -INFINITY ? 0.f : mn0, r1 = mn1 == -INFINITY ? 0.f : mn1;
+    const float al0 = __builtin_amdgcn_exp2f(m_run[0] - r0);
+    const float al1 = __builtin_amdgcn_exp2f(m_run[1] - r1);
     m_run[0] = mn0;
     m_run[1] = mn1;
     float sum0 = 0.f, sum1 = 0.f;
     _Float16* af = reinterpret_cast<_Float16*>(&lds.afrag[0][0]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const float p0 = xs[t][0] == -INFINITY ? 0.f : exp2f(xs[t][0] - mn0);
-      const float p1 = xs[t][1] == -INFINITY ? 0.f : exp2f(xs[t][1] - mn1);
+      const float p0 = __builtin_amdgcn_exp2f(xs[t][0] - r0);  // masked tokens: 2^(-inf) = 0
+      const float p1 = __builtin_amdgcn_exp2f(xs[t][1] - r1);
       sum0 += p0;
       sum1 += p1;
       // fragment position of token 64w + 16t + col for P.V MFMA i, lane (w, 2h + part), slot
@@ -552,14 +572,12 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       const float ps0 = p0 * kPScale, ps1 = p1 * kPScale;
       const _Float16 hi0 = (_Float16)ps0, hi1 = (_Float16)ps1;
       const _Float16 lo0 = (_Float16)(ps0 - (float)hi0), lo1 = (_Float16)(ps1 - (float)hi1);
-      if (h0 < G) {
-        af[base_idx + (2 * h0) * 8] = hi0;
-        af[base_idx + (2 * h0 + 1) * 8] = lo0;
-      }
-      if (h1 < G) {
-        af[base_idx + (2 * h1) * 8] = hi1;
-        af[base_idx + (2 * h1 + 1) * 8] = lo1;
-      }
+      // rows of heads >= G (zero query) are written too: they only feed output rows
+      // that are never stored
+      af[base_idx + (2 * h0) * 8] = hi0;
+      af[base_idx + (2 * h0 + 1) * 8] = lo0;
+      af[base_idx + (2 * h1) * 8] = hi1;
+      af[base_idx + (2 * h1 + 1) * 8] = lo1;
     }
     l_run[0] = l_run[0] * al0 + sum0;
     l_run[1] = l_run[1] * al1 + sum1;
@@ -614,7 +632,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
           const h8 pa = lds.afrag[i][lane];
           if (VK == kQ4) {
             const h8* e = dp + ((hf * 8 + i) * 4 + grp);
-            const h8 dh = e[0] * (_Float16)16.0f, dl = e[128] * (_Float16)16.0f;
+            const h8 dh = e[0], dl = e[128];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const int nt = 2 * hf + u;
