@@ -309,13 +309,24 @@ __global__ __launch_bounds__(256, 2) void decode_split(
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = n_q_heads / n_kv_heads;
 
+  // Issued together before anything waits: the query of the group's heads (element
+  // tid; unconditional loads of a clamped head), the context length and the split's
+  // first block-table entry (index clamped into the table).
+  float qv[kMaxGroup];
+#pragma unroll
+  for (int hh = 0; hh < kMaxGroup; ++hh) {
+    const int hc = min(hh, G - 1);
+    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + tid]);
+    qv[hh] = hh < G ? x : 0.f;
+  }
+  const int p_begin = split * pages_per_split;
+  const int32_t phys_first = block_tables[(size_t)b * max_pages + min(p_begin, max_pages - 1)];
   int T = context_lens[b];
   if (T > max_context || T < 0) {
     if (tid == 0 && split == 0 && g == 0) atomicOr(status, KV_STATUS_CONTEXT_CLAMPED);
     T = T < 0 ? 0 : max_context;
   }
   const int n_pages = (T + kPageTokens - 1) / kPageTokens;
-  const int p_begin = split * pages_per_split;
   const int p_end = min(n_pages, p_begin + pages_per_split);
   if (p_begin >= p_end) return;  // uniform over the workgroup
 
@@ -330,21 +341,14 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     return pool + (int64_t)phys * page_bytes + (int64_t)g * head_bytes;
   };
 
-  // ---- query of the group's heads (element tid), rotated by H when K is stored rotated
-  // (unconditional loads of a clamped head, so that all eight are in flight together)
-  float qv[kMaxGroup];
-#pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    const int hc = min(hh, G - 1);
-    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + tid]);
-    qv[hh] = hh < G ? x : 0.f;
-  }
   __builtin_amdgcn_sched_barrier(0);
   // then the first page's share: 4 K tiles (tokens 64w..64w+63) and the V share, issued
   // after the query so that the wait for the query does not also wait for the page
   KTile kt[4];
   VShare<VK> vsh;
-  const uint8_t* base = page_base(p_begin);
+  const uint8_t* base = phys_first < 0 || phys_first >= n_pool_pages
+                            ? nullptr
+                            : pool + (int64_t)phys_first * page_bytes + (int64_t)g * head_bytes;
   {
     const uint8_t* src = base ? base : pool;  // a bad page is read from page 0 and then ignored
 #pragma unroll
@@ -414,12 +418,15 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       f[0] = a4[0]; f[1] = a4[1]; f[2] = a4[2]; f[3] = a4[3];
       f[4] = b4[0]; f[5] = b4[1]; f[6] = b4[2]; f[7] = b4[3];
     }
+    // hi = f truncated to fp16, lo = the exact remainder truncated: ~21 bits together
+    u4 w;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const _Float16 hi = (_Float16)f[s];
-      const _Float16 lo = (_Float16)(f[s] - (float)hi);
-      qa[j][s] = a_live ? (a_part ? lo : hi) : (_Float16)0;
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f[2 * s2], f[2 * s2 + 1]));
+      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f[2 * s2] - (float)hi[0], f[2 * s2 + 1] - (float)hi[1]));
+      w[s2] = a_live ? as_u32(a_part ? lo : hi) : 0u;
     }
+    qa[j] = __builtin_bit_cast(h8, w);
   }
   // A operand of the offset correction: row 2*head + part, k-slot j (lane group 0) = block sum j
   h8 qc;

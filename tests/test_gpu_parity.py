@@ -232,3 +232,35 @@ def test_decode_split_timed_matches_split(gpu):
         outs.append(out.cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
     assert_close(outs[1], oracle_out(q, seqs, fmt))
+
+
+def extreme_v(v, fmt):
+    """Plant V vectors whose scales leave the folded-constant range: a huge one
+    (q4: y = H v has one element 32,000, so d = -4,000; int8: one element 8,000,
+    d ~ 63) and tiny ones (fp16 subnormal inputs, d far below 2^-10)."""
+    v = v.copy()
+    j = np.arange(256)
+    for h in range(v.shape[1]):
+        kk = 5 + 37 * h
+        sign = 1.0 - 2.0 * (np.array([bin(x & kk).count("1") for x in j]) & 1)
+        v[50, h] = (2000.0 * sign).astype(np.float16)           # q4: y_kk = 16 * 2000
+        v[51, h] = 0
+        v[51, h, 3 + h] = 8000.0                                  # int8: d = 8000 / 127
+        v[300, h] = (np.arange(256) % 7 - 3).astype(np.float16) * np.float16(2.0 ** -24)
+        v[301, h] = (np.arange(256) % 5 - 2).astype(np.float16) * np.float16(2.0 ** -16)
+    return v
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_extreme_scales(gpu, fmt):
+    """Pages whose V scales fall outside the fast path's exact range (huge, tiny,
+    subnormal) take the exact slower path and still match the oracle."""
+    T = 700
+    k, v = kvsynth.kv_tokens_np(27, 0, 0, 0, T)
+    v = extreme_v(v, fmt)
+    seqs = [Sequence(27, 0, 0, T, fmt, 4, k, v)]
+    q = kvsynth.q_np(27, 0, 1)
+    for pps in (0, 1):
+        got, status = run_decode(gpu, fmt, seqs, q, pps, seed=5 + pps)
+        assert status == 0
+        assert_close(got, oracle_out(q, seqs, fmt), what=f"{fmt} pps {pps}")
