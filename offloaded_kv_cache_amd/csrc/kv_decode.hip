@@ -183,27 +183,39 @@ __device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], h8 qc, float& 
   float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;  // hi and lo rows, units of 2^-24
   if (KK == kQ4) {
     const uint32_t w[8] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3]};
+    // software-pipelined: block j's scaling runs while block j + 1's MFMA is in flight
+    f4 cur = mfma(qa[0], k_codes_q4(w[0]), (f4){0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const f4 acc = mfma(qa[j], k_codes_q4(w[j]), (f4){0.f, 0.f, 0.f, 0.f});
+      f4 nxt;
+      if (j < 7) nxt = mfma(qa[j + 1], k_codes_q4(w[j + 1]), (f4){0.f, 0.f, 0.f, 0.f});
       const float d = scale_at(t.d, j);
-      a0 = fmaf(d, acc[0], a0);
-      b0 = fmaf(d, acc[1], b0);
-      a1 = fmaf(d, acc[2], a1);
-      b1 = fmaf(d, acc[3], b1);
+      a0 = fmaf(d, cur[0], a0);
+      b0 = fmaf(d, cur[1], b0);
+      a1 = fmaf(d, cur[2], a1);
+      b1 = fmaf(d, cur[3], b1);
+      if (j < 7) cur = nxt;
     }
   } else {
     const uint32_t w[16] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3],
                             t.c2[0], t.c2[1], t.c2[2], t.c2[3], t.c3[0], t.c3[1], t.c3[2], t.c3[3]};
+    // two chained MFMAs per 64-element group; a group is scaled while the next group's
+    // MFMAs are in flight
+    f4 cur = mfma(qa[0], k_codes_i8(w[0], w[1]), (f4){0.f, 0.f, 0.f, 0.f});
+    cur = mfma(qa[1], k_codes_i8(w[2], w[3]), cur);
 #pragma unroll
     for (int gg = 0; gg < 4; ++gg) {
-      f4 acc = mfma(qa[2 * gg], k_codes_i8(w[4 * gg], w[4 * gg + 1]), (f4){0.f, 0.f, 0.f, 0.f});
-      acc = mfma(qa[2 * gg + 1], k_codes_i8(w[4 * gg + 2], w[4 * gg + 3]), acc);
+      f4 nxt;
+      if (gg < 3) {
+        nxt = mfma(qa[2 * gg + 2], k_codes_i8(w[4 * gg + 4], w[4 * gg + 5]), (f4){0.f, 0.f, 0.f, 0.f});
+        nxt = mfma(qa[2 * gg + 3], k_codes_i8(w[4 * gg + 6], w[4 * gg + 7]), nxt);
+      }
       const float d = scale_at(t.d, gg);
-      a0 = fmaf(d, acc[0], a0);
-      b0 = fmaf(d, acc[1], b0);
-      a1 = fmaf(d, acc[2], a1);
-      b1 = fmaf(d, acc[3], b1);
+      a0 = fmaf(d, cur[0], a0);
+      b0 = fmaf(d, cur[1], b0);
+      a1 = fmaf(d, cur[2], a1);
+      b1 = fmaf(d, cur[3], b1);
+      if (gg < 3) cur = nxt;
     }
   }
   // sum_j d_j * Q_j per head (hi, lo rows), for the code offsets
@@ -610,25 +622,26 @@ __global__ __launch_bounds__(256, 2) void decode_split(
           if (VK == kQ4) {
             const h8* e = dp + ((hf * 8 + i) * 4 + grp);
             const h8 dh16 = e[0], nh = e[64], dl16 = e[128], nl = e[192];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int nt = 2 * hf + u;
-              const u4 xm = v_magic_q4(vsh.c[nt][i >> 2][i & 3], vmask, vmagic);
-              oacc[nt] = mfma(pa, pk_fma8(xm, dh16, nh), oacc[nt]);
-              oacc[nt] = mfma(pa, pk_fma8(xm, dl16, nl), oacc[nt]);
-            }
+            const u4 x0 = v_magic_q4(vsh.c[2 * hf][i >> 2][i & 3], vmask, vmagic);
+            const u4 x1 = v_magic_q4(vsh.c[2 * hf + 1][i >> 2][i & 3], vmask, vmagic);
+            // the two column tiles' MFMAs alternate, so no MFMA waits on the one before it
+            oacc[2 * hf] = mfma(pa, pk_fma8(x0, dh16, nh), oacc[2 * hf]);
+            oacc[2 * hf + 1] = mfma(pa, pk_fma8(x1, dh16, nh), oacc[2 * hf + 1]);
+            oacc[2 * hf] = mfma(pa, pk_fma8(x0, dl16, nl), oacc[2 * hf]);
+            oacc[2 * hf + 1] = mfma(pa, pk_fma8(x1, dl16, nl), oacc[2 * hf + 1]);
           } else {
             const h8* e = dp + (i * 4 + grp);
             const h8 pa_ = e[0], na = e[32], pb_ = e[64], nb = e[96], pc_ = e[128], nc = e[160];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int nt = 2 * hf + u;
-              const u4 words = vsh.c[nt][i >> 1];
-              const u4 xm = v_magic_i8(words[2 * (i & 1)], words[2 * (i & 1) + 1], vmagic);
-              oacc[nt] = mfma(pa, pk_fma8(xm, pa_, na), oacc[nt]);
-              oacc[nt] = mfma(pa, pk_fma8(xm, pb_, nb), oacc[nt]);
-              oacc[nt] = mfma(pa, pk_fma8(xm, pc_, nc), oacc[nt]);
-            }
+            const u4 w0 = vsh.c[2 * hf][i >> 1], w1 = vsh.c[2 * hf + 1][i >> 1];
+            const u4 x0 = v_magic_i8(w0[2 * (i & 1)], w0[2 * (i & 1) + 1], vmagic);
+            const u4 x1 = v_magic_i8(w1[2 * (i & 1)], w1[2 * (i & 1) + 1], vmagic);
+            // the two column tiles' MFMAs alternate, so no MFMA waits on the one before it
+            oacc[2 * hf] = mfma(pa, pk_fma8(x0, pa_, na), oacc[2 * hf]);
+            oacc[2 * hf + 1] = mfma(pa, pk_fma8(x1, pa_, na), oacc[2 * hf + 1]);
+            oacc[2 * hf] = mfma(pa, pk_fma8(x0, pb_, nb), oacc[2 * hf]);
+            oacc[2 * hf + 1] = mfma(pa, pk_fma8(x1, pb_, nb), oacc[2 * hf + 1]);
+            oacc[2 * hf] = mfma(pa, pk_fma8(x0, pc_, nc), oacc[2 * hf]);
+            oacc[2 * hf + 1] = mfma(pa, pk_fma8(x1, pc_, nc), oacc[2 * hf + 1]);
           }
           __builtin_amdgcn_sched_barrier(0);  // keep each step's LDS operands short-lived
         }
