@@ -84,6 +84,21 @@ __device__ inline f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Page loads go through a buffer resource of the page's KV-head planes (uniform
+// base, 32-bit per-lane offsets), so every load is "scalar base + vector offset +
+// immediate" and no 64-bit lane address is kept; reads past the planes return 0.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kRsrcWord3 = 0x00020000;  // raw, untyped 32-bit-element buffer access
+__device__ inline Rsrc page_rsrc(const uint8_t* head, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(head), (short)0, bytes, kRsrcWord3);
+}
+__device__ inline u4 ld16(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline u2 ld8(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // A value kept in a VGPR, opaque to constant folding, so that (x & m) | v
 // becomes one v_and_or_b32 inside the hot loops.
 __device__ inline uint32_t vgpr_const(uint32_t c) {
@@ -150,22 +165,29 @@ struct KTile {
   u4 d;               // the token's scales (q4: 8 fp16; int8: 4 fp16 in d.xy, d.zw = 0)
 };
 
+// Byte offsets (from the head's K plane) of the lane's part of K tile t (loop
+// invariant): codes of token row 64w + 16t + col, slice grp; the token's scales.
 template <int KK>
-__device__ inline KTile load_ktile(const uint8_t* kpl, int row, int grp) {
+__device__ inline uint32_t ktile_code_off(int wave, int t, int col, int grp) {
+  return (uint32_t)((64 * wave + 16 * t + col) * code_row_bytes(KK) + (KK == kQ4 ? 32 : 64) * grp);
+}
+template <int KK>
+__device__ inline uint32_t ktile_scale_off(int wave, int t, int col) {
+  return (uint32_t)(kPageTokens * code_row_bytes(KK) + (64 * wave + 16 * t + col) * n_scales(KK) * 2);
+}
+
+template <int KK>
+__device__ inline KTile load_ktile(Rsrc r, uint32_t coff, uint32_t soff) {
   KTile t;
+  t.c0 = ld16(r, coff);
+  t.c1 = ld16(r, coff + 16);
   if (KK == kQ4) {
-    const u4* cp = reinterpret_cast<const u4*>(kpl + (uint32_t)(row * 128 + 32 * grp));
-    t.c0 = cp[0];
-    t.c1 = cp[1];
     t.c2 = t.c3 = (u4){0, 0, 0, 0};
-    t.d = *reinterpret_cast<const u4*>(kpl + (uint32_t)(256 * 128 + row * 16));
+    t.d = ld16(r, soff);
   } else {
-    const u4* cp = reinterpret_cast<const u4*>(kpl + (uint32_t)(row * 256 + 64 * grp));
-    t.c0 = cp[0];
-    t.c1 = cp[1];
-    t.c2 = cp[2];
-    t.c3 = cp[3];
-    const u2 dd = *reinterpret_cast<const u2*>(kpl + (uint32_t)(256 * 256 + row * 8));
+    t.c2 = ld16(r, coff + 32);
+    t.c3 = ld16(r, coff + 48);
+    const u2 dd = ld8(r, soff);
     t.d = (u4){dd[0], dd[1], 0, 0};
   }
   return t;
@@ -235,42 +257,44 @@ struct VShare {
   u2 s0, s1;                   // q4: 4 + 4 token scales; int8: s0, s1 = 8 consecutive scales
 };
 
-// Column tile nt of the wave's V share: the lane's 32 (q4) / 64 (int8) code bytes of head
-// element 64w + 16nt + col.
-template <int VK>
-__device__ inline void load_vcodes(VShare<VK>& v, const uint8_t* vpl, int wave, int lane, int nt) {
+// Byte offset (from the head's K plane) of column tile nt of the wave's V share:
+// the lane's 32 (q4) / 64 (int8) code bytes of head element 64w + 16nt + col.
+template <int KK, int VK>
+__device__ inline uint32_t vcode_off(int wave, int lane, int nt) {
   const int grp = lane >> 4, col = lane & 15;
-  const int e = 64 * wave + 16 * nt + col;
-  const u4* src = reinterpret_cast<const u4*>(vpl + (uint32_t)(e * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp));
+  return (uint32_t)(plane_bytes(KK) + (64 * wave + 16 * nt + col) * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
+}
+template <int VK>
+__device__ inline void load_vcodes(VShare<VK>& v, Rsrc r, uint32_t off, int nt) {
 #pragma unroll
-  for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = src[u];
+  for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = ld16(r, off + 16 * u);
 }
 
-// The scales the lane turns into B parts.
-template <int VK>
-__device__ inline void load_vscales(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
-  const uint32_t vs = kHeadDim * code_row_bytes(VK);  // byte offset of the scales
+// Byte offset (from the head's K plane) of the scales the lane turns into B parts.
+template <int KK, int VK>
+__device__ inline uint32_t vscale_off(int wave, int lane) {
+  const uint32_t vs = plane_bytes(KK) + kHeadDim * code_row_bytes(VK);  // V scales
   if (VK == kQ4) {
     // B-part entry (block 2w + bb, MFMA i, lane group gq): tokens t_lo..+3 and t_lo+16..+19
     const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
     const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
-    const uint32_t row = vs + (uint32_t)(((2 * wave + bb) * kPageTokens + t_lo) * 2);
-    v.s0 = *reinterpret_cast<const u2*>(vpl + row);
-    v.s1 = *reinterpret_cast<const u2*>(vpl + row + 32);
+    return vs + (uint32_t)(((2 * wave + bb) * kPageTokens + t_lo) * 2);
   } else {
     // entry (MFMA i, lane group gq) = tokens 64gq + 8i .. +7 of group w (lanes 0..31)
     const int i = (lane >> 2) & 7, gq = lane & 3;
-    const u4 d = *reinterpret_cast<const u4*>(vpl + vs + (uint32_t)((wave * kPageTokens + 64 * gq + 8 * i) * 2));
+    return vs + (uint32_t)((wave * kPageTokens + 64 * gq + 8 * i) * 2);
+  }
+}
+template <int VK>
+__device__ inline void load_vscales(VShare<VK>& v, Rsrc r, uint32_t off) {
+  if (VK == kQ4) {
+    v.s0 = ld8(r, off);
+    v.s1 = ld8(r, off + 32);
+  } else {
+    const u4 d = ld16(r, off);
     v.s0 = (u2){d[0], d[1]};
     v.s1 = (u2){d[2], d[3]};
   }
-}
-
-template <int VK>
-__device__ inline void load_vshare(VShare<VK>& v, const uint8_t* vpl, int wave, int lane) {
-#pragma unroll
-  for (int nt = 0; nt < 4; ++nt) load_vcodes<VK>(v, vpl, wave, lane, nt);
-  load_vscales<VK>(v, vpl, wave, lane);
 }
 
 // Eight q4 codes of one dword (byte w: low nibble token t+w, high nibble token
@@ -361,11 +385,23 @@ __global__ __launch_bounds__(256, 2) void decode_split(
   const uint8_t* base = phys_first < 0 || phys_first >= n_pool_pages
                             ? nullptr
                             : pool + (int64_t)phys_first * page_bytes + (int64_t)g * head_bytes;
-  {
-    const uint8_t* src = base ? base : pool;  // a bad page is read from page 0 and then ignored
+  // loop-invariant lane offsets of every load of a page
+  uint32_t koff[4], ksoff[4], voff[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(src, 64 * wave + 16 * t + col, grp);
-    load_vshare<VK>(vsh, src + plane_bytes(KK), wave, lane);
+  for (int t = 0; t < 4; ++t) {
+    koff[t] = ktile_code_off<KK>(wave, t, col, grp);
+    ksoff[t] = ktile_scale_off<KK>(wave, t, col);
+    voff[t] = vcode_off<KK, VK>(wave, lane, t);
+  }
+  const uint32_t vsoff = vscale_off<KK, VK>(wave, lane);
+  {
+    // a bad page is read from page 0 and then ignored
+    const Rsrc r = page_rsrc(base ? base : pool, (int)head_bytes);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(r, koff[t], ksoff[t]);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) load_vcodes<VK>(vsh, r, voff[nt], nt);
+    load_vscales<VK>(vsh, r, vsoff);
   }
 
   // (all eight head slots are transformed, unused ones hold zeros, so that each step's
@@ -469,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     // Next page's loads are issued without a branch (the last page re-reads a
     // valid page) so that the wait counters before each use stay exact, and each
     // part is issued as soon as its registers are consumed, to overlap the math.
-    const uint8_t* nsrc = next ? next : (base ? base : pool);
+    const Rsrc nr = page_rsrc(next ? next : (base ? base : pool), (int)head_bytes);
 
     // ---------------- Q.K of the wave's 64 tokens, wave maximum per head
     float xs[4][2];
@@ -484,7 +520,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       xs[t][1] = ok ? s1 * scale_log2 : -INFINITY;
       mx0 = fmaxf(mx0, xs[t][0]);
       mx1 = fmaxf(mx1, xs[t][1]);
-      kt[t] = load_ktile<KK>(nsrc, 64 * wave + 16 * t + col, grp);  // next page's tile t
+      kt[t] = load_ktile<KK>(nr, koff[t], ksoff[t]);  // next page's tile t
       __builtin_amdgcn_sched_barrier(0);
     }
     mx0 = half_max(mx0);
@@ -551,7 +587,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
         fast = !__any(!(amax_bits < kI8FastBits));
       }
     }
-    load_vscales<VK>(vsh, nsrc + plane_bytes(KK), wave, lane);  // next page's scales
+    load_vscales<VK>(vsh, nr, vsoff);  // next page's scales
     __syncthreads();  // (A) wave maxima visible
 
     // ---------------- online softmax: page maximum over the four waves, p of the wave's tokens
@@ -680,8 +716,8 @@ __global__ __launch_bounds__(256, 2) void decode_split(
         }
       }
       // this half's code registers now take the next page's codes
-      load_vcodes<VK>(vsh, nsrc + plane_bytes(KK), wave, lane, 2 * hf);
-      load_vcodes<VK>(vsh, nsrc + plane_bytes(KK), wave, lane, 2 * hf + 1);
+      load_vcodes<VK>(vsh, nr, voff[2 * hf], 2 * hf);
+      load_vcodes<VK>(vsh, nr, voff[2 * hf + 1], 2 * hf + 1);
     }
     base = next;
   }
