@@ -34,6 +34,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -235,6 +237,137 @@ def cpu_baseline(args, wl, dev, state):
                 host_cpus=len(os.sched_getaffinity(0)))
 
 
+C5 = dict(fmt="int8", layers=16, host_tokens=1048576, slots=128, n_sel=8, miss=0.3, cfg=5)
+
+
+def streaming_selection(rng, table, n_pages, n_sel, miss):
+    """n_sel distinct logical pages: each a miss (a page not resident) with probability
+    `miss`, else a hit (a resident page); from non-resident pages when nothing is resident."""
+    resident = [int(p) for p in table.slot_page if p >= 0]
+    res = list(rng.permutation(resident))
+    res_set = set(resident)
+    picked = []
+    for _ in range(n_sel):
+        if res and rng.random() >= miss:
+            picked.append(res.pop())
+            continue
+        while True:
+            p = int(rng.integers(n_pages))
+            if p not in res_set and p not in picked:
+                break
+        picked.append(p)
+    return np.array(picked, np.int32)
+
+
+def run_streaming(args, dev):
+    """C5: KV kept in pinned host memory, 128 device slots per layer; each step, per layer,
+    8 selected pages go through the CLOCK table and the zero-copy gather, then attention."""
+    import torch
+
+    import kvsynth
+    import offloaded_kv_cache_amd as K
+
+    c = dict(C5)
+    c["host_tokens"] = args.host_tokens
+    fmt, L, cfg = c["fmt"], c["layers"], c["cfg"]
+    n_pages = c["host_tokens"] // PAGE
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    layer_bytes = n_pages * pb
+    log(f"pinning {L * layer_bytes / 1e9:.1f} GB of host memory")
+    host = torch.empty(L * layer_bytes, dtype=torch.uint8, pin_memory=True)
+    staging = K.paged.PagedPool(fmt, n_pages, device=dev)
+    ident = torch.arange(n_pages, dtype=torch.int32, device=dev)
+    for layer in range(L):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(kvsynth.torch_seed(cfg, layer))
+        gain = kvsynth.gain_torch(cfg, layer, 4, dev)
+        for t0 in range(0, c["host_tokens"], 2048):
+            k, v = kvsynth.kv_tokens_torch(gen, 2048, gain, dev)
+            staging.append(k, v, t0, ident)
+        host[layer * layer_bytes:(layer + 1) * layer_bytes].copy_(staging.data)
+        torch.cuda.synchronize()
+    del staging
+    log(f"host pool written: {L} layers x {n_pages} pages")
+    slots = [torch.zeros(c["slots"] * pb, dtype=torch.uint8, device=dev) for _ in range(L)]
+    tables = [K.Residency(c["slots"], n_pages) for _ in range(L)]
+    bts = [torch.empty(c["n_sel"], dtype=torch.int32, device=dev) for _ in range(L)]
+    ctx_tok = c["n_sel"] * PAGE
+    ctx = torch.tensor([ctx_tok], dtype=torch.int32, device=dev)
+    ws = K.paged.DecodeWorkspace(s, 1, ctx_tok, 0, device=dev)
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(1000 * cfg)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(kvsynth.torch_seed(cfg, 99))
+    n_steps = args.warmup + args.steps
+    q_all = torch.randn((n_steps, L, 1, 24, 256), generator=gen, device=dev).to(torch.float16)
+    stream = torch.cuda.current_stream()
+    # fill every layer's slots with distinct pages (all misses)
+    for layer in range(L):
+        fill = rng.permutation(n_pages)[:c["slots"]].astype(np.int32)
+        for i in range(0, c["slots"], c["n_sel"]):
+            K.gather_pages(s, tables[layer], fill[i:i + c["n_sel"]], host[layer * layer_bytes:(layer + 1) * layer_bytes],
+                           slots[layer], bts[layer], stream=stream)
+    torch.cuda.synchronize()
+    gather_ev = []
+    misses = 0
+
+    def step(st, timing):
+        nonlocal misses
+        for layer in range(L):
+            sel = streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+            if timing:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            m = K.gather_pages(s, tables[layer], sel, host[layer * layer_bytes:(layer + 1) * layer_bytes],
+                               slots[layer], bts[layer], stream=stream)
+            if timing:
+                e1.record(stream)
+                gather_ev.append((e0, e1, m))
+                misses += m
+            K.decode_attention(s, q_all[st, layer], slots[layer], bts[layer][None], ctx, ctx_tok, out, ws.data,
+                               stream=stream)
+
+    for st in range(args.warmup):
+        step(st, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.warmup, n_steps):
+        step(st, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"decode status word {ws.status()}")
+    g_ms = sum(a.elapsed_time(b) for a, b, _ in gather_ev)
+    copied = sum(m for _, _, m in gather_ev) * pb
+    # pinned host -> device peak on this box: one large plain copy
+    big = host[:min(host.numel(), 1 << 30)]
+    dst = torch.empty(big.numel(), dtype=torch.uint8, device=dev)
+    dst.copy_(big, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(big, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    h2d = 3 * big.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    kv_bytes = args.steps * L * ctx_tok * kv_bytes_per_token(fmt)
+    return dict(value=kv_bytes / wall / 1e9, ms_per_step=wall / args.steps * 1e3,
+                gather={"pcie_GBs": round(copied / (g_ms * 1e-3) / 1e9, 2) if g_ms > 0 else None,
+                        "h2d_pinned_peak_GBs": round(h2d, 2),
+                        "miss_rate": round(misses / (args.steps * L * c["n_sel"]), 4),
+                        "pages_copied": int(misses), "bytes_copied": int(copied),
+                        "gather_ms_per_step": round(g_ms / args.steps, 4)},
+                config={"workload": f"16 layers, {c['host_tokens']:,}-token int8 KV in pinned host memory, "
+                                    f"{c['slots']} device slots per layer, {c['n_sel']} selected pages per layer "
+                                    f"per step (~{int(c['miss'] * 100)}% misses), CLOCK residency + zero-copy gather "
+                                    f"+ attention over the {ctx_tok:,} selected tokens",
+                        "layers": L, "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256, "page_tokens": 256,
+                        "batch": 1, "kv_format": fmt, "host_tokens": c["host_tokens"], "slots_per_layer": c["slots"],
+                        "selected_pages": c["n_sel"], "miss_probability": c["miss"]})
+
+
 def counter_traffic(workload: str):
     """HBM bytes per decode_split launch from the committed counter summary, or None.
 
@@ -280,7 +413,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["c5"])
+    ap.add_argument("--host-tokens", type=int, default=C5["host_tokens"],
+                    help="c5: tokens per layer in the pinned host pool (multiple of 2048)")
     ap.add_argument("--pages-per-split", type=int, default=0)
     ap.add_argument("--event-every", type=int, default=4, metavar="N",
                     help="record the split kernel's start/stop events on every N-th layer of each "
@@ -304,6 +439,15 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(args, dev)
+        return
+    if args.workload == "c5":
+        res = run_streaming(args, dev)
+        print(json.dumps({
+            "metric": "KV GB/s streamed in decode attention (% of 8 TB/s HBM) at 128K q4_0",
+            "value": round(res["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8 KV, fp32 accumulate", "data": "synthetic",
+            "config": res["config"], "gather": res["gather"], "cpu_baseline": None}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     res, state = run_resident(args, wl, dev)
