@@ -62,14 +62,14 @@ int check_shape(const kv_shape* s) {
 
 int64_t page_bytes_of(const kv_shape* s) { return (int64_t)s->n_kv_heads * head_stride(s->format); }
 
-// Pages per split chosen so that the grid has about two workgroups per compute
-// unit (256 CUs) for the given batch, with every wave of a workgroup busy.
+// Pages per split chosen so that the grid fills the 256 compute units once for the
+// given batch: two 4-wave workgroups per CU, or one 8-wave workgroup (int8 K).
 int32_t auto_pages_per_split(const kv_shape* s, int32_t batch, int64_t max_pages_ctx) {
-  const int64_t target = 512;
+  const int64_t target = 256 * (8 / split_waves(k_kind(s->format)));
   int64_t per_seq_head = target / ((int64_t)batch * s->n_kv_heads);
   if (per_seq_head < 1) per_seq_head = 1;
   int64_t pps = (max_pages_ctx + per_seq_head - 1) / per_seq_head;
-  if (pps < 4) pps = 4;
+  if (pps < 1) pps = 1;
   return (int32_t)pps;
 }
 

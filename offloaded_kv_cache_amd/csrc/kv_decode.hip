@@ -74,7 +74,6 @@ constexpr float kTwo24 = 16777216.0f;
 constexpr uint32_t kQ4FastBits = 0x6300;  // fp16 896: |d| below this, -72 * d_hi is exact and finite
 constexpr uint32_t kQ4FastMinM1 = 0x13FF;  // fp16 2^-10 minus one: |d| from here up, d_lo / 16 is exact
 constexpr uint32_t kI8FastBits = 0x5300;  // fp16 56: |d| below this, -1152 * d_part is exact and finite
-constexpr int kWaves = 4;
 constexpr int kQsStride = kHeadDim + 4;  // padded rows of the query in LDS (bank spread)
 
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
@@ -167,13 +166,14 @@ struct KTile {
 
 // Byte offsets (from the head's K plane) of the lane's part of K tile t (loop
 // invariant): codes of token row 64w + 16t + col, slice grp; the token's scales.
+// A wave owns tpw = 256 / (waves per workgroup) tokens of a page for Q.K.
 template <int KK>
-__device__ inline uint32_t ktile_code_off(int wave, int t, int col, int grp) {
-  return (uint32_t)((64 * wave + 16 * t + col) * code_row_bytes(KK) + (KK == kQ4 ? 32 : 64) * grp);
+__device__ inline uint32_t ktile_code_off(int tpw, int wave, int t, int col, int grp) {
+  return (uint32_t)((tpw * wave + 16 * t + col) * code_row_bytes(KK) + (KK == kQ4 ? 32 : 64) * grp);
 }
 template <int KK>
-__device__ inline uint32_t ktile_scale_off(int wave, int t, int col) {
-  return (uint32_t)(kPageTokens * code_row_bytes(KK) + (64 * wave + 16 * t + col) * n_scales(KK) * 2);
+__device__ inline uint32_t ktile_scale_off(int tpw, int wave, int t, int col) {
+  return (uint32_t)(kPageTokens * code_row_bytes(KK) + (tpw * wave + 16 * t + col) * n_scales(KK) * 2);
 }
 
 template <int KK>
@@ -258,11 +258,12 @@ struct VShare {
 };
 
 // Byte offset (from the head's K plane) of column tile nt of the wave's V share:
-// the lane's 32 (q4) / 64 (int8) code bytes of head element 64w + 16nt + col.
+// the lane's 32 (q4) / 64 (int8) code bytes of head element epw * w + 16nt + col
+// (a wave owns epw = 256 / (waves per workgroup) head elements for P.V).
 template <int KK, int VK>
-__device__ inline uint32_t vcode_off(int wave, int lane, int nt) {
+__device__ inline uint32_t vcode_off(int epw, int wave, int lane, int nt) {
   const int grp = lane >> 4, col = lane & 15;
-  return (uint32_t)(plane_bytes(KK) + (64 * wave + 16 * nt + col) * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
+  return (uint32_t)(plane_bytes(KK) + (epw * wave + 16 * nt + col) * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
 }
 template <int VK>
 __device__ inline void load_vcodes(VShare<VK>& v, Rsrc r, uint32_t off, int nt) {
@@ -272,17 +273,18 @@ __device__ inline void load_vcodes(VShare<VK>& v, Rsrc r, uint32_t off, int nt) 
 
 // Byte offset (from the head's K plane) of the scales the lane turns into B parts.
 template <int KK, int VK>
-__device__ inline uint32_t vscale_off(int wave, int lane) {
+__device__ inline uint32_t vscale_off(int epw, int wave, int lane) {
   const uint32_t vs = plane_bytes(KK) + kHeadDim * code_row_bytes(VK);  // V scales
   if (VK == kQ4) {
-    // B-part entry (block 2w + bb, MFMA i, lane group gq): tokens t_lo..+3 and t_lo+16..+19
-    const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
+    // B-part entry (block of the wave bb, MFMA i, lane group gq): tokens t_lo..+3 and
+    // t_lo+16..+19; lanes past the wave's blocks read its first block again
+    const int nb = epw / 32, bb = (lane >> 5) < nb ? (lane >> 5) : 0, i = (lane >> 2) & 7, gq = lane & 3;
     const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
-    return vs + (uint32_t)(((2 * wave + bb) * kPageTokens + t_lo) * 2);
+    return vs + (uint32_t)(((nb * wave + bb) * kPageTokens + t_lo) * 2);
   } else {
-    // entry (MFMA i, lane group gq) = tokens 64gq + 8i .. +7 of group w (lanes 0..31)
+    // entry (MFMA i, lane group gq) = tokens 64gq + 8i .. +7 of the wave's 64-element group
     const int i = (lane >> 2) & 7, gq = lane & 3;
-    return vs + (uint32_t)((wave * kPageTokens + 64 * gq + 8 * i) * 2);
+    return vs + (uint32_t)(((epw * wave / 64) * kPageTokens + 64 * gq + 8 * i) * 2);
   }
 }
 template <int VK>
@@ -322,25 +324,32 @@ __device__ inline h8 pk_fma8(u4 x, h8 m, h8 a) {
 //           consecutive 16 B: q4 [4 parts][block 2][i 8][lane group 4], int8 [6 parts][i 8]
 //           [lane group 4], each an h8 in B slot order
 //   wmax:   each wave's maximum score per head;  lsum: each wave's probability sums
+template <int NW>
 struct SplitLds {
   h8 afrag[8][64];
-  h8 dpart[kWaves][64 * 6];
-  float wmax[kWaves][kMaxGroup];
-  float lsum[kWaves][kMaxGroup];
+  h8 dpart[NW][256];
+  float wmax[NW][kMaxGroup];
+  float lsum[NW][kMaxGroup];
   float qs[kMaxGroup][kQsStride];
   float bsum[kMaxGroup][8];
 };
 
-template <int KK, int VK>
-__global__ __launch_bounds__(256, 2) void decode_split(
+// NW waves per workgroup (4: two workgroups per CU; 8: one, with half the per-wave
+// registers, for the larger int8 K tiles).
+template <int KK, int VK, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t n_pool_pages,
     const int32_t* __restrict__ block_tables, int max_pages, const int32_t* __restrict__ context_lens,
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t* __restrict__ status) {
-  __shared__ __attribute__((aligned(16))) SplitLds lds;
+  __shared__ __attribute__((aligned(16))) SplitLds<NW> lds;
+  constexpr int TPW = kPageTokens / NW, KT = TPW / 16;  // Q.K: tokens and tiles per wave
+  constexpr int EPW = kHeadDim / NW, NTW = EPW / 16;    // P.V: elements and column tiles per wave
+  constexpr int HFN = NTW / 2;                           // P.V halves of two column tiles
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int elem = tid & (kHeadDim - 1);  // the query element of the thread (prologue)
   const int grp = lane >> 4, col = lane & 15;  // MFMA lane group and column
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = n_q_heads / n_kv_heads;
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
 #pragma unroll
   for (int hh = 0; hh < kMaxGroup; ++hh) {
     const int hc = min(hh, G - 1);
-    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + tid]);
+    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + elem]);
     qv[hh] = hh < G ? x : 0.f;
   }
   const int p_begin = split * pages_per_split;
@@ -378,29 +387,30 @@ __global__ __launch_bounds__(256, 2) void decode_split(
   };
 
   __builtin_amdgcn_sched_barrier(0);
-  // then the first page's share: 4 K tiles (tokens 64w..64w+63) and the V share, issued
+  // then the first page's share: KT K tiles (tokens TPW w ..) and the V share, issued
   // after the query so that the wait for the query does not also wait for the page
-  KTile kt[4];
+  KTile kt[KT];
   VShare<VK> vsh;
   const uint8_t* base = phys_first < 0 || phys_first >= n_pool_pages
                             ? nullptr
                             : pool + (int64_t)phys_first * page_bytes + (int64_t)g * head_bytes;
   // loop-invariant lane offsets of every load of a page
-  uint32_t koff[4], ksoff[4], voff[4];
+  uint32_t koff[KT], ksoff[KT], voff[NTW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    koff[t] = ktile_code_off<KK>(wave, t, col, grp);
-    ksoff[t] = ktile_scale_off<KK>(wave, t, col);
-    voff[t] = vcode_off<KK, VK>(wave, lane, t);
+  for (int t = 0; t < KT; ++t) {
+    koff[t] = ktile_code_off<KK>(TPW, wave, t, col, grp);
+    ksoff[t] = ktile_scale_off<KK>(TPW, wave, t, col);
   }
-  const uint32_t vsoff = vscale_off<KK, VK>(wave, lane);
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) voff[t] = vcode_off<KK, VK>(EPW, wave, lane, t);
+  const uint32_t vsoff = vscale_off<KK, VK>(EPW, wave, lane);
   {
     // a bad page is read from page 0 and then ignored
     const Rsrc r = page_rsrc(base ? base : pool, (int)head_bytes);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kt[t] = load_ktile<KK>(r, koff[t], ksoff[t]);
+    for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r, koff[t], ksoff[t]);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) load_vcodes<VK>(vsh, r, voff[nt], nt);
+    for (int nt = 0; nt < NTW; ++nt) load_vcodes<VK>(vsh, r, voff[nt], nt);
     load_vscales<VK>(vsh, r, vsoff);
   }
 
@@ -416,10 +426,12 @@ __global__ __launch_bounds__(256, 2) void decode_split(
 #pragma unroll
       for (int hh = 0; hh < kMaxGroup; ++hh) qv[hh] = (lane & m) ? (o[hh] - qv[hh]) : (qv[hh] + o[hh]);
     }
+    if (tid < kHeadDim) {
 #pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+      for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+    }
     __syncthreads();
-    const int e0 = tid & 63, k = tid >> 6;  // bits 6 and 7: a 4-point transform across waves
+    const int e0 = tid & 63, k = (tid >> 6) & 3;  // bits 6 and 7: a 4-point transform across waves
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh) {
       const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
@@ -429,8 +441,10 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     }
     __syncthreads();
   }
+  if (tid < kHeadDim) {
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
+  }
   __syncthreads();
   {
     // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8)
@@ -491,9 +505,9 @@ __global__ __launch_bounds__(256, 2) void decode_split(
   // per-lane running state for the two heads of its row group (rows 4grp..4grp+3)
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-  f4 oacc[4];
+  f4 oacc[NTW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NTW; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
 
   for (int pg = p_begin; pg < p_end; ++pg) {
@@ -507,12 +521,12 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     // part is issued as soon as its registers are consumed, to overlap the math.
     const Rsrc nr = page_rsrc(next ? next : (base ? base : pool), (int)head_bytes);
 
-    // ---------------- Q.K of the wave's 64 tokens, wave maximum per head
-    float xs[4][2];
+    // ---------------- Q.K of the wave's TPW tokens, wave maximum per head
+    float xs[KT][2];
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int row = 64 * wave + 16 * t + col;
+    for (int t = 0; t < KT; ++t) {
+      const int row = TPW * wave + 16 * t + col;
       float s0, s1;
       qk_tile<KK>(kt[t], qa, qc, s0, s1);
       const bool ok = row < valid;
@@ -537,8 +551,10 @@ __global__ __launch_bounds__(256, 2) void decode_split(
       if (VK == kQ4) {
         const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
         const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
-        // slot u = scale of token t_lo + (u & 3) + 16 (u >> 2): half (u & 1) of word u >> 1
+        // slot u = scale of token t_lo + (u & 3) + 16 (u >> 2): half (u & 1) of word u >> 1;
+        // lanes past the wave's blocks (one block per wave at 8 waves) hold zeros
         u4 wv = {vsh.s0[0], vsh.s0[1], vsh.s1[0], vsh.s1[1]};
+        if (bb >= EPW / 32) wv = (u4){0u, 0u, 0u, 0u};
         if (valid < kPageTokens) {  // a partial page: scales of rows past the context are 0
 #pragma unroll
           for (int u = 0; u < 8; ++u)
@@ -593,7 +609,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     // ---------------- online softmax: page maximum over the four waves, p of the wave's tokens
     float pm0 = lds.wmax[0][h0], pm1 = lds.wmax[0][h1];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 1; w < NW; ++w) {
       pm0 = fmaxf(pm0, lds.wmax[w][h0]);
       pm1 = fmaxf(pm1, lds.wmax[w][h1]);
     }
@@ -609,21 +625,24 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     float sum0 = 0.f, sum1 = 0.f;
     _Float16* af = reinterpret_cast<_Float16*>(&lds.afrag[0][0]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < KT; ++t) {
       const float p0 = __builtin_amdgcn_exp2f(xs[t][0] - r0);  // masked tokens: 2^(-inf) = 0
       const float p1 = __builtin_amdgcn_exp2f(xs[t][1] - r1);
       sum0 += p0;
       sum1 += p1;
-      // fragment position of token 64w + 16t + col for P.V MFMA i, lane (w, 2h + part), slot
+      // fragment position of token TPW w + 16t + col for P.V MFMA i, lane (k-group kg,
+      // row 2h + part), slot: k-group kg holds tokens 64kg..64kg+63, in the order in
+      // which a lane's V code bytes come (q4: 4 + 4 nibble tokens, int8: 8 bytes)
+      const int token = TPW * wave + 16 * t + col, kg = token >> 6, o = token & 63;
       int i, slot;
       if (VK == kQ4) {
-        i = 4 * (t >> 1) + (col >> 2);
-        slot = 4 * (t & 1) + (col & 3);
+        i = 4 * (o >> 5) + ((o & 15) >> 2);
+        slot = 4 * ((o >> 4) & 1) + (o & 3);
       } else {
-        i = 2 * t + (col >> 3);
-        slot = col & 7;
+        i = o >> 3;
+        slot = o & 7;
       }
-      const int base_idx = (i * 64 + 16 * wave) * 8 + slot;
+      const int base_idx = (i * 64 + 16 * kg) * 8 + slot;
       const float ps0 = p0 * kPScale, ps1 = p1 * kPScale;
       const _Float16 hi0 = (_Float16)ps0, hi1 = (_Float16)ps1;
       const _Float16 lo0 = (_Float16)(ps0 - (float)hi0), lo1 = (_Float16)(ps1 - (float)hi1);
@@ -637,7 +656,7 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     l_run[0] = l_run[0] * al0 + sum0;
     l_run[1] = l_run[1] * al1 + sum1;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NTW; ++t) {
       oacc[t][0] *= al0;
       oacc[t][1] *= al0;
       oacc[t][2] *= al1;
@@ -645,12 +664,11 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     }
     __syncthreads();  // (B) probabilities of all 256 tokens visible
 
-    // ---------------- P.V for the wave's 64 head elements (4 column tiles), in two halves
-    // of two column tiles (one q4 block each); after a half, its code registers take the
-    // next page's codes.
+    // ---------------- P.V for the wave's EPW head elements, in halves of two column tiles
+    // (one q4 block each); after a half, its code registers take the next page's codes.
     const h8* dp = lds.dpart[wave];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < HFN; ++hf) {
       if (fast) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -736,11 +754,14 @@ __global__ __launch_bounds__(256, 2) void decode_split(
     if (hh < G) {
       const size_t idx = ((size_t)b * n_q_heads + g * G + hh) * S + split;
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        part_o[idx * kHeadDim + 64 * wave + 16 * t + col] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
+      for (int t = 0; t < NTW; ++t)
+        part_o[idx * kHeadDim + EPW * wave + 16 * t + col] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
       if (wave == 0 && col == 0) {
+        float l = lds.lsum[0][hh];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) l += lds.lsum[w][hh];
         part_ml[2 * idx] = m_run[r];
-        part_ml[2 * idx + 1] = lds.lsum[0][hh] + lds.lsum[1][hh] + lds.lsum[2][hh] + lds.lsum[3][hh];
+        part_ml[2 * idx + 1] = l;
       }
     }
   }
@@ -855,8 +876,9 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
 
 template <int KK, int VK>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
-  dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch), block(256);
-  hipExtLaunchKernelGGL((decode_split<KK, VK>), grid, block, 0, stream, start, stop, 0, a.q, a.pool,
+  constexpr int NW = split_waves(KK);
+  dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch), block(64 * NW);
+  hipExtLaunchKernelGGL((decode_split<KK, VK, NW>), grid, block, 0, stream, start, stop, 0, a.q, a.pool,
                         a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens, a.max_context,
                         a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits, a.scale_log2,
                         a.part_ml, a.part_o, a.status);

@@ -25,6 +25,10 @@ __host__ __device__ constexpr int plane_bytes(int kind) {
 }
 __host__ __device__ constexpr int k_kind(int fmt) { return fmt == KV_FMT_Q4_0 ? kQ4 : kInt8; }
 __host__ __device__ constexpr int v_kind(int fmt) { return fmt == KV_FMT_INT8 ? kInt8 : kQ4; }
+// Waves per workgroup of the split-K decode kernel: 4 (two workgroups per CU) for
+// 4-bit K; 8 (one workgroup per CU, half the registers per wave) for int8 K, whose
+// tiles are twice as large.
+__host__ __device__ constexpr int split_waves(int k_kind_) { return k_kind_ == kQ4 ? 4 : 8; }
 __host__ __device__ constexpr int64_t head_stride(int fmt) {
   return plane_bytes(k_kind(fmt)) + plane_bytes(v_kind(fmt));
 }
