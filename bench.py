@@ -114,6 +114,9 @@ def run_resident(args, wl, dev):
 
     fmt, L, lens, cfg = wl["fmt"], wl["layers"], wl["lens"], wl["cfg"]
     B = len(lens)
+    if B > 1 and args.pages_per_split == 0:
+        # lengths differ: size the splits by the batch's total, not B x the longest
+        args.pages_per_split = K.decode_split_pages(K.shape(fmt), B, max(lens), sum(lens))
     s, pools, tables, start_lens, max_pages, append_ev = build_resident(args, wl, dev)
     torch.cuda.synchronize()
     app_ms = [a.elapsed_time(b) for a, b in append_ev]

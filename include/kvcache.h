@@ -183,6 +183,17 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
                         int32_t pages_per_split, void* stream);
 
 /*
+ * The pages per split that pages_per_split = 0 selects, for `batch` sequences of at
+ * most `max_context` tokens whose lengths add up to `total_context` (0: assume every
+ * sequence at max_context). The split count is chosen so that the grid about fills
+ * the GPU once; for a batch of very unequal lengths, passing its total here and the
+ * result as pages_per_split keeps the GPU full where the default would not.
+ * Returns >= 1, or 0 (kv_last_error) for an invalid shape or size.
+ */
+int32_t kv_decode_split_pages(const kv_shape* shape, int32_t batch, int64_t max_context,
+                              int64_t total_context);
+
+/*
  * The two phases of kv_decode_attention, for callers that schedule them
  * separately (e.g. to time or overlap them). Same arguments and checks as
  * kv_decode_attention; kv_decode_split enqueues only the split-K kernel

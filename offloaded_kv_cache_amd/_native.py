@@ -23,7 +23,8 @@ FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4}
 
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
-    "kv_decode_workspace_bytes", "kv_decode_attention", "kv_decode_split", "kv_decode_split_timed",
+    "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
+    "kv_decode_split_timed",
     "kv_decode_combine",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
@@ -59,6 +60,7 @@ def _load():
         "kv_page_bytes": (I64, [C.POINTER(KVShape)]),
         "kv_append_quantize": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, P, I32, P, I64, P, P]),
         "kv_decode_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I64, I32]),
+        "kv_decode_split_pages": (I32, [C.POINTER(KVShape), I32, I64, I64]),
         "kv_decode_attention": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                           P, P, SZ, I32, P]),
         "kv_decode_split": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
@@ -158,6 +160,14 @@ def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=
 def decode_workspace_bytes(s: KVShape, batch: int, max_context: int, pages_per_split: int = 0) -> int:
     r = lib.kv_decode_workspace_bytes(C.byref(s), batch, max_context, pages_per_split)
     if r == 0:
+        raise KVError(KV_EINVAL, last_error())
+    return int(r)
+
+
+def decode_split_pages(s: KVShape, batch: int, max_context: int, total_context: int = 0) -> int:
+    """Pages per split the library selects (for a batch whose lengths add up to total_context)."""
+    r = lib.kv_decode_split_pages(C.byref(s), batch, max_context, total_context)
+    if r <= 0:
         raise KVError(KV_EINVAL, last_error())
     return int(r)
 

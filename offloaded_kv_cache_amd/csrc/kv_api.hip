@@ -62,15 +62,22 @@ int check_shape(const kv_shape* s) {
 
 int64_t page_bytes_of(const kv_shape* s) { return (int64_t)s->n_kv_heads * head_stride(s->format); }
 
-// Pages per split chosen so that the grid fills the 256 compute units once for the
-// given batch: two 4-wave workgroups per CU, or one 8-wave workgroup (int8 K).
-int32_t auto_pages_per_split(const kv_shape* s, int32_t batch, int64_t max_pages_ctx) {
+// Pages per split chosen so that the grid fills the 256 compute units once: two
+// 4-wave workgroups per CU, or one 8-wave workgroup (int8 K), over all the
+// (sequence, KV head, split) items of `total_pages` pages. Each sequence's last
+// split may be partial, so the other batch - 1 sequences keep one workgroup per KV
+// head in reserve (a second, nearly empty round of workgroups would double the time).
+int32_t pages_per_split_for(const kv_shape* s, int32_t batch, int64_t total_pages) {
   const int64_t target = 256 * (8 / split_waves(k_kind(s->format)));
-  int64_t per_seq_head = target / ((int64_t)batch * s->n_kv_heads);
-  if (per_seq_head < 1) per_seq_head = 1;
-  int64_t pps = (max_pages_ctx + per_seq_head - 1) / per_seq_head;
+  int64_t room = target - (int64_t)(batch - 1) * s->n_kv_heads;
+  if (room < s->n_kv_heads) room = s->n_kv_heads;
+  int64_t pps = (total_pages * s->n_kv_heads + room - 1) / room;
   if (pps < 1) pps = 1;
+  if (pps > 0x7FFFFFFF) pps = 0x7FFFFFFF;
   return (int32_t)pps;
+}
+int32_t auto_pages_per_split(const kv_shape* s, int32_t batch, int64_t max_pages_ctx) {
+  return pages_per_split_for(s, batch, (int64_t)batch * max_pages_ctx);
 }
 
 struct WsLayout {
@@ -161,6 +168,21 @@ size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch, int64_t m
   const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, batch, max_pages_ctx);
   ok();
   return workspace_layout(shape, batch, max_context, pps).total;
+}
+
+int32_t kv_decode_split_pages(const kv_shape* shape, int32_t batch, int64_t max_context,
+                              int64_t total_context) {
+  if (check_shape(shape)) return 0;
+  if (batch < 1 || batch > 65535 || max_context < 0 || max_context > 0x7FFFFFFF || total_context < 0 ||
+      total_context > (int64_t)batch * max_context) {
+    fail(KV_EINVAL, "bad batch, max_context or total_context");
+    return 0;
+  }
+  const int64_t total = total_context > 0 ? total_context : (int64_t)batch * max_context;
+  ok();
+  // pages of the batch: the total rounded up per sequence is at most batch - 1 pages more
+  const int64_t pages = (total + kPageTokens - 1) / kPageTokens + (total_context > 0 ? batch - 1 : 0);
+  return pages_per_split_for(shape, batch, pages);
 }
 
 }  // extern "C"

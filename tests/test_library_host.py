@@ -158,3 +158,20 @@ def test_workspace_grows_with_context_and_split():
     assert a < b < c
     # status word + per-split (m, l) + 256 outputs, for 24 heads
     assert b >= 256 + 24 * 128 * (2 + 256) * 4
+
+
+def test_split_pages_fill_the_gpu_once():
+    q4, k8 = K.shape("q4_0"), K.shape("k8v4")
+    # 128K tokens, one sequence, 4-bit K: 512 workgroups of 4 waves -> 4 pages each
+    assert K.decode_split_pages(q4, 1, 131072) == 4
+    # int8 K runs 8-wave workgroups, one per CU: twice the pages per split
+    assert K.decode_split_pages(k8, 1, 131072) == 8
+    # four sequences of unequal length: sized by their total, not 4 x the longest
+    lens = [262144, 198000, 65536, 8192]
+    by_total = K.decode_split_pages(k8, 4, max(lens), sum(lens))
+    assert by_total < K.decode_split_pages(k8, 4, max(lens))
+    # one grid round: the workgroups that have pages fit on the 256 CUs
+    assert sum(-(-(-(-T // 256)) // by_total) for T in lens) * 4 <= 256
+    assert K.decode_split_pages(q4, 1, 1) == 1
+    with pytest.raises(K.KVError):
+        K.decode_split_pages(q4, 2, 100, 201)   # total above batch x max
