@@ -233,6 +233,7 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.status = (int32_t*)ws;
+  a.sched = (uint32_t*)(ws + 4);
   a.part_ml = (float*)(ws + w.ml_off);
   a.part_o = (float*)(ws + w.o_off);
   hipError_t e = launch_decode(a, phase, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);

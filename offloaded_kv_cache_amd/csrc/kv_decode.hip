@@ -335,15 +335,17 @@ struct SplitLds {
 };
 
 // NW waves per workgroup (4: two workgroups per CU; 8: one, with half the per-wave
-// registers, for the larger int8 K tiles).
-template <int KK, int VK, int NW>
+// registers, for the larger int8 K tiles). DYN: more work items than workgroups (taken
+// from a counter); otherwise workgroup i does item i only.
+template <int KK, int VK, int NW, bool DYN>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t n_pool_pages,
     const int32_t* __restrict__ block_tables, int max_pages, const int32_t* __restrict__ context_lens,
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch) {
   __shared__ __attribute__((aligned(16))) SplitLds<NW> lds;
+  __shared__ int item_s;
   constexpr int TPW = kPageTokens / NW, KT = TPW / 16;  // Q.K: tokens and tiles per wave
   constexpr int EPW = kHeadDim / NW, NTW = EPW / 16;    // P.V: elements and column tiles per wave
   constexpr int HFN = NTW / 2;                           // P.V halves of two column tiles
@@ -351,8 +353,25 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int elem = tid & (kHeadDim - 1);  // the query element of the thread (prologue)
   const int grp = lane >> 4, col = lane & 15;  // MFMA lane group and column
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = n_q_heads / n_kv_heads;
+  const int n_pairs = n_kv_heads * batch, n_items = n_splits * n_pairs;
+
+  // Work items (split, sequence, KV head), split-major. Workgroup i takes item i; when
+  // there are more items than workgroups (one round of resident workgroups), the rest
+  // are taken from a counter in the workspace, so that the workgroups on every CU share
+  // the items that have pages whatever the sequences' lengths. An item past a
+  // sequence's last page is skipped.
+  int item = blockIdx.x;
+  for (bool first = true;; first = false) {
+  if (!first) {
+    if (!DYN) break;
+    if (tid == 0) item_s = (int)gridDim.x + (int)atomicAdd(&sched[0], 1u);
+    __syncthreads();
+    item = item_s;
+    __syncthreads();
+  }
+  if (item >= n_items) break;
+  const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
 
   // Issued together before anything waits: the query of the group's heads (element
   // tid; unconditional loads of a clamped head), the context length and the split's
@@ -373,7 +392,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   }
   const int n_pages = (T + kPageTokens - 1) / kPageTokens;
   const int p_end = min(n_pages, p_begin + pages_per_split);
-  if (p_begin >= p_end) return;  // uniform over the workgroup
+  if (p_begin >= p_end) continue;  // uniform over the workgroup
 
   const int64_t head_bytes = plane_bytes(KK) + plane_bytes(VK);
   const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
@@ -765,6 +784,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       }
     }
   }
+  }  // work items
+
+  // the last workgroup to finish leaves the counters at zero for the next launch
+  if (DYN && tid == 0) {
+    __threadfence();
+    if (atomicAdd(&sched[1], 1u) == gridDim.x - 1) {
+      atomicExch(&sched[0], 0u);
+      atomicExch(&sched[1], 0u);
+    }
+  }
 }
 
 // Log-sum-exp merge of the partials of one (query head, sequence), then the
@@ -877,11 +906,20 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
 template <int KK, int VK>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   constexpr int NW = split_waves(KK);
-  dim3 grid((unsigned)a.n_splits, (unsigned)a.n_kv_heads, (unsigned)a.batch), block(64 * NW);
-  hipExtLaunchKernelGGL((decode_split<KK, VK, NW>), grid, block, 0, stream, start, stop, 0, a.q, a.pool,
-                        a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens, a.max_context,
-                        a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits, a.scale_log2,
-                        a.part_ml, a.part_o, a.status);
+  // one round of resident workgroups (two 4-wave or one 8-wave per CU), at most one per item
+  const int64_t items = (int64_t)a.n_splits * a.n_kv_heads * a.batch;
+  const int64_t resident = 256 * (8 / NW);
+  dim3 grid((unsigned)(items < resident ? items : resident)), block(64 * NW);
+  if (items > resident)
+    hipExtLaunchKernelGGL((decode_split<KK, VK, NW, true>), grid, block, 0, stream, start, stop, 0, a.q,
+                          a.pool, a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens,
+                          a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits,
+                          a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch);
+  else
+    hipExtLaunchKernelGGL((decode_split<KK, VK, NW, false>), grid, block, 0, stream, start, stop, 0, a.q,
+                          a.pool, a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens,
+                          a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits,
+                          a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch);
   return hipGetLastError();
 }
 

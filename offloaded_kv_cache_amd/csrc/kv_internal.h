@@ -112,6 +112,7 @@ struct DecodeArgs {
   float scale_log2;           // softmax_scale * log2(e)
   float* out;
   int32_t* status;
+  uint32_t* sched;            // two work counters, zero between launches
   float* part_ml;             // [batch][n_q_heads][n_splits][2]
   float* part_o;              // [batch][n_q_heads][n_splits][256]
 };
