@@ -423,15 +423,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 #pragma unroll
   for (int t = 0; t < NTW; ++t) voff[t] = vcode_off<KK, VK>(EPW, wave, lane, t);
   const uint32_t vsoff = vscale_off<KK, VK>(EPW, wave, lane);
-  {
-    // a bad page is read from page 0 and then ignored
-    const Rsrc r = page_rsrc(base ? base : pool, (int)head_bytes);
+  // a bad page is read from page 0 and then ignored
+  const Rsrc r0 = page_rsrc(base ? base : pool, (int)head_bytes);
+  // the K tiles now; the V share after the query's rotation, so that the query math
+  // runs while the memory pipeline drains the first burst
 #pragma unroll
-    for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r, koff[t], ksoff[t]);
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) load_vcodes<VK>(vsh, r, voff[nt], nt);
-    load_vscales<VK>(vsh, r, vsoff);
-  }
+  for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r0, koff[t], ksoff[t]);
 
   // (all eight head slots are transformed, unused ones hold zeros, so that each step's
   // exchanges are in flight together)
@@ -478,6 +475,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     }
   }
   __syncthreads();
+
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) load_vcodes<VK>(vsh, r0, voff[nt], nt);
+  load_vscales<VK>(vsh, r0, vsoff);
 
   // A operands of Q.K: row r = 2*head + part; MFMA j covers block j (elements 32j..32j+31)
   const int a_head = col >> 1, a_part = col & 1;
