@@ -484,9 +484,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   const int a_head = col >> 1, a_part = col & 1;
   const bool a_live = a_head < G;
   const float* qrow = lds.qs[a_head];
+  // The eight fragments are alike in every wave: each wave builds 8 / NW of them into
+  // LDS (the P.V fragment area, unused until the first page's softmax) and all read them.
   h8 qa[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int jj = 0; jj < 8 / NW; ++jj) {
+    const int j = (8 / NW) * wave + jj;
     float f[8];
     if (KK == kQ4) {
       // slots [e, e+2, e+16, e+18, e+1, e+3, e+17, e+19] with e = 32j + 4grp; high-nibble slots hold q/16
@@ -508,8 +511,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f[2 * s2] - (float)hi[0], f[2 * s2 + 1] - (float)hi[1]));
       w[s2] = a_live ? as_u32(a_part ? lo : hi) : 0u;
     }
-    qa[j] = __builtin_bit_cast(h8, w);
+    lds.afrag[j][lane] = __builtin_bit_cast(h8, w);
   }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qa[j] = lds.afrag[j][lane];
   // A operand of the offset correction: row 2*head + part, k-slot j (lane group 0) = block sum j
   h8 qc;
 #pragma unroll
