@@ -772,7 +772,60 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const float lsum = half_sum(l_run[r]);
     if (col == 0) lds.lsum[wave][2 * grp + r] = lsum;
   }
-  __syncthreads();
+  // the partial of heads 2grp + r at element EPW w + 16t + col (hi + lo rows)
+  float po[2][NTW];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) po[r][t] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
+  if (VK == kQ4) {
+    // V is stored rotated: the partial is rotated back here (H is linear, so the merge of
+    // rotated partials is the rotated merge). Element bits 0-3 (col) between lanes,
+    // the tile bits inside the lane, the wave bits through LDS.
+#pragma unroll
+    for (int bit = 0; bit < 4; ++bit) {
+      const int m = 1 << bit;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const float o = __shfl_xor(po[r][t], m);
+          po[r][t] = (lane & m) ? (o - po[r][t]) : (po[r][t] + o);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < NTW; m <<= 1)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          if (!(t & m)) {
+            const float x = po[r][t], y = po[r][t + m];
+            po[r][t] = x + y;
+            po[r][t + m] = x - y;
+          }
+    __syncthreads();  // the query rows in LDS are no longer read
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) lds.qs[2 * grp + r][EPW * wave + 16 * t + col] = po[r][t];
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const int e = EPW * wave + 16 * t + col, lo = e & (EPW - 1);
+        float acc = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) {  // NW-point transform over the wave bits
+          const float x = lds.qs[2 * grp + r][lo + EPW * k];
+          acc += (__builtin_popcount(k & wave) & 1) ? -x : x;
+        }
+        po[r][t] = acc * 0.0625f;
+      }
+  } else {
+    __syncthreads();
+  }
   const size_t S = (size_t)n_splits;
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
@@ -780,8 +833,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     if (hh < G) {
       const size_t idx = ((size_t)b * n_q_heads + g * G + hh) * S + split;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t)
-        part_o[idx * kHeadDim + EPW * wave + 16 * t + col] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
+      for (int t = 0; t < NTW; ++t) part_o[idx * kHeadDim + EPW * wave + 16 * t + col] = po[r][t];
       if (wave == 0 && col == 0) {
         float l = lds.lsum[0][hh];
 #pragma unroll
@@ -803,26 +855,29 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   }
 }
 
-// Log-sum-exp merge of the partials of one (query head, sequence), then the
-// rotation back by H. 1,024 threads: four groups of 256 (one thread per head
-// element) each merge a quarter of the splits. A thread's 32 partial values of
-// a pass are loaded together with the split maxima, before the weights are
-// known; the group sums are added in a fixed order.
-constexpr int kCombineThreads = 1024;
-constexpr int kCombineGroups = kCombineThreads / kHeadDim;
+// Log-sum-exp merge of the partials of one (query head, sequence) for one chunk of
+// 64 head elements (partials of rotated V were rotated back by the split kernel).
+// 256 threads: four groups of 64 (one thread per element) each merge a quarter of
+// the splits; a thread's 32 partial values of a pass are loaded together with the
+// split maxima, before the weights are known; the group sums are added in a fixed
+// order. Every chunk's workgroup forms the (cheap) maximum and weights itself.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineElems = 64;                              // head elements per workgroup
+constexpr int kCombineGroups = kCombineThreads / kCombineElems;
 constexpr int kCombineRun = 32;                                // splits per thread per pass
 constexpr int kCombinePass = kCombineGroups * kCombineRun;     // splits per pass
+constexpr int kCombineChunk = 1024;                            // split weights held in LDS
 
-template <bool ROTATE>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ context_lens, int max_context, int n_q_heads,
     int pages_per_split, int n_splits, float* __restrict__ out) {
-  __shared__ float wts[kCombineThreads];
-  __shared__ float part[kCombineGroups][kHeadDim];
+  __shared__ float wts[kCombineChunk];
+  __shared__ float part[kCombineGroups][kCombineElems];
   __shared__ float red[2][kCombineThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e = tid & (kHeadDim - 1), sg = tid / kHeadDim;
+  const int el = tid & (kCombineElems - 1), sg = tid / kCombineElems;
+  const int e = kCombineElems * blockIdx.z + el;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t base = ((size_t)b * n_q_heads + h) * (size_t)n_splits;
   // issued before the context length is known: split tid's maximum and the first
@@ -847,14 +902,14 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
 #pragma unroll
     for (int w = 1; w < kCombineThreads / 64; ++w) M = fmaxf(M, red[0][w]);
     float acc = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += kCombineThreads) {  // chunks of splits whose weights fit in LDS
-      const int cnt = min(kCombineThreads, ns - s0);
+    for (int s0 = 0; s0 < ns; s0 += kCombineChunk) {  // chunks of splits whose weights fit in LDS
+      const int cnt = min(kCombineChunk, ns - s0);
       __syncthreads();
-      if (tid < cnt) {
-        const float ms = s0 == 0 ? m_first : part_ml[2 * (base + s0 + tid)];
+      for (int s = tid; s < cnt; s += kCombineThreads) {
+        const float ms = (s0 == 0 && s == tid) ? m_first : part_ml[2 * (base + s0 + s)];
         const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        wts[tid] = w;
-        L += w * part_ml[2 * (base + s0 + tid) + 1];
+        wts[s] = w;
+        L += w * part_ml[2 * (base + s0 + s) + 1];
       }
       __syncthreads();
       for (int p0 = 0; p0 < cnt; p0 += kCombinePass) {
@@ -868,44 +923,24 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
 #pragma unroll
         for (int u = 0; u < kCombineRun; ++u) {
           const int s = first + u;
-          a += s < cnt ? wts[min(s, kCombineThreads - 1)] * v[u] : 0.f;  // splits past ns add nothing
+          a += s < cnt ? wts[min(s, kCombineChunk - 1)] * v[u] : 0.f;  // splits past ns add nothing
         }
         acc += a;
       }
     }
-    part[sg][e] = acc;
+    part[sg][el] = acc;
     for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
     if (lane == 0) red[1][wave] = L;
   }
   __syncthreads();
   if (ns > 0 && sg == 0) {
-    o = part[0][e];
+    o = part[0][el];
 #pragma unroll
-    for (int g = 1; g < kCombineGroups; ++g) o += part[g][e];
+    for (int g = 1; g < kCombineGroups; ++g) o += part[g][el];
     L = red[1][0];
 #pragma unroll
     for (int w = 1; w < kCombineThreads / 64; ++w) L += red[1][w];
     o = L > 0.f ? o / L : 0.f;  // L == 0 only if every page of the sequence was skipped
-  }
-  if (ROTATE) {
-    // bits 0..5 of the element index inside the wave, bits 6 and 7 through LDS
-    if (sg == 0) {
-#pragma unroll
-      for (int bit = 0; bit < 6; ++bit) {
-        const int m = 1 << bit;
-        const float other = __shfl_xor(o, m);
-        o = (lane & m) ? (other - o) : (o + other);
-      }
-    }
-    __syncthreads();
-    if (sg == 0) part[0][e] = o;
-    __syncthreads();
-    if (sg == 0) {
-      const int e0 = e & 63, k = e >> 6;
-      const float x0 = part[0][e0], x1 = part[0][e0 + 64], x2 = part[0][e0 + 128], x3 = part[0][e0 + 192];
-      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
-      o = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
-    }
   }
   if (sg == 0) out[((size_t)b * n_q_heads + h) * kHeadDim + e] = o;
 }
@@ -944,15 +979,9 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hip
     if (e != hipSuccess) return e;
   }
   if (phase & 2) {
-    dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch), block(kCombineThreads);
-    if (a.fmt == KV_FMT_INT8)
-      hipLaunchKernelGGL((decode_combine<false>), grid, block, 0, stream, a.part_ml, a.part_o,
-                         a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
-                         a.out);
-    else
-      hipLaunchKernelGGL((decode_combine<true>), grid, block, 0, stream, a.part_ml, a.part_o,
-                         a.context_lens, a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits,
-                         a.out);
+    dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch, kHeadDim / kCombineElems), block(kCombineThreads);
+    hipLaunchKernelGGL(decode_combine, grid, block, 0, stream, a.part_ml, a.part_o, a.context_lens,
+                       a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits, a.out);
     return hipGetLastError();
   }
   return hipSuccess;
