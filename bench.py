@@ -371,24 +371,37 @@ def run_streaming(args, dev):
                         "selected_pages": c["n_sel"], "miss_probability": c["miss"]})
 
 
+KERNEL_SRC = os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", "kv_decode.hip")
+
+
+def kernel_code_hash(path: str = KERNEL_SRC) -> str:
+    """sha256 of a kernel source with its comments removed and whitespace runs
+    collapsed, so that an edit of comments alone keeps the hash (the code that
+    the counters measured is unchanged)."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def counter_traffic(workload: str):
     """HBM bytes per decode_split launch from the committed counter summary, or None.
 
-    The summary records the sha256 of the kernel source its counters were taken
-    with; a kernel changed since then gives None."""
-    import hashlib
+    The summary records the code hash (kernel_code_hash) of the kernel its counters
+    were taken with; a kernel changed since then gives None."""
     path = os.path.join(ROOT, "profiles", "decode_q4_0_128k_hbm_bytes.txt")
     if workload != "c3" or not os.path.exists(path):
         return None
     sha = traffic = None
     for line in open(path):
-        if line.startswith("kernel source sha256"):
+        if line.startswith("kernel code sha256"):
             sha = line.rsplit(":", 1)[1].strip()
         elif line.startswith("decode_split traffic bytes per launch:"):
             traffic = int(float(line.rsplit(":", 1)[1]))
-    src = os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", "kv_decode.hip")
-    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return traffic if sha == cur else None
+    return traffic if sha == kernel_code_hash() else None
 
 
 def copy_calibration(args, dev):
@@ -427,12 +440,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--kernel-hash", action="store_true",
+                    help="print the code hash of the decode kernel source (comments removed) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times "
                          "(reference kernel for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.kernel_hash:
+        print(kernel_code_hash())
+        return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build measures the single-GPU decode path "
+        print(f"bench.py runs on one GPU only: it measures the single-GPU decode path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -156,7 +156,8 @@ size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch,
  * k^ and v^ are the dequantized records. T == 0 gives a zero output.
  * The work is split along the context ("split-K"): each split of
  * pages_per_split pages writes a partial (max, sum, weighted values) that a
- * second kernel combines with the log-sum-exp rule and rotates back.
+ * second kernel combines with the log-sum-exp rule (partials of rotated V are
+ * rotated back by the first kernel; H is linear, so this equals H o').
  * The arithmetic order depends only on logical token order, never on the
  * physical page ids, so results do not depend on where pages are placed.
  *
@@ -170,8 +171,13 @@ size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch,
  *   softmax_scale  e.g. 1/16 = 1/sqrt(256).
  *   out            device fp32 [batch][n_q_heads][256].
  *   workspace      device, >= kv_decode_workspace_bytes() bytes. Its first
- *                  int32 is a status word into which the kernels OR
- *                  KV_STATUS_* bits; the caller may read and clear it.
+ *                  16 bytes must be zero before the first call (e.g. once,
+ *                  right after allocation). The first int32 is a status word
+ *                  into which the kernels OR KV_STATUS_* bits; the caller may
+ *                  read and clear it. Bytes 4..11 are work counters that a
+ *                  call leaves at zero again when it ends; calls that use one
+ *                  workspace must therefore not overlap (same stream, or
+ *                  ordered by events).
  *   pages_per_split  pages per split (>= 1), or 0 for the library's choice.
  */
 int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
@@ -198,7 +204,7 @@ int32_t kv_decode_split_pages(const kv_shape* shape, int32_t batch, int64_t max_
  * separately (e.g. to time or overlap them). Same arguments and checks as
  * kv_decode_attention; kv_decode_split enqueues only the split-K kernel
  * (partials into the workspace), kv_decode_combine only the log-sum-exp
- * combine and rotation back (partials to `out`). Calling them in this order
+ * combine (partials to `out`). Calling them in this order
  * on one stream with identical arguments is exactly kv_decode_attention.
  */
 int kv_decode_split(const kv_shape* shape, const void* q, int32_t batch,

@@ -9,12 +9,17 @@
 // H): for every sequence and query head, softmax(scale * q'.k^) . v^ over the
 // dequantized records, then H for rotated V.
 //
-// Kernel 1 (decode_split): one workgroup of four wavefronts per (split, KV
-// head, sequence). A split is `pages_per_split` consecutive logical pages,
-// processed one 256-token page at a time by the whole workgroup: wave w
-// computes the scores of tokens 64w..64w+63 and the outputs of head elements
-// 64w..64w+63. Each wave holds its share of the next page in registers while
-// it works on the current one, so HBM latency is hidden behind the math.
+// Kernel 1 (decode_split): one workgroup of NW wavefronts per work item
+// (split, KV head, sequence); NW = 4 for q4 K (two workgroups per CU), 8 for
+// int8 K (one per CU, half the registers per wave for the larger K tiles). A
+// split is `pages_per_split` consecutive logical pages, processed one 256-token
+// page at a time by the whole workgroup: wave w computes the scores of tokens
+// (256/NW)w.. and the outputs of head elements (256/NW)w... Each wave holds its
+// share of the next page in registers while it works on the current one, so
+// HBM latency is hidden behind the math. Pages are read through a buffer
+// resource with loop-invariant 32-bit lane offsets. The grid is at most one
+// round of resident workgroups; items beyond it are taken from a counter in
+// the workspace, so a batch of mixed lengths keeps every CU busy.
 //
 //   Q.K on MFMA 16x16x32 f16. A = the query of the group's heads (rotated by H
 //   for q4 K), each head as two fp16 rows (hi, lo) carrying ~22 bits. B = 16
@@ -45,11 +50,13 @@
 //   exactly and multiplies it by the parts (exact while |8 d| stays below the
 //   fp16 maximum, i.e. rotated V elements below about 2^16 / 8 in magnitude).
 //
-//   The four waves then share the page maximum and sum; each writes its
-//   elements of the split's partial (max, sum, unnormalised output).
+//   The waves then share the page maximum and sum; each writes its elements of
+//   the split's partial (max, sum, unnormalised output). With rotated V the
+//   partial is rotated back by H first (H is linear, so merging rotated-back
+//   partials equals rotating the merged output back).
 //
-// Kernel 2 (decode_combine): per (query head, sequence), the log-sum-exp
-// merge of the partials, then the rotation back by H when V is rotated.
+// Kernel 2 (decode_combine): per (query head, sequence, 64-element chunk), the
+// log-sum-exp merge of the partials.
 //
 // Tokens past the context length are masked (score -inf, scale 0), so stale
 // or uninitialised rows of a partly filled page never contribute. Nothing
