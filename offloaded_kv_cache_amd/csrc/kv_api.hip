@@ -68,7 +68,7 @@ int64_t page_bytes_of(const kv_shape* s) { return (int64_t)s->n_kv_heads * head_
 // split may be partial, so the other batch - 1 sequences keep one workgroup per KV
 // head in reserve (a second, nearly empty round of workgroups would double the time).
 int32_t pages_per_split_for(const kv_shape* s, int32_t batch, int64_t total_pages) {
-  const int64_t target = 256 * (8 / split_waves(k_kind(s->format)));
+  const int64_t target = kComputeUnits * (8 / split_waves(k_kind(s->format)));
   int64_t room = target - (int64_t)(batch - 1) * s->n_kv_heads;
   if (room < s->n_kv_heads) room = s->n_kv_heads;
   int64_t pps = (total_pages * s->n_kv_heads + room - 1) / room;

@@ -401,6 +401,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   const int p_end = min(n_pages, p_begin + pages_per_split);
   if (p_begin >= p_end) continue;  // uniform over the workgroup
 
+  // Two workgroups share a CU when the grid is larger than the CU count; the one
+  // dispatched second (blockIdx past the CU count) would otherwise lose every issue
+  // tie to the older one's waves and finish its item well after it, leaving the CU
+  // half occupied at the end. Its waves take a higher issue priority for the first
+  // half of its pages, so the two finish close together.
+  const int boost_until = (!DYN && NW == 4 && (int)blockIdx.x >= kComputeUnits) ? p_begin + (p_end - p_begin) / 2 : p_begin;
+  if (boost_until > p_begin) __builtin_amdgcn_s_setprio(1);
+
   const int64_t head_bytes = plane_bytes(KK) + plane_bytes(VK);
   const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
   const int32_t* bt = block_tables + (size_t)b * max_pages;
@@ -771,6 +779,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       load_vcodes<VK>(vsh, nr, voff[2 * hf + 1], 2 * hf + 1);
     }
     base = next;
+    if (pg + 1 == boost_until) __builtin_amdgcn_s_setprio(0);
   }
 
   // ---------------- this split's partials: common max, summed weights, each wave's elements
@@ -957,7 +966,7 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t star
   constexpr int NW = split_waves(KK);
   // one round of resident workgroups (two 4-wave or one 8-wave per CU), at most one per item
   const int64_t items = (int64_t)a.n_splits * a.n_kv_heads * a.batch;
-  const int64_t resident = 256 * (8 / NW);
+  const int64_t resident = kComputeUnits * (8 / NW);
   dim3 grid((unsigned)(items < resident ? items : resident)), block(64 * NW);
   if (items > resident)
     hipExtLaunchKernelGGL((decode_split<KK, VK, NW, true>), grid, block, 0, stream, start, stop, 0, a.q,

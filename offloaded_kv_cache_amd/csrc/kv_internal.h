@@ -14,6 +14,7 @@ namespace kvc {
 
 constexpr int kHeadDim = 256;
 constexpr int kPageTokens = 256;
+constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxGroup = 8;  // query heads per KV head handled by one MFMA row tile
 
 enum RecordKind : int { kInt8 = 0, kQ4 = 1 };
