@@ -126,8 +126,8 @@ def run_resident(args, wl, dev):
     gen = torch.Generator(device=dev)
     gen.manual_seed(kvsynth.torch_seed(cfg, 99))
     q_all = torch.randn((n_steps, L, B, 24, 256), generator=gen, device=dev).to(torch.float16)
-    knew = torch.randn((n_steps, L, B, 1, 4, 256), generator=gen, device=dev).to(torch.float16)
-    vnew = torch.randn((n_steps, L, B, 1, 4, 256), generator=gen, device=dev).to(torch.float16)
+    knew = torch.randn((n_steps, L, B, 4, 256), generator=gen, device=dev).to(torch.float16)
+    vnew = torch.randn((n_steps, L, B, 4, 256), generator=gen, device=dev).to(torch.float16)
     ctx = torch.tensor([[start_lens[b] + st + 1 for b in range(B)] for st in range(n_steps)],
                        dtype=torch.int32, device=dev)
     ws = K.paged.DecodeWorkspace(s, B, max_ctx, args.pages_per_split, device=dev)
@@ -143,21 +143,27 @@ def run_resident(args, wl, dev):
 
     def step(st, timing):
         for layer in range(L):
-            for b in range(B):
-                T = start_lens[b] + st + 1
-                pools[layer].append(knew[st, layer, b], vnew[st, layer, b], T - 1,
-                                    tables[layer][b].contiguous() if B > 1 else tables[layer][0])
             # the split kernel's own start and end are recorded on its stream (kernel duration
             # without the queueing gap in front of it)
             evs = events[st][layer] if timing and layer % args.event_every == 0 else None
-            K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
-                               out, ws.data, pages_per_split=args.pages_per_split, phase="split",
-                               stream=stream, events=evs)
+            if args.separate_append:
+                for b in range(B):
+                    T = start_lens[b] + st + 1
+                    pools[layer].append(knew[st, layer, b][None], vnew[st, layer, b][None], T - 1,
+                                        tables[layer][b].contiguous() if B > 1 else tables[layer][0])
+                K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
+                                   out, ws.data, pages_per_split=args.pages_per_split, phase="split",
+                                   stream=stream, events=evs)
+                K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
+                                   out, ws.data, pages_per_split=args.pages_per_split, phase="combine",
+                                   stream=stream)
+            else:
+                # one layer's decode step: the token's append runs inside the split kernel
+                K.append_decode(s, knew[st, layer], vnew[st, layer], q_all[st, layer], pools[layer].data,
+                                tables[layer], ctx[st], max_ctx, out, ws.data,
+                                pages_per_split=args.pages_per_split, stream=stream, events=evs)
             if evs is not None:
                 timed_split.append((evs[0], evs[1], sum(start_lens[b] + st + 1 for b in range(B)) * per_tok))
-            K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
-                               out, ws.data, pages_per_split=args.pages_per_split, phase="combine",
-                               stream=stream)
 
     for st in range(args.warmup):
         step(st, False)
@@ -371,20 +377,24 @@ def run_streaming(args, dev):
                         "selected_pages": c["n_sel"], "miss_probability": c["miss"]})
 
 
-KERNEL_SRC = os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", "kv_decode.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", f)
+               for f in ("kv_decode.hip", "kv_encode.h", "kv_internal.h")]
 
 
-def kernel_code_hash(path: str = KERNEL_SRC) -> str:
-    """sha256 of a kernel source with its comments removed and whitespace runs
-    collapsed, so that an edit of comments alone keeps the hash (the code that
-    the counters measured is unchanged)."""
+def kernel_code_hash(paths=None) -> str:
+    """sha256 of the decode kernel's sources (the kernel file and the headers it
+    compiles from) with comments removed and whitespace runs collapsed, so that an
+    edit of comments alone keeps the hash (the code the counters measured is
+    unchanged)."""
     import hashlib
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()
+    h = hashlib.sha256()
+    for path in paths or KERNEL_SRCS:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
 
 
 def counter_traffic(workload: str):
@@ -437,6 +447,9 @@ def main():
                     help="record the split kernel's start/stop events on every N-th layer of each "
                          "timed step (all layers do identical work; recording them on every layer "
                          "adds about 2 us of queueing per layer to the step)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append each step's token with its own kernel (kv_append_quantize) before "
+                         "kv_decode_attention, instead of the fused kv_append_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -496,7 +509,8 @@ def main():
                                 "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4"}[args.workload],
                    "layers": wl["layers"], "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256,
                    "page_tokens": 256, "batch": len(wl["lens"]), "context": wl["lens"],
-                   "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto"},
+                   "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto",
+                   "append": "separate kernel" if args.separate_append else "fused into the split kernel"},
         "pct_of_hbm_peak": round(100 * res["value"] / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "decode_split", "achieved": round(res["achieved"], 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),

@@ -240,6 +240,39 @@ int kv_decode_split_timed(const kv_shape* shape, const void* q, int32_t batch,
                           void* start_event, void* stop_event);
 
 /*
+ * kv_append_decode - one decode step of one layer: append one token per
+ * sequence, then attend (Strata page, section "4-bit KV 缓存：先旋转，再压到
+ * 4-bit": K and V are rotated and quantized as they are written; KV-offload
+ * news page, section "缓存为何不能直接搬走？": the step then reads the whole
+ * cache of the layer).
+ *
+ * Equivalent, byte for byte in the pool and bit for bit in `out`, to
+ * kv_append_quantize of token T_b - 1 of every sequence b (T_b =
+ * context_lens[b], its block table row) followed by kv_decode_attention with
+ * the same arguments. The append is done inside the split-K kernel by the
+ * workgroup whose split holds the token's page, before that page is read, so
+ * the step takes two launches instead of three.
+ *
+ *   k_new, v_new   device fp16 [batch][n_kv_heads][256]: the token's K and V
+ *                  (finite values).
+ *   pool           device, writable (the token's row of its page is written).
+ *   start_event, stop_event  hipEvent_t or NULL: recorded at the start and
+ *                  end of the split-K kernel (as in kv_decode_split_timed).
+ * Every other argument is that of kv_decode_attention. A sequence whose
+ * context length is 0 or out of range appends nothing (the range case sets
+ * KV_STATUS_CONTEXT_CLAMPED); a token page id outside the pool appends nothing
+ * and sets KV_STATUS_BAD_PAGE_ID. Calls that share a workspace must not
+ * overlap.
+ */
+int kv_append_decode(const kv_shape* shape, const void* k_new, const void* v_new,
+                     const void* q, int32_t batch, void* pool, int64_t n_pool_pages,
+                     const int32_t* block_tables, int32_t max_pages,
+                     const int32_t* context_lens, int64_t max_context,
+                     float softmax_scale, float* out, void* workspace,
+                     size_t workspace_bytes, int32_t pages_per_split, void* stream,
+                     void* start_event, void* stop_event);
+
+/*
  * Residency table of one layer's device page slots (Strata page, section
  * "KV 从显存搬进内存之后发生了什么": a residency table with CLOCK second-chance
  * eviction). Plain host memory owned by the caller:

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed",
-    "kv_decode_combine",
+    "kv_decode_combine", "kv_append_decode",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
 )
@@ -69,6 +69,8 @@ def _load():
                                         P, P, SZ, I32, P]),
         "kv_decode_split_timed": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                             P, P, SZ, I32, P, P, P]),
+        "kv_append_decode": (C.c_int, [C.POINTER(KVShape), P, P, P, I32, P, I64, P, I32, P, I64,
+                                       F32, P, P, SZ, I32, P, P, P]),
         "kv_residency_reset": (C.c_int, [C.POINTER(KVResidency)]),
         "kv_residency_select": (C.c_int, [C.POINTER(KVResidency), P, I32, P, P, P, P]),
         "kv_gather_pages": (C.c_int, [C.POINTER(KVShape), C.POINTER(KVResidency), P, I32, P, P, P,
@@ -208,6 +210,38 @@ def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_contex
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
         softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream), *extra))
+
+
+def append_decode(s: KVShape, k_new, v_new, q, pool, block_tables, context_lens, max_context: int,
+                  out, workspace, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
+                  stream=None, events=None):
+    """One decode step of one layer (kv_append_decode): append token context_lens[b] - 1
+    of every sequence (``k_new``, ``v_new`` fp16 [B, n_kv_heads, 256]) into ``pool``,
+    then attend; writes fp32 ``out`` [B, Hq, 256]. ``events`` = (start, stop)
+    torch.cuda.Event pair recorded at the split kernel's own start and end."""
+    torch = _torch()
+    B = q.shape[0]
+    if q.shape != (B, s.n_q_heads, s.head_dim) or out.shape != (B, s.n_q_heads, s.head_dim):
+        raise ValueError("q and out must be [batch, n_q_heads, head_dim]")
+    if k_new.shape != (B, s.n_kv_heads, s.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [batch, n_kv_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
+    ev = [None, None]
+    if events is not None:
+        for i, e in enumerate(events):
+            if not e.cuda_event:
+                e.record()  # creates the underlying event
+            ev[i] = e.cuda_event
+    pb = page_bytes(s)
+    _check(lib.kv_append_decode(
+        C.byref(s), _ptr(k_new, torch.float16, name="k_new"), _ptr(v_new, torch.float16, name="v_new"),
+        _ptr(q, torch.float16, name="q"), B, C.c_void_p(pool.data_ptr()), pool.numel() // pb,
+        _ptr(block_tables, torch.int32, name="block_tables"), block_tables.shape[1],
+        _ptr(context_lens, torch.int32, name="context_lens"), max_context, softmax_scale,
+        _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream),
+        C.c_void_p(ev[0]), C.c_void_p(ev[1])))
 
 
 class Residency:

@@ -193,7 +193,8 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
                  int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
                  const int32_t* context_lens, int64_t max_context, float softmax_scale, float* out,
                  void* workspace, size_t workspace_bytes, int32_t pages_per_split, void* stream,
-                 void* start_event = nullptr, void* stop_event = nullptr) {
+                 void* start_event = nullptr, void* stop_event = nullptr,
+                 const void* k_new = nullptr, const void* v_new = nullptr) {
   if (int r = check_shape(shape)) return r;
   if (batch < 0 || batch > 65535) return fail(KV_EINVAL, "batch out of range (%d)", batch);
   if (batch == 0) return ok();
@@ -236,6 +237,11 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.sched = (uint32_t*)(ws + 4);
   a.part_ml = (float*)(ws + w.ml_off);
   a.part_o = (float*)(ws + w.o_off);
+  if (k_new) {
+    a.k_new = (const uint16_t*)k_new;
+    a.v_new = (const uint16_t*)v_new;
+    a.pool_w = (uint8_t*)const_cast<void*>(pool);
+  }
   hipError_t e = launch_decode(a, phase, (hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();
@@ -274,6 +280,23 @@ int kv_decode_split_timed(const kv_shape* shape, const void* q, int32_t batch, c
   return decode_phase(1, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
                       max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
                       stream, start_event, stop_event);
+}
+
+int kv_append_decode(const kv_shape* shape, const void* k_new, const void* v_new, const void* q,
+                     int32_t batch, void* pool, int64_t n_pool_pages, const int32_t* block_tables,
+                     int32_t max_pages, const int32_t* context_lens, int64_t max_context,
+                     float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                     int32_t pages_per_split, void* stream, void* start_event, void* stop_event) {
+  if (batch > 0 && (!k_new || !v_new)) return fail(KV_EINVAL, "NULL buffer");
+  if (batch > 0 && (!aligned(k_new, 2) || !aligned(v_new, 2)))
+    return fail(KV_EALIGN, "misaligned buffer (k_new, v_new: 2 B)");
+  int r = decode_phase(1, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
+                       max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
+                       stream, start_event, stop_event, k_new, v_new);
+  if (r != KV_OK) return r;
+  return decode_phase(2, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
+                      max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
+                      stream);
 }
 
 int kv_decode_combine(const kv_shape* shape, const void* q, int32_t batch, const void* pool,

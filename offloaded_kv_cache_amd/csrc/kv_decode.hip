@@ -63,7 +63,7 @@
 // depends on the physical page ids except the addresses read.
 #include <hip/hip_ext.h>
 
-#include "kv_internal.h"
+#include "kv_encode.h"
 
 namespace kvc {
 namespace {
@@ -341,16 +341,23 @@ struct SplitLds {
   float bsum[kMaxGroup][8];
 };
 
+__device__ inline int32_t bt_row_entry(const int32_t* __restrict__ block_tables, int b, int max_pages, int pg) {
+  return block_tables[(size_t)b * max_pages + pg];
+}
+
 // NW waves per workgroup (4: two workgroups per CU; 8: one, with half the per-wave
 // registers, for the larger int8 K tiles). DYN: more work items than workgroups (taken
-// from a counter); otherwise workgroup i does item i only.
-template <int KK, int VK, int NW, bool DYN>
+// from a counter); otherwise workgroup i does item i only. APPEND: the call also
+// appends one token per sequence (k_new, v_new [batch][n_kv_heads][256] fp16, at
+// position context_lens[b] - 1), written through pool_w (the pool's address).
+template <int KK, int VK, int NW, bool DYN, bool APPEND>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ pool, int64_t n_pool_pages,
+    const uint16_t* __restrict__ q, const uint8_t* pool, int64_t n_pool_pages,
     const int32_t* __restrict__ block_tables, int max_pages, const int32_t* __restrict__ context_lens,
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch) {
+    int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint8_t* pool_w) {
   __shared__ __attribute__((aligned(16))) SplitLds<NW> lds;
   __shared__ int item_s;
   constexpr int TPW = kPageTokens / NW, KT = TPW / 16;  // Q.K: tokens and tiles per wave
@@ -379,6 +386,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   }
   if (item >= n_items) break;
   const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
+  // APPEND: the new token's K (even waves) or V (odd waves) inputs, loaded first so that
+  // they arrive before the page loads fill the memory pipeline (only the workgroup whose
+  // split holds the token's page uses them, in waves 0 and 1)
+  uint16_t new_in[4];
+  if (APPEND) enc::load_vals((wave & 1 ? v_new : k_new) + ((size_t)b * n_kv_heads + g) * kHeadDim, lane, new_in);
 
   // Issued together before anything waits: the query of the group's heads (element
   // tid; unconditional loads of a clamped head), the context length and the split's
@@ -393,7 +405,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   const int p_begin = split * pages_per_split;
   const int32_t phys_first = block_tables[(size_t)b * max_pages + min(p_begin, max_pages - 1)];
   int T = context_lens[b];
-  if (T > max_context || T < 0) {
+  const bool t_in_range = T <= max_context && T >= 0;
+  if (!t_in_range) {
     if (tid == 0 && split == 0 && g == 0) atomicOr(status, KV_STATUS_CONTEXT_CLAMPED);
     T = T < 0 ? 0 : max_context;
   }
@@ -406,7 +419,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   // tie to the older one's waves and finish its item well after it, leaving the CU
   // half occupied at the end. Its waves take a higher issue priority for the first
   // half of its pages, so the two finish close together.
-  const int boost_until = (!DYN && NW == 4 && (int)blockIdx.x >= kComputeUnits) ? p_begin + (p_end - p_begin) / 2 : p_begin;
+  // The appended token (APPEND, length in range): written by the item whose pages hold
+  // it, before any wave of the workgroup reads its page. On the item's first page it is
+  // written before the first loads; on a later page, while the first page is in flight,
+  // and the workgroup synchronises once before that page's loads are issued.
+  int new_pg = -1;
+  if (APPEND && t_in_range && T > 0 && (T - 1) / kPageTokens >= p_begin && (T - 1) / kPageTokens < p_end)
+    new_pg = (T - 1) / kPageTokens;
+  const bool new_first = new_pg == p_begin;
+  const int32_t phys_new = new_pg >= 0 ? bt_row_entry(block_tables, b, max_pages, new_pg) : -1;
+  // (the appending workgroup, which also encodes the token, keeps it for its whole item)
+  const int boost_until = (!DYN && NW == 4 && ((int)blockIdx.x >= kComputeUnits || new_pg >= 0))
+                              ? (new_pg >= 0 ? p_end : p_begin + (p_end - p_begin) / 2)
+                              : p_begin;
   if (boost_until > p_begin) __builtin_amdgcn_s_setprio(1);
 
   const int64_t head_bytes = plane_bytes(KK) + plane_bytes(VK);
@@ -442,8 +467,45 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   const Rsrc r0 = page_rsrc(base ? base : pool, (int)head_bytes);
   // the K tiles now; the V share after the query's rotation, so that the query math
   // runs while the memory pipeline drains the first burst
+  if (!new_first) {
 #pragma unroll
-  for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r0, koff[t], ksoff[t]);
+    for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r0, koff[t], ksoff[t]);
+  }
+  // The token's records: wave 0 encodes its K vector of this KV head, wave 1 its V
+  // vector, from the inputs `in` (fp16 bits of elements lane + 64k), and writes them.
+  auto append_token = [&](const uint16_t (&in)[4]) {
+    const int row = (T - 1) % kPageTokens;
+    if (phys_new < 0 || phys_new >= n_pool_pages) {
+      if (tid == 0) atomicOr(status, KV_STATUS_BAD_PAGE_ID);
+    } else if (wave < 2) {
+      uint8_t* head = pool_w + (int64_t)phys_new * page_bytes + (int64_t)g * head_bytes;
+      int code[4];
+      uint16_t scale[4];
+      if (KK == VK) {
+        enc::encode_vals<KK>(in, lane, code, scale);
+      } else if (wave == 0) {
+        enc::encode_vals<KK>(in, lane, code, scale);
+      } else {
+        enc::encode_vals<VK>(in, lane, code, scale);
+      }
+      if (wave == 0) {
+        enc::write_k_row<KK>(head, row, lane, code, scale);
+      } else {
+        enc::write_v_scales<VK>(head + plane_bytes(KK), row, lane, scale);
+        enc::write_v_codes_one<VK>(head + plane_bytes(KK), row, lane, code);
+      }
+    }
+    // the token's bytes are complete (and visible to the workgroup) before its page is read
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+  };
+  // On the item's first page the token is written before the first loads.
+  if (APPEND && new_first) append_token(new_in);
+  if (new_first) {
+#pragma unroll
+    for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r0, koff[t], ksoff[t]);
+  }
 
   // (all eight head slots are transformed, unused ones hold zeros, so that each step's
   // exchanges are in flight together)
@@ -550,6 +612,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 #pragma unroll
   for (int t = 0; t < NTW; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
   __syncthreads();
+  // On a later page the token is written here, once the query is prepared and its inputs
+  // (loaded first) have long arrived, and before the loop issues any load of its page.
+  if (APPEND && new_pg > p_begin) append_token(new_in);
 
   for (int pg = p_begin; pg < p_end; ++pg) {
     const bool page_ok = base != nullptr;
@@ -961,23 +1026,28 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
   if (sg == 0) out[((size_t)b * n_q_heads + h) * kHeadDim + e] = o;
 }
 
+template <int KK, int VK, bool DYN, bool APPEND>
+void launch_split_v(const DecodeArgs& a, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  constexpr int NW = split_waves(KK);
+  hipExtLaunchKernelGGL((decode_split<KK, VK, NW, DYN, APPEND>), grid, dim3(64 * NW), 0, stream, start,
+                        stop, 0, a.q, a.pool, a.n_pool_pages, a.block_tables, a.max_pages,
+                        a.context_lens, a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split,
+                        a.n_splits, a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch,
+                        a.k_new, a.v_new, a.pool_w);
+}
+
 template <int KK, int VK>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   constexpr int NW = split_waves(KK);
   // one round of resident workgroups (two 4-wave or one 8-wave per CU), at most one per item
   const int64_t items = (int64_t)a.n_splits * a.n_kv_heads * a.batch;
   const int64_t resident = kComputeUnits * (8 / NW);
-  dim3 grid((unsigned)(items < resident ? items : resident)), block(64 * NW);
-  if (items > resident)
-    hipExtLaunchKernelGGL((decode_split<KK, VK, NW, true>), grid, block, 0, stream, start, stop, 0, a.q,
-                          a.pool, a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens,
-                          a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits,
-                          a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch);
-  else
-    hipExtLaunchKernelGGL((decode_split<KK, VK, NW, false>), grid, block, 0, stream, start, stop, 0, a.q,
-                          a.pool, a.n_pool_pages, a.block_tables, a.max_pages, a.context_lens,
-                          a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split, a.n_splits,
-                          a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch);
+  const dim3 grid((unsigned)(items < resident ? items : resident));
+  const bool dyn = items > resident, app = a.k_new != nullptr;
+  if (dyn && app) launch_split_v<KK, VK, true, true>(a, grid, stream, start, stop);
+  else if (dyn) launch_split_v<KK, VK, true, false>(a, grid, stream, start, stop);
+  else if (app) launch_split_v<KK, VK, false, true>(a, grid, stream, start, stop);
+  else launch_split_v<KK, VK, false, false>(a, grid, stream, start, stop);
   return hipGetLastError();
 }
 

@@ -116,6 +116,11 @@ struct DecodeArgs {
   uint32_t* sched;            // two work counters, zero between launches
   float* part_ml;             // [batch][n_q_heads][n_splits][2]
   float* part_o;              // [batch][n_q_heads][n_splits][256]
+  // optional: one token per sequence appended by the split kernel (position
+  // context_lens[b] - 1) before attention reads it; null = no append
+  const uint16_t* k_new = nullptr;  // [batch][n_kv_heads][256] fp16
+  const uint16_t* v_new = nullptr;
+  uint8_t* pool_w = nullptr;        // the pool, writable
 };
 
 // phase: 1 = split kernel only, 2 = combine only, 3 = both. start/stop (may be
