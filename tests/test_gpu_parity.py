@@ -264,3 +264,61 @@ def test_decode_extreme_scales(gpu, fmt):
         got, status = run_decode(gpu, fmt, seqs, q, pps, seed=5 + pps)
         assert status == 0
         assert_close(got, oracle_out(q, seqs, fmt), what=f"{fmt} pps {pps}")
+
+
+MERGE_CASES = [
+    ("T4096", [4096], 0),
+    ("T3000_pps2", [3000], 2),
+    ("T200k_pps1", [200000], 1),       # more work items than resident workgroups (counter-fed)
+    ("batch", [1000, 4096, 17, 0, 513], 1),
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("name, lens, pps", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_attention_equals_its_two_phases(gpu, fmt, name, lens, pps):
+    """kv_decode_attention is bit-identical to kv_decode_split then kv_decode_combine,
+    also when more work items than resident workgroups are fed from the workspace
+    counters, which every call leaves at zero for the next."""
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    need = [-(-T // 256) for T in lens]
+    n_pool = sum(need) + 1
+    rng = np.random.default_rng(len(lens) + pps)
+    # valid records are not needed for a bitwise comparison of two merges: random bytes
+    # with small positive fp16 scales (set through the oracle's layout of one page)
+    one = layout.pack_pages(*records_of_noise(fmt, rng), fmt_id(fmt))[0]
+    pool = to_dev(np.tile(one, n_pool), gpu)
+    perm = kvsynth.permutation_np(3, n_pool)
+    bt = np.zeros((len(lens), max(need)), np.int32)
+    off = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[off:off + n]
+        off += n
+    q = to_dev(kvsynth.q_np(27, 0, len(lens)), gpu)
+    ctx, btd = to_dev(np.array(lens, np.int32), gpu), to_dev(bt, gpu)
+    max_ctx = max(lens)
+    outs = []
+    for fused in (True, False, True):
+        ws = K.paged.DecodeWorkspace(s, len(lens), max_ctx, pps, device=gpu)
+        out = torch.full((len(lens), 24, 256), float("nan"), dtype=torch.float32, device=gpu)
+        if fused:
+            K.decode_attention(s, q, pool, btd, ctx, max_ctx, out, ws.data, pages_per_split=pps)
+            K.decode_attention(s, q, pool, btd, ctx, max_ctx, out, ws.data, pages_per_split=pps)
+        else:
+            K.decode_attention(s, q, pool, btd, ctx, max_ctx, out, ws.data, pages_per_split=pps, phase="split")
+            K.decode_attention(s, q, pool, btd, ctx, max_ctx, out, ws.data, pages_per_split=pps, phase="combine")
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        assert int(ws.data[4:16].view(torch.int32).abs().sum().item()) == 0, "counters not reset"
+        outs.append(out.cpu().numpy())
+    assert np.all(np.isfinite(outs[0]))
+    assert np.array_equal(outs[0], outs[1]), f"{fmt} {name}: one call differs from its two phases"
+    assert np.array_equal(outs[0], outs[2])
+
+
+def records_of_noise(fmt, rng):
+    """Oracle records of one page of noise vectors (256 tokens, 4 KV heads)."""
+    k = (rng.standard_normal((256, 4, 256)) * 2).astype(np.float16)
+    v = (rng.standard_normal((256, 4, 256)) * 2).astype(np.float16)
+    return oracle_records(k, v, fmt)
