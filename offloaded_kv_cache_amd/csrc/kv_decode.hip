@@ -386,11 +386,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   }
   if (item >= n_items) break;
   const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
-  // APPEND: the new token's K (even waves) or V (odd waves) inputs, loaded first so that
-  // they arrive before the page loads fill the memory pipeline (only the workgroup whose
-  // split holds the token's page uses them, in waves 0 and 1)
-  uint16_t new_in[4];
-  if (APPEND) enc::load_vals((wave & 1 ? v_new : k_new) + ((size_t)b * n_kv_heads + g) * kHeadDim, lane, new_in);
 
   // Issued together before anything waits: the query of the group's heads (element
   // tid; unconditional loads of a clamped head), the context length and the split's
@@ -427,10 +422,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   if (APPEND && t_in_range && T > 0 && (T - 1) / kPageTokens >= p_begin && (T - 1) / kPageTokens < p_end)
     new_pg = (T - 1) / kPageTokens;
   const bool new_first = new_pg == p_begin;
+  // its K (even waves) or V (odd waves) inputs, loaded before the pages (waves 0 and 1 use them)
+  uint16_t new_in[4] = {0, 0, 0, 0};
+  if (APPEND && new_pg >= 0)
+    enc::load_vals((wave & 1 ? v_new : k_new) + ((size_t)b * n_kv_heads + g) * kHeadDim, lane, new_in);
   const int32_t phys_new = new_pg >= 0 ? bt_row_entry(block_tables, b, max_pages, new_pg) : -1;
-  // (the appending workgroup, which also encodes the token, keeps it for its whole item)
+  // (the appending workgroup, which also encodes the token, keeps it one page longer)
   const int boost_until = (!DYN && NW == 4 && ((int)blockIdx.x >= kComputeUnits || new_pg >= 0))
-                              ? (new_pg >= 0 ? p_end : p_begin + (p_end - p_begin) / 2)
+                              ? min(p_end, p_begin + (p_end - p_begin) / 2 + (new_pg >= 0 ? 1 : 0))
                               : p_begin;
   if (boost_until > p_begin) __builtin_amdgcn_s_setprio(1);
 

@@ -10,7 +10,9 @@
 // One wave encodes one vector. Lane l holds elements e = l + 64k (k = 0..3).
 // The rotation is done in fp64, where it is exact for fp16 inputs (partial sums
 // are multiples of 2^-28 below 2^20): stages for bits 0..5 exchange between
-// lanes, bits 6 and 7 are inside the lane.
+// lanes (DPP lane selects and lane swaps, no LDS), bits 6 and 7 are inside the
+// lane. Scales are rounded to fp16 and codes decided without branches on
+// per-lane data and without fp64 division, each decision being the exact one.
 #pragma once
 
 #include "kv_internal.h"
@@ -18,37 +20,114 @@
 namespace kvc {
 namespace enc {
 
-// Maximum over the wave of each of the lane's four values (exchanges of the four
-// values are issued together).
-__device__ inline void wave_max4(double (&v)[4]) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) t[k] = __shfl_xor(v[k], o);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], t[k]);
+// Lane exchanges without the LDS crossbar: the value of lane (lane ^ M). M = 1, 2, 8
+// are DPP lane selects inside a row of 16 (quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_ror:8); M = 4 is row_half_mirror (lane ^ 7) then quad_perm [3,2,1,0] (lane ^ 3);
+// M = 16 and 32 are the row and half-wave swaps of gfx950, whose second result holds
+// the partner's value in the lower rows and the first result in the upper ones.
+typedef uint32_t swap2 __attribute__((ext_vector_type(2)));
+template <int M>
+__device__ inline uint32_t xchg32(uint32_t v, int lane) {
+  if (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  if (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  if (M == 4) {
+    const int t = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp(t, 0x1B, 0xF, 0xF, false);
   }
+  if (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+  if (M == 16) {
+    const swap2 r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  }
+  const swap2 r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane & 32) ? r[0] : r[1];
+}
+template <int M>
+__device__ inline double xchg64(double v, int lane) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = xchg32<M>((uint32_t)b, lane), hi = xchg32<M>((uint32_t)(b >> 32), lane);
+  return __builtin_bit_cast(double, (hi << 32) | lo);
+}
+
+// One butterfly stage (bit log2 M) and one max stage on the lane's four values.
+template <int M>
+__device__ inline void wht_stage(double (&y)[4], int lane) {
+  const bool upper = lane & M;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double o = xchg64<M>(y[k], lane);
+    y[k] = upper ? (o - y[k]) : (y[k] + o);
+  }
+}
+template <int M>
+__device__ inline void max_stage(double (&v)[4], int lane) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], xchg64<M>(v[k], lane));
+}
+
+// Maximum over the wave of each of the lane's four values.
+__device__ inline void wave_max4(double (&v)[4], int lane) {
+  max_stage<1>(v, lane);
+  max_stage<2>(v, lane);
+  max_stage<4>(v, lane);
+  max_stage<8>(v, lane);
+  max_stage<16>(v, lane);
+  max_stage<32>(v, lane);
 }
 
 // Exact y = H x on the lane's four elements.
 __device__ inline void wht256(double (&y)[4], int lane) {
-#pragma unroll
-  for (int bit = 0; bit < 6; ++bit) {
-    const int m = 1 << bit;
-    const bool upper = lane & m;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double o = __shfl_xor(y[k], m);
-      y[k] = upper ? (o - y[k]) : (y[k] + o);
-    }
-  }
+  wht_stage<1>(y, lane);
+  wht_stage<2>(y, lane);
+  wht_stage<4>(y, lane);
+  wht_stage<8>(y, lane);
+  wht_stage<16>(y, lane);
+  wht_stage<32>(y, lane);
   const double a0 = y[0] + y[1], a1 = y[0] - y[1];  // bit 6
   const double a2 = y[2] + y[3], a3 = y[2] - y[3];
   y[0] = (a0 + a2) * 0.0625;                          // bit 7, then 1/16
   y[2] = (a0 - a2) * 0.0625;
   y[1] = (a1 + a3) * 0.0625;
   y[3] = (a1 - a3) * 0.0625;
+}
+
+// fp64 -> fp16, round to nearest even, without branches: x is rounded to fp32 with
+// round-to-odd (the fp32 nearest, moved toward zero by one unit if it lies beyond x,
+// and its last bit set whenever it is not x), then to fp16 with round to nearest even.
+// fp32 keeps 13 bits more than fp16 (and reaches 2^-149 against fp16's 2^-24), so the
+// odd last bit stands for every discarded bit and the second rounding is the one an
+// exact rounding of x would make. Overflow gives infinity.
+__device__ inline uint16_t f64_to_f16_fast(double x) {
+  const float f = (float)x;
+  const uint32_t fb = __builtin_bit_cast(uint32_t, f);
+  const double fd = (double)f;
+  const uint32_t beyond = fabs(fd) > fabs(x) ? 1u : 0u;  // toward zero by one unit (same sign)
+  const uint32_t odd = ((fb - beyond) | 1u);
+  const uint32_t r = fd != x ? odd : fb;
+  return __builtin_bit_cast(uint16_t, (_Float16)__builtin_bit_cast(float, r));
+}
+
+// Codes decided exactly without a division: an fp32 estimate of x/d, then the exact
+// tests of the rounding thresholds (c +- 1/2) * |d|, which are fp64 products of an
+// 11-bit scale and a 6-bit constant. The estimate is within a small fraction of a unit
+// of x/d (|x/d| is at most about 128), so at most one correction applies.
+// The integer c with (c - 1/2) ad <= sx < (c + 1/2) ad (ties upward), ad > 0.
+__device__ inline double round_quotient(double sx, double ad) {
+  double c = __builtin_floor((double)((float)sx * __builtin_amdgcn_rcpf((float)ad)) + 0.5);
+  c += sx >= (c + 0.5) * ad ? 1.0 : 0.0;
+  c -= sx < (c - 0.5) * ad ? 1.0 : 0.0;
+  return c;
+}
+// int8: round half away from zero of x/d, clamped to +-127 (d >= 0).
+__device__ inline int int8_code_fast(double x, double d) {
+  const double c = round_quotient(fabs(x), d == 0.0 ? 1.0 : d);
+  const int ci = d == 0.0 ? 0 : (c > 127.0 ? 127 : (int)c);
+  return x < 0 ? -ci : ci;
+}
+// q4: floor(y/d + 1/2) + 8, clamped to [0, 15].
+__device__ inline int q4_code_fast(double y, double d) {
+  const double c = round_quotient(d < 0 ? -y : y, d == 0.0 ? 1.0 : fabs(d)) + 8.0;
+  return d == 0.0 ? 8 : (c < 0.0 ? 0 : (c > 15.0 ? 15 : (int)c));
 }
 
 // The record of one vector: codes of the lane's elements and the scales.
@@ -65,11 +144,11 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
     double a[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
-    wave_max4(a);
+    wave_max4(a, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      scale[k] = f64_to_f16_rne(a[k] / 127.0);
-      code[k] = int8_code(x[k], f16_to_f64(scale[k]));
+      scale[k] = f64_to_f16_fast(a[k] / 127.0);
+      code[k] = int8_code_fast(x[k], f16_to_f64(scale[k]));
     }
   } else {
     wht256(x, lane);
@@ -78,22 +157,26 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
     double m[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      double t[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) t[k] = __shfl_xor(m[k], o);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) m[k] = fmax(m[k], t[k]);
-    }
+    max_stage<1>(m, lane);
+    max_stage<2>(m, lane);
+    max_stage<4>(m, lane);
+    max_stage<8>(m, lane);
+    max_stage<16>(m, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint64_t hit = __ballot(fabs(x[k]) == m[k]);
-      const uint32_t half = (lane & 32) ? (uint32_t)(hit >> 32) : (uint32_t)hit;
       // (no hit only for NaN inputs, whose codes are unspecified)
-      const double best = __shfl(x[k], (lane & 32) + (half ? __builtin_ctz(half) : (lane & 31)));
-      scale[k] = f64_to_f16_rne(-best * 0.125);  // -m/8 is exact in fp64
-      code[k] = q4_code(x[k], f16_to_f64(scale[k]));
+      const int i_lo = (uint32_t)hit ? __builtin_ctz((uint32_t)hit) : 0;
+      const int i_hi = 32 + ((uint32_t)(hit >> 32) ? __builtin_ctz((uint32_t)(hit >> 32)) : 0);
+      // both halves' values read as scalars, then each lane keeps its half's
+      const uint64_t xb = __builtin_bit_cast(uint64_t, x[k]);
+      const uint32_t l0 = __builtin_amdgcn_readlane((uint32_t)xb, i_lo), l1 = __builtin_amdgcn_readlane((uint32_t)xb, i_hi);
+      const uint32_t h0 = __builtin_amdgcn_readlane((uint32_t)(xb >> 32), i_lo),
+                     h1 = __builtin_amdgcn_readlane((uint32_t)(xb >> 32), i_hi);
+      const uint32_t sel = (lane & 32) ? ~0u : 0u;
+      const double best = __builtin_bit_cast(double, ((uint64_t)(h0 ^ ((h0 ^ h1) & sel)) << 32) | (l0 ^ ((l0 ^ l1) & sel)));
+      scale[k] = f64_to_f16_fast(-best * 0.125);  // -m/8 is exact in fp64
+      code[k] = q4_code_fast(x[k], f16_to_f64(scale[k]));
     }
   }
 }
@@ -126,7 +209,7 @@ __device__ inline void write_k_row(uint8_t* __restrict__ plane, int row, int lan
     if (KIND == kInt8) {
       codes[64 * (r >> 3) + 8 * j + (r & 7)] = (uint8_t)(int8_t)code[k];
     } else {
-      const int partner = __shfl_xor(code[k], 16);  // element e ^ 16, same block
+      const int partner = (int)xchg32<16>((uint32_t)code[k], lane);  // element e ^ 16, same block
       if (r < 16) codes[32 * (r >> 2) + 4 * j + (r & 3)] = (uint8_t)(code[k] | (partner << 4));
     }
   }

@@ -83,6 +83,50 @@ def test_append_bitexact(gpu, fmt):
     assert np.array_equal(got_pages[:2], want[:2])
 
 
+def rounding_edge_vectors(n_kv_heads=4):
+    """Vectors a e_0 + b e_1: after the rotation every element is (a +- b) / 16, so the
+    q4 scale is fp16(-(a + b) / 128) and the other elements sit at -8 (a - b) / (a + b)
+    in units of it. Chosen to hit fp16 ties of the scale (2049, 2051: ties to even),
+    a value just past a tie, code ties (-0.5, -3.5: half up) and a subnormal scale."""
+    pairs = [(2048, 1), (2048, 3), (2048, 1 + 2 ** -10), (17, 15), (23, 9), (-23, -9),
+             (2 ** -14, 2 ** -20), (2048, -1), (65504, 65504)]
+    vs = []
+    for a, b in pairs:
+        x = np.zeros((n_kv_heads, 256), np.float16)
+        x[:, 0], x[:, 1] = a, b
+        vs.append(x)
+        y = x.copy()
+        y[:, 0], y[:, 1] = b, a  # the larger magnitude second
+        vs.append(y)
+    return np.stack(vs)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_rounding_edges_bitexact(gpu, fmt):
+    """Scale and code rounding edge cases appended one token at a time and as a chunk,
+    bit for bit against the oracle's records."""
+    sp = np.concatenate([rounding_edge_vectors(), special_vectors()])
+    T = len(sp)
+    s = K.shape(fmt)
+    pb = K.page_bytes(s)
+    for chunk in (1, T):
+        pool = torch.zeros(2 * pb, dtype=torch.uint8, device=gpu)
+        btd = to_dev(np.array([1], np.int32), gpu)
+        status = torch.zeros(1, dtype=torch.int32, device=gpu)
+        kd, vd = to_dev(sp, gpu), to_dev(sp[::-1].copy(), gpu)
+        for a in range(0, T, chunk):
+            K.append_quantize(s, kd[a:a + chunk].contiguous(), vd[a:a + chunk].contiguous(), a, btd, pool, status)
+        torch.cuda.synchronize()
+        assert status.item() == 0
+        got = pool.cpu().numpy().reshape(2, pb)[[1]]
+        kc, ks, vc, vs = oracle_records(sp, sp[::-1].copy(), fmt)
+        a_, b_, c_, d_ = layout.unpack_pages(got, fmt_id(fmt), 4)
+        assert np.array_equal(a_[:T], kc), f"K codes (chunk {chunk})"
+        assert np.array_equal(b_[:T].view(np.uint16), ks.view(np.uint16)), f"K scales (chunk {chunk})"
+        assert np.array_equal(c_[:T], vc), f"V codes (chunk {chunk})"
+        assert np.array_equal(d_[:T].view(np.uint16), vs.view(np.uint16)), f"V scales (chunk {chunk})"
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_append_bad_page_id_is_skipped_and_flagged(gpu, fmt):
     s = K.shape(fmt)
