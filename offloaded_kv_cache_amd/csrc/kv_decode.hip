@@ -462,8 +462,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 #pragma unroll
   for (int t = 0; t < NTW; ++t) voff[t] = vcode_off<KK, VK>(EPW, wave, lane, t);
   const uint32_t vsoff = vscale_off<KK, VK>(EPW, wave, lane);
-  // a bad page is read from page 0 and then ignored
-  const Rsrc r0 = page_rsrc(base ? base : pool, (int)head_bytes);
+  // a bad page id reads an empty range (zeros, no memory) and is then skipped
+  const Rsrc r0 = base ? page_rsrc(base, (int)head_bytes) : page_rsrc(pool, 0);
   // the K tiles now; the V share after the query's rotation, so that the query math
   // runs while the memory pipeline drains the first burst
   if (!new_first) {
@@ -621,10 +621,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const int valid = page_ok ? min(kPageTokens, T - pg * kPageTokens) : 0;  // tokens in context
     const uint8_t* next = pg + 1 < p_end ? page_base(pg + 1) : nullptr;
 
-    // Next page's loads are issued without a branch (the last page re-reads a
-    // valid page) so that the wait counters before each use stay exact, and each
-    // part is issued as soon as its registers are consumed, to overlap the math.
-    const Rsrc nr = page_rsrc(next ? next : (base ? base : pool), (int)head_bytes);
+    // Next page's loads are issued without a branch so that the wait counters before
+    // each use stay exact, and each part is issued as soon as its registers are
+    // consumed, to overlap the math. After the last page, and for a bad page id, they
+    // are issued against an empty range: they return zeros and read no memory.
+    const Rsrc nr = next ? page_rsrc(next, (int)head_bytes) : page_rsrc(pool, 0);
 
     // ---------------- Q.K of the wave's TPW tokens, wave maximum per head
     float xs[KT][2];
