@@ -64,6 +64,7 @@
 #include <hip/hip_ext.h>
 
 #include "kv_encode.h"
+#include "kv_lanes.h"
 
 namespace kvc {
 namespace {
@@ -134,19 +135,29 @@ __device__ inline uint32_t min_abs_bits_m1(u4 w) {
   return m[0] < m[1] ? m[0] : m[1];
 }
 
-__device__ inline float half_max(float v) {  // max over the 16 lanes of a lane group
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
+__device__ inline float half_max(float v, int lane) {  // max over the 16 lanes of a lane group
+  v = fmaxf(v, xchgf<1>(v, lane));
+  v = fmaxf(v, xchgf<2>(v, lane));
+  v = fmaxf(v, xchgf<4>(v, lane));
+  v = fmaxf(v, xchgf<8>(v, lane));
   return v;
 }
-__device__ inline float half_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+__device__ inline float half_sum(float v, int lane) {
+  v += xchgf<1>(v, lane);
+  v += xchgf<2>(v, lane);
+  v += xchgf<4>(v, lane);
+  v += xchgf<8>(v, lane);
   return v;
+}
+
+// One butterfly stage (bit log2 M) of the Walsh-Hadamard transform on N values per lane.
+template <int M, int N>
+__device__ inline void butterfly(float (&v)[N], int lane) {
+  float o[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) o[i] = xchgf<M>(v[i], lane);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (lane & M) ? (o[i] - v[i]) : (v[i] + o[i]);
 }
 
 // ---- Q.K operands --------------------------------------------------------
@@ -509,15 +520,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   // (all eight head slots are transformed, unused ones hold zeros, so that each step's
   // exchanges are in flight together)
   if (KK == kQ4) {
-#pragma unroll
-    for (int bit = 0; bit < 6; ++bit) {  // butterflies inside the wave
-      const int m = 1 << bit;
-      float o[kMaxGroup];
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) o[hh] = __shfl_xor(qv[hh], m);
-#pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) qv[hh] = (lane & m) ? (o[hh] - qv[hh]) : (qv[hh] + o[hh]);
-    }
+    // butterflies inside the wave
+    butterfly<1>(qv, lane);
+    butterfly<2>(qv, lane);
+    butterfly<4>(qv, lane);
+    butterfly<8>(qv, lane);
+    butterfly<16>(qv, lane);
+    butterfly<32>(qv, lane);
     if (tid < kHeadDim) {
 #pragma unroll
       for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
@@ -643,8 +652,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       kt[t] = load_ktile<KK>(nr, koff[t], ksoff[t]);  // next page's tile t
       __builtin_amdgcn_sched_barrier(0);
     }
-    mx0 = half_max(mx0);
-    mx1 = half_max(mx1);
+    mx0 = half_max(mx0, lane);
+    mx1 = half_max(mx1, lane);
     if (col == 0) {
       lds.wmax[wave][h0] = mx0;
       lds.wmax[wave][h1] = mx1;
@@ -850,7 +859,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   // ---------------- this split's partials: common max, summed weights, each wave's elements
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const float lsum = half_sum(l_run[r]);
+    const float lsum = half_sum(l_run[r], lane);
     if (col == 0) lds.lsum[wave][2 * grp + r] = lsum;
   }
   // the partial of heads 2grp + r at element EPW w + 16t + col (hi + lo rows)
@@ -863,16 +872,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     // V is stored rotated: the partial is rotated back here (H is linear, so the merge of
     // rotated partials is the rotated merge). Element bits 0-3 (col) between lanes,
     // the tile bits inside the lane, the wave bits through LDS.
-#pragma unroll
-    for (int bit = 0; bit < 4; ++bit) {
-      const int m = 1 << bit;
+    {
+      float pv[2 * NTW];
 #pragma unroll
       for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-          const float o = __shfl_xor(po[r][t], m);
-          po[r][t] = (lane & m) ? (o - po[r][t]) : (po[r][t] + o);
-        }
+        for (int t = 0; t < NTW; ++t) pv[NTW * r + t] = po[r][t];
+      butterfly<1>(pv, lane);
+      butterfly<2>(pv, lane);
+      butterfly<4>(pv, lane);
+      butterfly<8>(pv, lane);
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) po[r][t] = pv[NTW * r + t];
     }
 #pragma unroll
     for (int m = 1; m < NTW; m <<= 1)
