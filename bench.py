@@ -298,9 +298,12 @@ def run_streaming(args, dev):
         torch.cuda.synchronize()
     del staging
     log(f"host pool written: {L} layers x {n_pages} pages")
-    slots = [torch.zeros(c["slots"] * pb, dtype=torch.uint8, device=dev) for _ in range(L)]
-    tables = [K.Residency(c["slots"], n_pages) for _ in range(L)]
-    bts = [torch.empty(c["n_sel"], dtype=torch.int32, device=dev) for _ in range(L)]
+    # per-layer tables and slots; the page-in schedule of --gather-mode: "layers" = one
+    # launch pages in all 16 layers' selections, then the layers attend; "serial" = per
+    # layer gather then attention; "overlap" = per-layer gathers on a copy stream
+    sl = K.streaming.StreamedLayers(s, L, c["slots"], n_pages, c["n_sel"], dev,
+                                    overlap=args.gather_mode == "overlap")
+    tables = sl.tables
     ctx_tok = c["n_sel"] * PAGE
     ctx = torch.tensor([ctx_tok], dtype=torch.int32, device=dev)
     ws = K.paged.DecodeWorkspace(s, 1, ctx_tok, 0, device=dev)
@@ -316,26 +319,43 @@ def run_streaming(args, dev):
         fill = rng.permutation(n_pages)[:c["slots"]].astype(np.int32)
         for i in range(0, c["slots"], c["n_sel"]):
             K.gather_pages(s, tables[layer], fill[i:i + c["n_sel"]], host[layer * layer_bytes:(layer + 1) * layer_bytes],
-                           slots[layer], bts[layer], stream=stream)
+                           sl.slots[layer], sl.block_tables[layer], stream=stream)
     torch.cuda.synchronize()
     gather_ev = []
     misses = 0
+    gstream = sl.copy_stream if sl.overlap else stream
+
+    host_layers = [host[layer * layer_bytes:(layer + 1) * layer_bytes] for layer in range(L)]
 
     def step(st, timing):
         nonlocal misses
-        for layer in range(L):
-            sel = streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+        if args.gather_mode == "layers":
+            sels = np.stack([streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+                             for layer in range(L)])
             if timing:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            m = K.gather_pages(s, tables[layer], sel, host[layer * layer_bytes:(layer + 1) * layer_bytes],
-                               slots[layer], bts[layer], stream=stream)
+            m = int(sl.gather_layers(sels, host_layers, stream).sum())
             if timing:
                 e1.record(stream)
                 gather_ev.append((e0, e1, m))
                 misses += m
-            K.decode_attention(s, q_all[st, layer], slots[layer], bts[layer][None], ctx, ctx_tok, out, ws.data,
-                               stream=stream)
+            for layer in range(L):
+                sl.attend(layer, q_all[st, layer], ctx, ctx_tok, out, ws.data, stream)
+            return
+        for layer in range(L):
+            sel = streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+            if timing:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                if sl.overlap:
+                    gstream.wait_event(sl.attended[layer])  # (the gather's own wait, taken first)
+                e0.record(gstream)
+            m = sl.gather(layer, sel, host_layers[layer], stream)
+            if timing:
+                e1.record(gstream)
+                gather_ev.append((e0, e1, m))
+                misses += m
+            sl.attend(layer, q_all[st, layer], ctx, ctx_tok, out, ws.data, stream)
 
     for st in range(args.warmup):
         step(st, False)
@@ -367,14 +387,16 @@ def run_streaming(args, dev):
                         "h2d_pinned_peak_GBs": round(h2d, 2),
                         "miss_rate": round(misses / (args.steps * L * c["n_sel"]), 4),
                         "pages_copied": int(misses), "bytes_copied": int(copied),
-                        "gather_ms_per_step": round(g_ms / args.steps, 4)},
+                        "gather_ms_per_step": round(g_ms / args.steps, 4),
+                        "schedule": args.gather_mode},
                 config={"workload": f"16 layers, {c['host_tokens']:,}-token int8 KV in pinned host memory, "
                                     f"{c['slots']} device slots per layer, {c['n_sel']} selected pages per layer "
                                     f"per step (~{int(c['miss'] * 100)}% misses), CLOCK residency + zero-copy gather "
                                     f"+ attention over the {ctx_tok:,} selected tokens",
                         "layers": L, "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256, "page_tokens": 256,
                         "batch": 1, "kv_format": fmt, "host_tokens": c["host_tokens"], "slots_per_layer": c["slots"],
-                        "selected_pages": c["n_sel"], "miss_probability": c["miss"]})
+                        "selected_pages": c["n_sel"], "miss_probability": c["miss"],
+                        "page_in": args.gather_mode})
 
 
 KERNEL_SRCS = [os.path.join(ROOT, "offloaded_kv_cache_amd", "csrc", f)
@@ -437,7 +459,7 @@ def copy_calibration(args, dev):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 30; 100 for c5)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["c5"])
     ap.add_argument("--host-tokens", type=int, default=C5["host_tokens"],
@@ -450,6 +472,9 @@ def main():
     ap.add_argument("--separate-append", action="store_true",
                     help="append each step's token with its own kernel (kv_append_quantize) before "
                          "kv_decode_attention, instead of the fused kv_append_decode")
+    ap.add_argument("--gather-mode", choices=["layers", "serial", "overlap"], default="layers",
+                    help="streaming workload: one page-in launch for all layers (default), a gather "
+                         "per layer before its attention, or per-layer gathers on a copy stream")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -459,6 +484,8 @@ def main():
                     help="only run a plain device-to-device copy of MIB MiB --steps times "
                          "(reference kernel for calibrating HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 100 if args.workload == "c5" else 30
     if args.kernel_hash:
         print(kernel_code_hash())
         return

@@ -335,6 +335,29 @@ int kv_gather_pages(const kv_shape* shape, kv_residency* table,
                     const void* host_pool, void* slot_pool,
                     int32_t* out_block_table, int32_t* out_n_miss, void* stream);
 
+/*
+ * kv_gather_pages_layers - the page-in of several layers' selections in one
+ * launch (each layer has its own residency table, pools and block table; the
+ * Strata page's streaming step, section "KV 从显存搬进内存之后发生了什么", done
+ * for a whole set of layers whose selections are known together).
+ *
+ * For each layer l: kv_residency_select on tables[l] with the n_sel pages at
+ * selections[l * n_sel] (host int32); then one kernel copies every missing
+ * page of every layer from host_pools[l] (pinned, device-accessible) to its
+ * slot of slot_pools[l] (device), and writes each layer's slot block table to
+ * out_block_tables[l * n_sel .. +n_sel) (device int32 [n_layers][n_sel]).
+ * The result is that of kv_gather_pages called for each layer in turn.
+ *   tables         host array of n_layers tables.
+ *   host_pools, slot_pools  host arrays of n_layers pointers.
+ *   out_n_miss     host int32 [n_layers] or NULL.
+ * All arguments are checked before any table changes. The host pages must not
+ * change until the enqueued copies complete.
+ */
+int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
+                           const int32_t* selections, int32_t n_sel,
+                           const void* const* host_pools, void* const* slot_pools,
+                           int32_t* out_block_tables, int32_t* out_n_miss, void* stream);
+
 /* Host-side helpers of the record rules, exposed so the rounding can be
  * checked without a GPU. Not part of the hot path.
  *   kv_host_f64_to_f16: round a double to fp16 bits once, nearest-even.

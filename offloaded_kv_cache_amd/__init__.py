@@ -11,7 +11,8 @@ not been built (``python offloaded_kv_cache_amd/build.py``).
 from ._native import (  # noqa: F401
     FORMATS, KV_FMT_INT8, KV_FMT_K8V4, KV_FMT_Q4_0, KV_STATUS_BAD_PAGE_ID,
     KV_STATUS_CONTEXT_CLAMPED, KVError, KVShape, Residency, append_decode, append_quantize,
-    decode_attention, decode_split_pages, decode_workspace_bytes, gather_pages, host_encode_vector,
+    decode_attention, decode_split_pages, decode_workspace_bytes, gather_pages, gather_pages_layers,
+    host_encode_vector,
     host_f64_to_f16, last_error, page_bytes, shape, version,
 )
-from . import paged  # noqa: F401
+from . import paged, streaming  # noqa: F401

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed",
-    "kv_decode_combine", "kv_append_decode",
+    "kv_decode_combine", "kv_append_decode", "kv_gather_pages_layers",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
 )
@@ -75,6 +75,8 @@ def _load():
         "kv_residency_select": (C.c_int, [C.POINTER(KVResidency), P, I32, P, P, P, P]),
         "kv_gather_pages": (C.c_int, [C.POINTER(KVShape), C.POINTER(KVResidency), P, I32, P, P, P,
                                       P, P]),
+        "kv_gather_pages_layers": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
+                                             P, P, P, P, P]),
         "kv_host_f64_to_f16": (C.c_uint16, [C.c_double]),
         "kv_host_encode_vector": (C.c_int, [I32, P, P, P]),
     }
@@ -288,6 +290,34 @@ def gather_pages(s: KVShape, table: Residency, selection, host_pool, slot_pool, 
                                _ptr(out_block_table, torch.int32, name="out_block_table"),
                                C.byref(nm), _stream(stream)))
     return nm.value
+
+
+def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, out_block_tables,
+                        stream=None):
+    """kv_gather_pages_layers: CLOCK step of every layer, then one page-in launch for all
+    of them. selections int32 [L, n_sel]; out_block_tables device int32 [L, n_sel].
+    Returns the misses per layer (numpy int32 [L])."""
+    torch = _torch()
+    sel = np.ascontiguousarray(selections, dtype=np.int32)
+    L = len(tables)
+    if sel.ndim != 2 or sel.shape[0] != L or len(host_pools) != L or len(slot_pools) != L:
+        raise ValueError("one selection row, host pool and slot pool per table")
+    if out_block_tables.shape != sel.shape:
+        raise ValueError("out_block_tables must be [n_layers, n_sel]")
+    for h in host_pools:
+        if not h.is_pinned():
+            raise ValueError("host pools must be pinned host memory")
+    arr = (KVResidency * L)(*[t.c for t in tables])
+    hp = (C.c_void_p * L)(*[h.data_ptr() for h in host_pools])
+    sp = (C.c_void_p * L)(*[p.data_ptr() for p in slot_pools])
+    nm = np.zeros(L, np.int32)
+    _check(lib.kv_gather_pages_layers(C.byref(s), L, arr, sel.ctypes.data_as(C.c_void_p), sel.shape[1],
+                                      C.cast(hp, C.c_void_p), C.cast(sp, C.c_void_p),
+                                      _ptr(out_block_tables, torch.int32, name="out_block_tables"),
+                                      nm.ctypes.data_as(C.c_void_p), _stream(stream)))
+    for t, a in zip(tables, arr):  # the tables' arrays are shared; the hand is copied back
+        t.c.hand = a.hand
+    return nm
 
 
 def host_f64_to_f16(x: float) -> int:

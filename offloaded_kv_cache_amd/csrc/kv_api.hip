@@ -411,6 +411,69 @@ int kv_gather_pages(const kv_shape* shape, kv_residency* t, const int32_t* selec
   return ok();
 }
 
+int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
+                           const int32_t* selections, int32_t n_sel, const void* const* host_pools,
+                           void* const* slot_pools, int32_t* out_block_tables, int32_t* out_n_miss,
+                           void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (n_layers < 0 || n_sel < 0) return fail(KV_EINVAL, "negative size");
+  if (n_layers == 0 || n_sel == 0) return ok();
+  if (!tables || !selections || !host_pools || !slot_pools || !out_block_tables)
+    return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(out_block_tables, 4)) return fail(KV_EALIGN, "misaligned block tables (4 B)");
+  // every argument is checked before any table changes
+  for (int32_t l = 0; l < n_layers; ++l) {
+    if (!host_pools[l] || !slot_pools[l]) return fail(KV_EINVAL, "NULL pool of layer %d", l);
+    if (!aligned(host_pools[l], 16) || !aligned(slot_pools[l], 16))
+      return fail(KV_EALIGN, "misaligned pool of layer %d (16 B)", l);
+    int32_t dummy = 0;
+    if (int r = validate_selection(&tables[l], selections + (size_t)l * n_sel, n_sel, &dummy)) return r;
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof attr);
+    hipError_t pe = hipPointerGetAttributes(&attr, host_pools[l]);
+    if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(KV_EINVAL, "host pool of layer %d is not pinned, device-accessible host memory", l);
+    }
+  }
+  const int64_t pb = page_bytes_of(shape);
+  const size_t total = (size_t)n_layers * n_sel;
+  std::vector<int32_t> slots(total), mp(n_sel), ms(n_sel);
+  std::vector<const uint8_t*> src;
+  std::vector<uint8_t*> dst;
+  for (int32_t l = 0; l < n_layers; ++l) {
+    int32_t misses = 0;
+    if (int r = kv_residency_select(&tables[l], selections + (size_t)l * n_sel, n_sel,
+                                    slots.data() + (size_t)l * n_sel, mp.data(), ms.data(), &misses))
+      return r;  // (earlier layers' tables were updated; nothing was enqueued)
+    for (int32_t i = 0; i < misses; ++i) {
+      src.push_back((const uint8_t*)host_pools[l] + (int64_t)mp[i] * pb);
+      dst.push_back((uint8_t*)slot_pools[l] + (int64_t)ms[i] * pb);
+    }
+    if (out_n_miss) out_n_miss[l] = misses;
+  }
+  // launches of at most kMultiMaxCopies copies and kMultiMaxEntries block-table entries
+  size_t done_e = 0, done_c = 0;
+  while (done_e < total || done_c < src.size()) {
+    MultiGatherBatch gb;
+    const size_t ne = total - done_e < (size_t)kMultiMaxEntries ? total - done_e : kMultiMaxEntries;
+    const size_t nc = src.size() - done_c < (size_t)kMultiMaxCopies ? src.size() - done_c : kMultiMaxCopies;
+    gb.n_entries = (int32_t)ne;
+    gb.n_copies = (int32_t)nc;
+    gb.block_tables = out_block_tables + done_e;
+    for (size_t i = 0; i < ne; ++i) gb.slots[i] = slots[done_e + i];
+    for (size_t i = 0; i < nc; ++i) {
+      gb.src[i] = src[done_c + i];
+      gb.dst[i] = dst[done_c + i];
+    }
+    hipError_t e = launch_gather_multi(gb, pb, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gather launch (the residency tables were already updated)");
+    done_e += ne;
+    done_c += nc;
+  }
+  return ok();
+}
+
 uint16_t kv_host_f64_to_f16(double x) { return f64_to_f16_rne(x); }
 
 int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales) {

@@ -48,7 +48,38 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(GatherBatch batch, int
   }
 }
 
+// The same copy for a list of (source page, destination slot) pairs of any layers.
+__global__ __launch_bounds__(kThreads) void gather_multi_kernel(MultiGatherBatch batch, int64_t page_bytes) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < batch.n_entries; i += kThreads) batch.block_tables[i] = batch.slots[i];
+  }
+  if ((int)blockIdx.y >= batch.n_copies) return;
+  const u4* src = reinterpret_cast<const u4*>(batch.src[blockIdx.y]);
+  u4* dst = reinterpret_cast<u4*>(batch.dst[blockIdx.y]);
+  const int64_t n16 = page_bytes / 16;
+  const int64_t first = (int64_t)blockIdx.x * (kChunk / 16);
+  u4 buf[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = first + (int64_t)u * kThreads + tid;
+    if (i < n16) buf[u] = __builtin_nontemporal_load(src + i);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t i = first + (int64_t)u * kThreads + tid;
+    if (i < n16) dst[i] = buf[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_multi(const MultiGatherBatch& batch, int64_t page_bytes, hipStream_t stream) {
+  const unsigned chunks = (unsigned)((page_bytes + kChunk - 1) / kChunk);
+  dim3 grid(chunks, (unsigned)(batch.n_copies > 0 ? batch.n_copies : 1)), block(kThreads);
+  hipLaunchKernelGGL(gather_multi_kernel, grid, block, 0, stream, batch, page_bytes);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather(const GatherBatch& batch, int64_t page_bytes, const uint8_t* host_pool,
                          uint8_t* slot_pool, int32_t* out_block_table, hipStream_t stream) {

@@ -138,6 +138,22 @@ struct GatherBatch {
   int32_t miss_slot[kGatherMaxBatch];   // destination slots
 };
 
+// Page copies of several layers in one launch (kernel arguments): each copy has its
+// own source (pinned host page) and destination (device slot); the block tables of all
+// layers are one device array [n_layers][n_sel].
+constexpr int kMultiMaxCopies = 96;
+constexpr int kMultiMaxEntries = 256;  // block-table entries per launch
+struct MultiGatherBatch {
+  int32_t n_copies;
+  int32_t n_entries;                       // block-table entries written by this launch
+  int32_t* block_tables;                   // where entry 0 of this launch goes
+  const uint8_t* src[kMultiMaxCopies];
+  uint8_t* dst[kMultiMaxCopies];
+  int32_t slots[kMultiMaxEntries];
+};
+
+hipError_t launch_gather_multi(const MultiGatherBatch& batch, int64_t page_bytes, hipStream_t stream);
+
 hipError_t launch_gather(const GatherBatch& batch, int64_t page_bytes, const uint8_t* host_pool,
                          uint8_t* slot_pool, int32_t* out_block_table, hipStream_t stream);
 

@@ -96,3 +96,107 @@ def test_gather_refuses_unpinned_host_memory(gpu):
     bt = torch.empty(2, dtype=torch.int32, device=gpu)
     with pytest.raises(ValueError):
         K.gather_pages(s, table, [0, 1], host, slots, bt)
+
+
+def draw_selections(L, n_pages, n_slots, n_sel, steps, seed):
+    """One selection per (step, layer) with a mix of hits and misses, drawn from shadow
+    CLOCK tables that make the same decisions as the library's."""
+    rng = np.random.default_rng(seed)
+    shadows = [ClockTable(n_slots, n_pages) for _ in range(L)]
+    sels = []
+    for st in range(steps):
+        row = []
+        for layer in range(L):
+            res = [p for p in shadows[layer].slot_page if p >= 0]
+            if res and st > 0:
+                k = min(len(res), n_sel - 3)
+                pick = list(rng.choice(res, k, replace=False))
+                non = [p for p in range(n_pages) if p not in res]
+                pick += list(rng.choice(non, n_sel - k, replace=False))
+            else:
+                pick = list(rng.choice(n_pages, n_sel, replace=False))
+            sel = np.array(pick, np.int32)
+            shadows[layer].select(sel)
+            row.append(sel)
+        sels.append(row)
+    return sels
+
+
+@pytest.mark.parametrize("fmt", ["int8", "k8v4"])
+def test_gather_layers_equals_per_layer_gathers(gpu, fmt):
+    """kv_gather_pages_layers (one launch for every layer) leaves the same tables, slots
+    and block tables as kv_gather_pages per layer, and attention over them is identical."""
+    L, n_pages, n_slots, n_sel, steps = 4, 30, 10, 8, 4
+    s = K.shape(fmt)
+    seqs = [Sequence(35, layer, 0, n_pages * 256, fmt) for layer in range(L)]
+    host = [torch.from_numpy(sq.pages.reshape(-1).copy()).pin_memory() for sq in seqs]
+    sels = draw_selections(L, n_pages, n_slots, n_sel, steps, 6)
+    q = to_dev(kvsynth.q_np(35, 0, steps * L).reshape(steps, L, 1, 24, 256), gpu)
+    ctx = to_dev(np.array([n_sel * 256], np.int32), gpu)
+    runs = []
+    for batched in (False, True):
+        sl = K.streaming.StreamedLayers(s, L, n_slots, n_pages, n_sel, gpu)
+        stream = torch.cuda.current_stream()
+        ws = K.paged.DecodeWorkspace(s, 1, n_sel * 256, 0, device=gpu)
+        out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+        keep = torch.empty((steps, L, 24, 256), dtype=torch.float32, device=gpu)
+        bts, miss = [], []
+        for st in range(steps):
+            if batched:
+                miss.append(list(sl.gather_layers(np.stack(sels[st]), host, stream)))
+            else:
+                miss.append([sl.gather(layer, sels[st][layer], host[layer], stream) for layer in range(L)])
+            bts.append(sl.block_table_all.cpu().numpy().copy())
+            for layer in range(L):
+                sl.attend(layer, q[st, layer], ctx, n_sel * 256, out, ws.data, stream)
+                keep[st, layer].copy_(out[0])
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        runs.append((keep.cpu().numpy(), bts, miss, [t.slot_page.copy() for t in sl.tables],
+                     [t.hand for t in sl.tables], [x.cpu().numpy() for x in sl.slots]))
+    a, b = runs
+    assert a[2] == b[2], "misses per layer"
+    assert all(np.array_equal(x, y) for x, y in zip(a[1], b[1])), "block tables"
+    assert all(np.array_equal(x, y) for x, y in zip(a[3], b[3])) and a[4] == b[4], "residency tables"
+    assert all(np.array_equal(x, y) for x, y in zip(a[5], b[5])), "slot contents"
+    assert np.array_equal(a[0], b[0]), "attention outputs"
+    assert sum(sum(m) for m in a[2]) > 0
+
+
+@pytest.mark.parametrize("fmt", ["int8", "q4_0"])
+def test_overlapped_streaming_equals_serial(gpu, fmt):
+    """Each layer's gather on a copy stream, overlapped with the attention of earlier
+    layers (and of the previous step), gives bit for bit the outputs of the same calls
+    serialized on one stream."""
+    L, n_pages, n_slots, n_sel, steps = 3, 40, 12, 8, 5
+    s = K.shape(fmt)
+    seqs = [Sequence(34, layer, 0, n_pages * 256, fmt) for layer in range(L)]
+    host = [torch.from_numpy(sq.pages.reshape(-1).copy()).pin_memory() for sq in seqs]
+    sels = draw_selections(L, n_pages, n_slots, n_sel, steps, 5)
+    q = to_dev(kvsynth.q_np(34, 0, steps * L).reshape(steps, L, 1, 24, 256), gpu)
+    ctx = to_dev(np.array([n_sel * 256], np.int32), gpu)
+    results = []
+    for overlap in (False, True):
+        sl = K.streaming.StreamedLayers(s, L, n_slots, n_pages, n_sel, gpu, overlap=overlap)
+        stream = torch.cuda.current_stream()
+        ws = K.paged.DecodeWorkspace(s, 1, n_sel * 256, 0, device=gpu)
+        out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+        keep = torch.empty((steps, L, 24, 256), dtype=torch.float32, device=gpu)
+        for st in range(steps):
+            for layer in range(L):
+                sl.gather(layer, sels[st][layer], host[layer], stream)
+                sl.attend(layer, q[st, layer], ctx, n_sel * 256, out, ws.data, stream)
+                keep[st, layer].copy_(out[0])
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        results.append(keep.cpu().numpy())
+    assert np.array_equal(results[0], results[1])
+    # and the outputs are those of attention over the selected pages
+    for st in (0, steps - 1):
+        for layer in range(L):
+            sel = sels[st][layer]
+            k = np.concatenate([seqs[layer].k[256 * p:256 * p + 256] for p in sel])
+            v = np.concatenate([seqs[layer].v[256 * p:256 * p + 256] for p in sel])
+            sub = Sequence(34, layer, 0, n_sel * 256, fmt, k=k, v=v)
+            assert_close(results[1][st, layer][None], oracle_out(q[st, layer].cpu().numpy(), [sub], fmt),
+                         what=f"step {st} layer {layer}")
