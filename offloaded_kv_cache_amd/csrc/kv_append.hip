@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void append_kernel(
   if (in) {
     const size_t src = (size_t)(t - start) * stride + (size_t)h * kHeadDim;
     if (!is_v) {
-      enc::encode<KK>(k + src, lane, code, scale);
+      enc::encode<KK, false>(k + src, lane, code, scale);  // many vectors: LDS lane exchanges
       enc::write_k_row<KK>(kplane, row, lane, code, scale);
     } else {
-      enc::encode<VK>(v + src, lane, code, scale);
+      enc::encode<VK, false>(v + src, lane, code, scale);
       enc::write_v_scales<VK>(vplane, row, lane, scale);
       if (VK == kInt8) {
 #pragma unroll

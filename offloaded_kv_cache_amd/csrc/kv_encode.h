@@ -21,39 +21,52 @@ namespace kvc {
 namespace enc {
 
 // One butterfly stage (bit log2 M) and one max stage on the lane's four values.
-template <int M>
+// Two forms of the encoder, with identical results. DPP = true (a lone vector, latency
+// bound): DPP selects and lane swaps, branch-free rounding, division-free codes.
+// DPP = false (many vectors at once, VALU-throughput bound): lane exchanges through the
+// LDS crossbar (no VALU instructions), and the plain rounding and code rules of
+// kv_internal.h (fewer instructions when most lanes take the same branch).
+template <int M, bool DPP>
+__device__ inline double xchg_enc(double v, int lane) {
+  if (DPP) return xchg64<M>(v, lane);
+  return __shfl_xor(v, M);
+}
+
+template <int M, bool DPP>
 __device__ inline void wht_stage(double (&y)[4], int lane) {
   const bool upper = lane & M;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const double o = xchg64<M>(y[k], lane);
+    const double o = xchg_enc<M, DPP>(y[k], lane);
     y[k] = upper ? (o - y[k]) : (y[k] + o);
   }
 }
-template <int M>
+template <int M, bool DPP>
 __device__ inline void max_stage(double (&v)[4], int lane) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], xchg64<M>(v[k], lane));
+  for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], xchg_enc<M, DPP>(v[k], lane));
 }
 
 // Maximum over the wave of each of the lane's four values.
+template <bool DPP>
 __device__ inline void wave_max4(double (&v)[4], int lane) {
-  max_stage<1>(v, lane);
-  max_stage<2>(v, lane);
-  max_stage<4>(v, lane);
-  max_stage<8>(v, lane);
-  max_stage<16>(v, lane);
-  max_stage<32>(v, lane);
+  max_stage<1, DPP>(v, lane);
+  max_stage<2, DPP>(v, lane);
+  max_stage<4, DPP>(v, lane);
+  max_stage<8, DPP>(v, lane);
+  max_stage<16, DPP>(v, lane);
+  max_stage<32, DPP>(v, lane);
 }
 
 // Exact y = H x on the lane's four elements.
+template <bool DPP>
 __device__ inline void wht256(double (&y)[4], int lane) {
-  wht_stage<1>(y, lane);
-  wht_stage<2>(y, lane);
-  wht_stage<4>(y, lane);
-  wht_stage<8>(y, lane);
-  wht_stage<16>(y, lane);
-  wht_stage<32>(y, lane);
+  wht_stage<1, DPP>(y, lane);
+  wht_stage<2, DPP>(y, lane);
+  wht_stage<4, DPP>(y, lane);
+  wht_stage<8, DPP>(y, lane);
+  wht_stage<16, DPP>(y, lane);
+  wht_stage<32, DPP>(y, lane);
   const double a0 = y[0] + y[1], a1 = y[0] - y[1];  // bit 6
   const double a2 = y[2] + y[3], a3 = y[2] - y[3];
   y[0] = (a0 + a2) * 0.0625;                          // bit 7, then 1/16
@@ -105,7 +118,7 @@ __device__ inline int q4_code_fast(double y, double d) {
 // int8: scale[k] is group k (elements 64k..64k+63 are exactly register k).
 // q4: scale of block (lane >> 5) + 2k lives in register k of every lane of
 // that half-wave.
-template <int KIND>
+template <int KIND, bool DPP = true>
 __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code)[4],
                                    uint16_t (&scale)[4]) {
   double x[4];
@@ -115,24 +128,25 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
     double a[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
-    wave_max4(a, lane);
+    wave_max4<DPP>(a, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      scale[k] = f64_to_f16_fast(a[k] / 127.0);
-      code[k] = int8_code_fast(x[k], f16_to_f64(scale[k]));
+      scale[k] = DPP ? f64_to_f16_fast(a[k] / 127.0) : f64_to_f16_rne(a[k] / 127.0);
+      const double d = f16_to_f64(scale[k]);
+      code[k] = DPP ? int8_code_fast(x[k], d) : int8_code(x[k], d);
     }
   } else {
-    wht256(x, lane);
+    wht256<DPP>(x, lane);
     // per block (the 32 lanes of a half-wave, register k): largest |y|, then the
     // first element holding it, then its signed value
     double m[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
-    max_stage<1>(m, lane);
-    max_stage<2>(m, lane);
-    max_stage<4>(m, lane);
-    max_stage<8>(m, lane);
-    max_stage<16>(m, lane);
+    max_stage<1, DPP>(m, lane);
+    max_stage<2, DPP>(m, lane);
+    max_stage<4, DPP>(m, lane);
+    max_stage<8, DPP>(m, lane);
+    max_stage<16, DPP>(m, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint64_t hit = __ballot(fabs(x[k]) == m[k]);
@@ -146,8 +160,9 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
                      h1 = __builtin_amdgcn_readlane((uint32_t)(xb >> 32), i_hi);
       const uint32_t sel = (lane & 32) ? ~0u : 0u;
       const double best = __builtin_bit_cast(double, ((uint64_t)(h0 ^ ((h0 ^ h1) & sel)) << 32) | (l0 ^ ((l0 ^ l1) & sel)));
-      scale[k] = f64_to_f16_fast(-best * 0.125);  // -m/8 is exact in fp64
-      code[k] = q4_code_fast(x[k], f16_to_f64(scale[k]));
+      scale[k] = DPP ? f64_to_f16_fast(-best * 0.125) : f64_to_f16_rne(-best * 0.125);  // -m/8 exact
+      const double d = f16_to_f64(scale[k]);
+      code[k] = DPP ? q4_code_fast(x[k], d) : q4_code(x[k], d);
     }
   }
 }
@@ -158,12 +173,12 @@ __device__ inline void load_vals(const uint16_t* __restrict__ src, int lane, uin
   for (int k = 0; k < 4; ++k) in[k] = src[lane + 64 * k];
 }
 
-template <int KIND>
+template <int KIND, bool DPP>
 __device__ inline void encode(const uint16_t* __restrict__ src, int lane, int (&code)[4],
                               uint16_t (&scale)[4]) {
   uint16_t in[4];
   load_vals(src, lane, in);
-  encode_vals<KIND>(in, lane, code, scale);
+  encode_vals<KIND, DPP>(in, lane, code, scale);
 }
 
 // K plane row of a token (token-major, slice-permuted code bytes).
