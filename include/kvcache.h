@@ -358,6 +358,40 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
                            const void* const* host_pools, void* const* slot_pools,
                            int32_t* out_block_tables, int32_t* out_n_miss, void* stream);
 
+/*
+ * Page selection for streaming mode (KV-offload news page, section
+ * "新招不是全搬，而是分层放": attention over a fixed budget of selected tokens,
+ * whose selection rule the page does not give; this library declares the
+ * plain rule below). All arithmetic is on exact integers, so the result does
+ * not depend on summation order and is the same on every call.
+ *
+ * kv_page_key_sums - adds tokens [start_pos, start_pos + n_tokens) of one
+ * sequence to its per-page key sums:
+ *   sums[p][g][e] += k[t][g][e] * 2^24 for every token t of logical page p
+ * (fp16 keys are integer multiples of 2^-24, so each term is an exact integer;
+ * a page's sum stays below 2^48).
+ *   k       device fp16 [n_tokens][n_kv_heads][256] (the keys as appended).
+ *   sums    device int64 [n_pages_cap][n_kv_heads][256], zero before the
+ *           first token of each page is added. Atomic adds: calls may overlap.
+ *
+ * kv_select_pages - the pages one step attends (per sequence and layer):
+ *   score[p] = sum over KV heads g and elements e of
+ *              (sum over g's query heads h of q[h][e] * 2^24) * sums[p][g][e]
+ * (an exact 128-bit integer); the selection is the last page (p = n_pages - 1,
+ * the newest tokens) and the k_sel - 1 other pages of largest score, ties to
+ * the lower page index, written in ascending order to out_selection (device
+ * int32 [min(k_sel, n_pages)]); with n_pages <= k_sel, every page.
+ *   q          device fp16 [n_q_heads][256] (the step's query of the sequence).
+ *   n_pages    pages of the context (<= 32768); k_sel in 1..256.
+ *   workspace  device, >= kv_select_workspace_bytes(n_pages) bytes, 16-B aligned.
+ */
+int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,
+                     int64_t* sums, int64_t n_pages_cap, void* stream);
+size_t kv_select_workspace_bytes(int64_t n_pages);
+int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t n_pages,
+                    int32_t k_sel, int32_t* out_selection, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Host-side helpers of the record rules, exposed so the rounding can be
  * checked without a GPU. Not part of the hot path.
  *   kv_host_f64_to_f16: round a double to fp16 bits once, nearest-even.

@@ -13,6 +13,7 @@ from ._native import (  # noqa: F401
     KV_STATUS_CONTEXT_CLAMPED, KVError, KVShape, Residency, append_decode, append_quantize,
     decode_attention, decode_split_pages, decode_workspace_bytes, gather_pages, gather_pages_layers,
     host_encode_vector,
-    host_f64_to_f16, last_error, page_bytes, shape, version,
+    host_f64_to_f16, last_error, page_bytes, page_key_sums, select_pages, select_workspace_bytes, shape,
+    version,
 )
 from . import paged, streaming  # noqa: F401

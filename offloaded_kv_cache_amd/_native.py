@@ -25,7 +25,8 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed",
-    "kv_decode_combine", "kv_append_decode", "kv_gather_pages_layers",
+    "kv_decode_combine", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
+    "kv_select_workspace_bytes", "kv_select_pages",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
 )
@@ -77,6 +78,9 @@ def _load():
                                       P, P]),
         "kv_gather_pages_layers": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
                                              P, P, P, P, P]),
+        "kv_page_key_sums": (C.c_int, [C.POINTER(KVShape), P, I64, I64, P, I64, P]),
+        "kv_select_workspace_bytes": (SZ, [I64]),
+        "kv_select_pages": (C.c_int, [C.POINTER(KVShape), P, P, I64, I32, P, P, SZ, P]),
         "kv_host_f64_to_f16": (C.c_uint16, [C.c_double]),
         "kv_host_encode_vector": (C.c_int, [I32, P, P, P]),
     }
@@ -318,6 +322,38 @@ def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, 
     for t, a in zip(tables, arr):  # the tables' arrays are shared; the hand is copied back
         t.c.hand = a.hand
     return nm
+
+
+def page_key_sums(s: KVShape, k, start_pos: int, sums, stream=None):
+    """kv_page_key_sums: add keys k (fp16 [n, n_kv_heads, 256]) of tokens start_pos.. to
+    sums (device int64 [n_pages_cap, n_kv_heads, 256])."""
+    torch = _torch()
+    if k.dim() != 3 or k.shape[1:] != (s.n_kv_heads, s.head_dim):
+        raise ValueError("k must be [n_tokens, n_kv_heads, head_dim]")
+    if sums.dim() != 3 or sums.shape[1:] != (s.n_kv_heads, s.head_dim):
+        raise ValueError("sums must be [n_pages_cap, n_kv_heads, head_dim]")
+    _check(lib.kv_page_key_sums(C.byref(s), _ptr(k, torch.float16, name="k"), k.shape[0], start_pos,
+                                _ptr(sums, torch.int64, name="sums"), sums.shape[0], _stream(stream)))
+
+
+def select_workspace_bytes(n_pages: int) -> int:
+    nb = lib.kv_select_workspace_bytes(n_pages)
+    if nb == 0:
+        raise KVError(-1, last_error())
+    return nb
+
+
+def select_pages(s: KVShape, q, sums, n_pages: int, k_sel: int, out_selection, workspace, stream=None):
+    """kv_select_pages: the step's pages (ascending) into out_selection (device int32)."""
+    torch = _torch()
+    if q.shape != (s.n_q_heads, s.head_dim):
+        raise ValueError("q must be [n_q_heads, head_dim]")
+    if out_selection.numel() < min(k_sel, n_pages):
+        raise ValueError("out_selection too small")
+    _check(lib.kv_select_pages(C.byref(s), _ptr(q, torch.float16, name="q"), _ptr(sums, torch.int64, name="sums"),
+                               n_pages, k_sel, _ptr(out_selection, torch.int32, name="out_selection"),
+                               C.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                               _stream(stream)))
 
 
 def host_f64_to_f16(x: float) -> int:

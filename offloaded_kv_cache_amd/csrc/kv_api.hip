@@ -474,6 +474,51 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
   return ok();
 }
 
+int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,
+                     int64_t* sums, int64_t n_pages_cap, void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (n_tokens < 0 || start_pos < 0) return fail(KV_EINVAL, "negative token count or position");
+  if (n_tokens == 0) return ok();
+  if (!k || !sums) return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(k, 2) || !aligned(sums, 8)) return fail(KV_EALIGN, "misaligned buffer (k: 2 B, sums: 8 B)");
+  if ((start_pos + n_tokens - 1) / kPageTokens >= n_pages_cap)
+    return fail(KV_EINVAL, "tokens up to position %lld need more than %lld pages of sums",
+                (long long)(start_pos + n_tokens - 1), (long long)n_pages_cap);
+  hipError_t e = launch_key_sums(shape->n_kv_heads, (const uint16_t*)k, n_tokens, start_pos, sums,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "key-sum launch");
+  return ok();
+}
+
+size_t kv_select_workspace_bytes(int64_t n_pages) {
+  if (n_pages < 0 || n_pages > select_max_pages()) {
+    fail(KV_EINVAL, "n_pages out of range (0..%d)", select_max_pages());
+    return 0;
+  }
+  ok();
+  return (size_t)(n_pages > 0 ? n_pages : 1) * 16;
+}
+
+int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t n_pages,
+                    int32_t k_sel, int32_t* out_selection, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (int r = check_shape(shape)) return r;
+  if (n_pages < 0 || n_pages > select_max_pages())
+    return fail(KV_EINVAL, "n_pages out of range (0..%d)", select_max_pages());
+  if (k_sel < 1 || k_sel > select_max_k()) return fail(KV_EINVAL, "k_sel out of range (1..%d)", select_max_k());
+  if (n_pages == 0) return ok();
+  if (!q || !sums || !out_selection || !workspace) return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(q, 2) || !aligned(sums, 8) || !aligned(out_selection, 4) || !aligned(workspace, 16))
+    return fail(KV_EALIGN, "misaligned buffer (q: 2 B, sums: 8 B, selection: 4 B, workspace: 16 B)");
+  if (workspace_bytes < (size_t)n_pages * 16)
+    return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                (size_t)n_pages * 16);
+  hipError_t e = launch_select(shape->n_q_heads, shape->n_kv_heads, (const uint16_t*)q, sums, (int)n_pages,
+                               k_sel, out_selection, workspace, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "selection launch");
+  return ok();
+}
+
 uint16_t kv_host_f64_to_f16(double x) { return f64_to_f16_rne(x); }
 
 int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales) {

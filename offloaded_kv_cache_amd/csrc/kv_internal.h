@@ -128,6 +128,14 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
+// Page selection (kv_select.hip).
+hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
+                           int64_t* sums, hipStream_t stream);
+hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const int64_t* sums,
+                         int n_pages, int k_sel, int32_t* out, void* scores, hipStream_t stream);
+int select_max_pages();
+int select_max_k();
+
 constexpr int kGatherMaxBatch = 256;  // selections per gather launch (kernel-argument size)
 
 struct GatherBatch {

@@ -1,0 +1,93 @@
+"""GPU page selection (kv_page_key_sums, kv_select_pages) against the oracle's
+declared rule (oracle/selection.py): key sums and selections bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import offloaded_kv_cache_amd as K
+from oracle import selection as osel
+
+pytestmark = pytest.mark.gpu
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def gpu_sums(gpu, s, k, chunks, cap):
+    sums = torch.zeros((cap, s.n_kv_heads, 256), dtype=torch.int64, device=gpu)
+    kd = to_dev(k, gpu)
+    t = 0
+    for n in chunks:
+        K.page_key_sums(s, kd[t:t + n].contiguous(), t, sums)
+        t += n
+    assert t == k.shape[0]
+    return sums
+
+
+def gpu_select(gpu, s, q, sums, n_pages, k_sel):
+    ws = torch.empty(K.select_workspace_bytes(n_pages), dtype=torch.uint8, device=gpu)
+    out = torch.full((max(1, min(k_sel, n_pages)),), -1, dtype=torch.int32, device=gpu)
+    K.select_pages(s, to_dev(q, gpu), sums, n_pages, k_sel, out, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()[:min(k_sel, n_pages)].tolist()
+
+
+@pytest.mark.parametrize("T, chunks", [(1, [1]), (700, [1, 17, 300, 382]), (4096, [4096]),
+                                       (10000, [2048] * 4 + [1808])])
+def test_key_sums_bitexact(gpu, T, chunks):
+    s = K.shape("q4_0")
+    k, _ = kvsynth.kv_tokens_np(41, 0, 0, 0, T)
+    cap = -(-T // 256) + 2
+    got = gpu_sums(gpu, s, k, chunks, cap).cpu().numpy()
+    want = osel.key_sums(k, cap)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("T", [256, 700, 8192, 65536 + 100])
+@pytest.mark.parametrize("k_sel", [1, 3, 8, 32])
+def test_selection_matches_oracle(gpu, T, k_sel):
+    s = K.shape("int8")
+    k, _ = kvsynth.kv_tokens_np(42, 0, 0, 0, T)
+    n = -(-T // 256)
+    sums = gpu_sums(gpu, s, k, [T], n)
+    for step in range(3):
+        q = kvsynth.q_np(42, step, 1)[0]
+        want = osel.select_pages(osel.page_scores(q, sums.cpu().numpy()), k_sel)
+        assert want == osel.select(q, k, k_sel)
+        assert gpu_select(gpu, s, q, sums, n, k_sel) == want, (T, k_sel, step)
+
+
+def test_selection_ties_and_forced_last_page(gpu):
+    """Pages with equal key sums: the lower page wins; the last page is always taken."""
+    s = K.shape("q4_0")
+    c = [1.0, 4.0, -2.0, 4.0, 3.0, 4.0, -8.0]
+    k = np.zeros((256 * len(c), 4, 256), np.float16)
+    for p, v in enumerate(c):
+        k[256 * p:256 * p + 256, :, 0] = v
+    q = np.zeros((24, 256), np.float16)
+    q[:, 0] = 1.0
+    sums = gpu_sums(gpu, s, k, [k.shape[0]], len(c))
+    for k_sel in (1, 2, 3, 4, 7, 9):
+        want = osel.select(q, k, k_sel)
+        assert gpu_select(gpu, s, q, sums, len(c), k_sel) == want, k_sel
+    assert osel.select(q, k, 3) == [1, 3, 6]
+
+
+def test_selection_over_a_million_tokens(gpu):
+    """4,096 pages (the streaming workload's host pool per layer), the 2,048-token budget."""
+    s = K.shape("int8")
+    T = 1 << 20
+    gen = torch.Generator(device=gpu)
+    gen.manual_seed(kvsynth.torch_seed(5, 0))
+    gain = kvsynth.gain_torch(5, 0, 4, gpu)
+    sums = torch.zeros((T // 256, 4, 256), dtype=torch.int64, device=gpu)
+    for t0 in range(0, T, 65536):
+        kd, _ = kvsynth.kv_tokens_torch(gen, 65536, gain, gpu)
+        K.page_key_sums(s, kd, t0, sums)
+    q = kvsynth.q_np(43, 0, 1)[0]
+    got = gpu_select(gpu, s, q, sums, T // 256, 8)
+    want = osel.select_pages(osel.page_scores(q, sums.cpu().numpy()), 8)
+    assert got == want and got[-1] == T // 256 - 1
