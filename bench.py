@@ -287,6 +287,10 @@ def run_streaming(args, dev):
     host = torch.empty(L * layer_bytes, dtype=torch.uint8, pin_memory=True)
     staging = K.paged.PagedPool(fmt, n_pages, device=dev)
     ident = torch.arange(n_pages, dtype=torch.int32, device=dev)
+    qsa = args.selection == "qsa"
+    if qsa and args.gather_mode != "layers":
+        raise SystemExit("--selection qsa chooses every layer's pages at once: use --gather-mode layers")
+    key_sums = torch.zeros((L, n_pages, 4, 256), dtype=torch.int64, device=dev) if qsa else None
     for layer in range(L):
         gen = torch.Generator(device=dev)
         gen.manual_seed(kvsynth.torch_seed(cfg, layer))
@@ -294,6 +298,8 @@ def run_streaming(args, dev):
         for t0 in range(0, c["host_tokens"], 2048):
             k, v = kvsynth.kv_tokens_torch(gen, 2048, gain, dev)
             staging.append(k, v, t0, ident)
+            if qsa:
+                K.page_key_sums(s, k, t0, key_sums[layer])
         host[layer * layer_bytes:(layer + 1) * layer_bytes].copy_(staging.data)
         torch.cuda.synchronize()
     del staging
@@ -326,12 +332,30 @@ def run_streaming(args, dev):
     gstream = sl.copy_stream if sl.overlap else stream
 
     host_layers = [host[layer * layer_bytes:(layer + 1) * layer_bytes] for layer in range(L)]
+    sel_dev = torch.empty((L, c["n_sel"]), dtype=torch.int32, device=dev)
+    sel_ws = torch.empty(K.select_workspace_bytes(n_pages, L), dtype=torch.uint8, device=dev)
+    select_ev = []
+
+    def choose(st, timing):
+        """Every layer's selection for step st: random with the workload's miss rate, or the
+        GPU page selection from each layer's query (copied to the host for the CLOCK step)."""
+        if not qsa:
+            return np.stack([streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+                             for layer in range(L)])
+        if timing:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        # one call selects for all 16 layers (each from its own query and key sums)
+        K.select_pages(s, q_all[st, :, 0], key_sums, n_pages, c["n_sel"], sel_dev, sel_ws, stream=stream)
+        if timing:
+            e1.record(stream)
+            select_ev.append((e0, e1))
+        return sel_dev.cpu().numpy()
 
     def step(st, timing):
         nonlocal misses
         if args.gather_mode == "layers":
-            sels = np.stack([streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
-                             for layer in range(L)])
+            sels = choose(st, timing)
             if timing:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -388,7 +412,10 @@ def run_streaming(args, dev):
                         "miss_rate": round(misses / (args.steps * L * c["n_sel"]), 4),
                         "pages_copied": int(misses), "bytes_copied": int(copied),
                         "gather_ms_per_step": round(g_ms / args.steps, 4),
-                        "schedule": args.gather_mode},
+                        "schedule": args.gather_mode,
+                        "selection": args.selection,
+                        "selection_ms_per_step": round(sum(a.elapsed_time(b) for a, b in select_ev) / args.steps, 4)
+                        if select_ev else None},
                 config={"workload": f"16 layers, {c['host_tokens']:,}-token int8 KV in pinned host memory, "
                                     f"{c['slots']} device slots per layer, {c['n_sel']} selected pages per layer "
                                     f"per step (~{int(c['miss'] * 100)}% misses), CLOCK residency + zero-copy gather "
@@ -475,6 +502,9 @@ def main():
     ap.add_argument("--gather-mode", choices=["layers", "serial", "overlap"], default="layers",
                     help="streaming workload: one page-in launch for all layers (default), a gather "
                          "per layer before its attention, or per-layer gathers on a copy stream")
+    ap.add_argument("--selection", choices=["random", "qsa"], default="random",
+                    help="streaming workload: pages drawn at random with the set miss rate, or chosen on "
+                         "the GPU from each layer's query and per-page key sums (kv_select_pages)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

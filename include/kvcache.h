@@ -374,23 +374,26 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
  *   sums    device int64 [n_pages_cap][n_kv_heads][256], zero before the
  *           first token of each page is added. Atomic adds: calls may overlap.
  *
- * kv_select_pages - the pages one step attends (per sequence and layer):
+ * kv_select_pages - the pages one step attends, for n_sets independent sets
+ * (layers, or sequences of equal page count) in one call. For set i:
  *   score[p] = sum over KV heads g and elements e of
- *              (sum over g's query heads h of q[h][e] * 2^24) * sums[p][g][e]
+ *              (sum over g's query heads h of q[i][h][e] * 2^24) * sums[i][p][g][e]
  * (an exact 128-bit integer); the selection is the last page (p = n_pages - 1,
  * the newest tokens) and the k_sel - 1 other pages of largest score, ties to
- * the lower page index, written in ascending order to out_selection (device
- * int32 [min(k_sel, n_pages)]); with n_pages <= k_sel, every page.
- *   q          device fp16 [n_q_heads][256] (the step's query of the sequence).
+ * the lower page index, written in ascending order to out_selection[i] (device
+ * int32 [n_sets][k_sel]; the first min(k_sel, n_pages) entries); with
+ * n_pages <= k_sel, every page.
+ *   q          device fp16 [n_sets][n_q_heads][256] (each set's query).
+ *   sums       device int64 [n_sets][sums_pages][n_kv_heads][256], sums_pages >= n_pages.
  *   n_pages    pages of the context (<= 32768); k_sel in 1..256.
- *   workspace  device, >= kv_select_workspace_bytes(n_pages) bytes, 16-B aligned.
+ *   workspace  device, >= kv_select_workspace_bytes(n_pages, n_sets) bytes, 16-B aligned.
  */
 int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,
                      int64_t* sums, int64_t n_pages_cap, void* stream);
-size_t kv_select_workspace_bytes(int64_t n_pages);
-int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t n_pages,
-                    int32_t k_sel, int32_t* out_selection, void* workspace, size_t workspace_bytes,
-                    void* stream);
+size_t kv_select_workspace_bytes(int64_t n_pages, int32_t n_sets);
+int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t sums_pages,
+                    int64_t n_pages, int32_t k_sel, int32_t n_sets, int32_t* out_selection,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-side helpers of the record rules, exposed so the rounding can be
  * checked without a GPU. Not part of the hot path.

@@ -79,8 +79,8 @@ def _load():
         "kv_gather_pages_layers": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
                                              P, P, P, P, P]),
         "kv_page_key_sums": (C.c_int, [C.POINTER(KVShape), P, I64, I64, P, I64, P]),
-        "kv_select_workspace_bytes": (SZ, [I64]),
-        "kv_select_pages": (C.c_int, [C.POINTER(KVShape), P, P, I64, I32, P, P, SZ, P]),
+        "kv_select_workspace_bytes": (SZ, [I64, I32]),
+        "kv_select_pages": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, I32, I32, P, P, SZ, P]),
         "kv_host_f64_to_f16": (C.c_uint16, [C.c_double]),
         "kv_host_encode_vector": (C.c_int, [I32, P, P, P]),
     }
@@ -336,22 +336,29 @@ def page_key_sums(s: KVShape, k, start_pos: int, sums, stream=None):
                                 _ptr(sums, torch.int64, name="sums"), sums.shape[0], _stream(stream)))
 
 
-def select_workspace_bytes(n_pages: int) -> int:
-    nb = lib.kv_select_workspace_bytes(n_pages)
+def select_workspace_bytes(n_pages: int, n_sets: int = 1) -> int:
+    nb = lib.kv_select_workspace_bytes(n_pages, n_sets)
     if nb == 0:
         raise KVError(-1, last_error())
     return nb
 
 
 def select_pages(s: KVShape, q, sums, n_pages: int, k_sel: int, out_selection, workspace, stream=None):
-    """kv_select_pages: the step's pages (ascending) into out_selection (device int32)."""
+    """kv_select_pages over the leading dimension of q ([n_sets, Hq, 256], or [Hq, 256] for
+    one set), sums ([n_sets, sums_pages, Hkv, 256] or [sums_pages, Hkv, 256]) and
+    out_selection ([n_sets, k_sel] or [k_sel]); each set's pages in ascending order."""
     torch = _torch()
-    if q.shape != (s.n_q_heads, s.head_dim):
-        raise ValueError("q must be [n_q_heads, head_dim]")
-    if out_selection.numel() < min(k_sel, n_pages):
-        raise ValueError("out_selection too small")
+    one = q.dim() == 2
+    n_sets = 1 if one else q.shape[0]
+    if q.shape[-2:] != (s.n_q_heads, s.head_dim) or sums.dim() != (3 if one else 4):
+        raise ValueError("q must be [n_sets, n_q_heads, head_dim] and sums [n_sets, pages, n_kv_heads, head_dim]")
+    if not one and (sums.shape[0] != n_sets or out_selection.dim() != 2 or out_selection.shape[0] != n_sets):
+        raise ValueError("one sums block and one selection row per set")
+    if out_selection.shape[-1] != k_sel:
+        raise ValueError("out_selection rows must hold k_sel entries")
     _check(lib.kv_select_pages(C.byref(s), _ptr(q, torch.float16, name="q"), _ptr(sums, torch.int64, name="sums"),
-                               n_pages, k_sel, _ptr(out_selection, torch.int32, name="out_selection"),
+                               sums.shape[-3], n_pages, k_sel, n_sets,
+                               _ptr(out_selection, torch.int32, name="out_selection"),
                                C.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
                                _stream(stream)))
 

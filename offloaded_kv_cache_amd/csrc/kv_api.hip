@@ -490,31 +490,35 @@ int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int
   return ok();
 }
 
-size_t kv_select_workspace_bytes(int64_t n_pages) {
-  if (n_pages < 0 || n_pages > select_max_pages()) {
-    fail(KV_EINVAL, "n_pages out of range (0..%d)", select_max_pages());
+size_t kv_select_workspace_bytes(int64_t n_pages, int32_t n_sets) {
+  if (n_pages < 0 || n_pages > select_max_pages() || n_sets < 0 || n_sets > 65535) {
+    fail(KV_EINVAL, "n_pages (0..%d) or n_sets (0..65535) out of range", select_max_pages());
     return 0;
   }
   ok();
-  return (size_t)(n_pages > 0 ? n_pages : 1) * 16;
+  const int64_t n = (int64_t)n_pages * n_sets;
+  return (size_t)(n > 0 ? n : 1) * 16;
 }
 
-int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t n_pages,
-                    int32_t k_sel, int32_t* out_selection, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t sums_pages,
+                    int64_t n_pages, int32_t k_sel, int32_t n_sets, int32_t* out_selection,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   if (int r = check_shape(shape)) return r;
   if (n_pages < 0 || n_pages > select_max_pages())
     return fail(KV_EINVAL, "n_pages out of range (0..%d)", select_max_pages());
   if (k_sel < 1 || k_sel > select_max_k()) return fail(KV_EINVAL, "k_sel out of range (1..%d)", select_max_k());
-  if (n_pages == 0) return ok();
+  if (n_sets < 0 || n_sets > 65535) return fail(KV_EINVAL, "n_sets out of range (0..65535)");
+  if (sums_pages < n_pages) return fail(KV_EINVAL, "sums_pages (%lld) below n_pages (%lld)",
+                                        (long long)sums_pages, (long long)n_pages);
+  if (n_pages == 0 || n_sets == 0) return ok();
   if (!q || !sums || !out_selection || !workspace) return fail(KV_EINVAL, "NULL buffer");
   if (!aligned(q, 2) || !aligned(sums, 8) || !aligned(out_selection, 4) || !aligned(workspace, 16))
     return fail(KV_EALIGN, "misaligned buffer (q: 2 B, sums: 8 B, selection: 4 B, workspace: 16 B)");
-  if (workspace_bytes < (size_t)n_pages * 16)
-    return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
-                (size_t)n_pages * 16);
-  hipError_t e = launch_select(shape->n_q_heads, shape->n_kv_heads, (const uint16_t*)q, sums, (int)n_pages,
-                               k_sel, out_selection, workspace, (hipStream_t)stream);
+  const size_t need = (size_t)n_pages * n_sets * 16;
+  if (workspace_bytes < need)
+    return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  hipError_t e = launch_select(shape->n_q_heads, shape->n_kv_heads, (const uint16_t*)q, sums, sums_pages,
+                               (int)n_pages, k_sel, n_sets, out_selection, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "selection launch");
   return ok();
 }

@@ -132,7 +132,8 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream,
 hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
                            int64_t* sums, hipStream_t stream);
 hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const int64_t* sums,
-                         int n_pages, int k_sel, int32_t* out, void* scores, hipStream_t stream);
+                         int64_t sums_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
+                         hipStream_t stream);
 int select_max_pages();
 int select_max_k();
 

@@ -39,14 +39,18 @@ __global__ __launch_bounds__(kThreads) void key_sums_kernel(const uint16_t* __re
             (unsigned long long)acc);
 }
 
-// Score of page blockIdx.x.
+// Score of page blockIdx.x of selection set blockIdx.y (a layer or a sequence).
 __global__ __launch_bounds__(kThreads) void page_score_kernel(const uint16_t* __restrict__ q,
                                                              const int64_t* __restrict__ sums,
+                                                             int64_t sums_pages, int n_pages,
                                                              int n_q_heads, int n_kv_heads,
                                                              i128* __restrict__ scores) {
   __shared__ i128 red[kThreads];
   const int e = threadIdx.x;
   const int64_t page = blockIdx.x;
+  q += (size_t)blockIdx.y * n_q_heads * kHeadDim;
+  sums += (size_t)blockIdx.y * sums_pages * n_kv_heads * kHeadDim;
+  scores += (size_t)blockIdx.y * n_pages;
   const int G = n_q_heads / n_kv_heads;
   i128 acc = 0;
   for (int g = 0; g < n_kv_heads; ++g) {
@@ -70,6 +74,8 @@ constexpr int kMaxPages = 32768;
 __global__ __launch_bounds__(kThreads) void top_pages_kernel(const i128* __restrict__ scores, int n_pages,
                                                             int k_sel, int32_t* __restrict__ out) {
   __shared__ uint8_t taken[kMaxPages];
+  scores += (size_t)blockIdx.x * n_pages;  // selection set blockIdx.x
+  out += (size_t)blockIdx.x * k_sel;
   __shared__ i128 best_s[kThreads];
   __shared__ int best_p[kThreads];
   __shared__ int chosen[kMaxSelect];
@@ -147,14 +153,15 @@ hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, 
 }
 
 hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const int64_t* sums,
-                         int n_pages, int k_sel, int32_t* out, void* scores, hipStream_t stream) {
-  if (n_pages <= 0) return hipSuccess;
-  hipLaunchKernelGGL(page_score_kernel, dim3((unsigned)n_pages), dim3(kThreads), 0, stream, q, sums,
-                     n_q_heads, n_kv_heads, (i128*)scores);
+                         int64_t sums_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
+                         hipStream_t stream) {
+  if (n_pages <= 0 || n_sets <= 0) return hipSuccess;
+  hipLaunchKernelGGL(page_score_kernel, dim3((unsigned)n_pages, (unsigned)n_sets), dim3(kThreads), 0, stream,
+                     q, sums, sums_pages, n_pages, n_q_heads, n_kv_heads, (i128*)scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(top_pages_kernel, dim3(1), dim3(kThreads), 0, stream, (const i128*)scores, n_pages,
-                     k_sel, out);
+  hipLaunchKernelGGL(top_pages_kernel, dim3((unsigned)n_sets), dim3(kThreads), 0, stream, (const i128*)scores,
+                     n_pages, k_sel, out);
   return hipGetLastError();
 }
 

@@ -29,7 +29,7 @@ def gpu_sums(gpu, s, k, chunks, cap):
 
 def gpu_select(gpu, s, q, sums, n_pages, k_sel):
     ws = torch.empty(K.select_workspace_bytes(n_pages), dtype=torch.uint8, device=gpu)
-    out = torch.full((max(1, min(k_sel, n_pages)),), -1, dtype=torch.int32, device=gpu)
+    out = torch.full((k_sel,), -1, dtype=torch.int32, device=gpu)
     K.select_pages(s, to_dev(q, gpu), sums, n_pages, k_sel, out, ws)
     torch.cuda.synchronize()
     return out.cpu().numpy()[:min(k_sel, n_pages)].tolist()
@@ -91,3 +91,25 @@ def test_selection_over_a_million_tokens(gpu):
     got = gpu_select(gpu, s, q, sums, T // 256, 8)
     want = osel.select_pages(osel.page_scores(q, sums.cpu().numpy()), 8)
     assert got == want and got[-1] == T // 256 - 1
+
+
+def test_selection_of_several_sets_in_one_call(gpu):
+    """Sixteen sets (layers) with their own queries and key sums in one call; sums with
+    spare pages past the context."""
+    s = K.shape("int8")
+    L, T, k_sel = 16, 40 * 256 + 9, 8
+    n = -(-T // 256)
+    sums = torch.zeros((L, n + 3, 4, 256), dtype=torch.int64, device=gpu)
+    keys = []
+    for layer in range(L):
+        k, _ = kvsynth.kv_tokens_np(44, layer, 0, 0, T)
+        keys.append(k)
+        K.page_key_sums(s, to_dev(k, gpu), 0, sums[layer])
+    q = kvsynth.q_np(44, 0, L)
+    ws = torch.empty(K.select_workspace_bytes(n, L), dtype=torch.uint8, device=gpu)
+    out = torch.full((L, k_sel), -1, dtype=torch.int32, device=gpu)
+    K.select_pages(s, to_dev(q, gpu), sums, n, k_sel, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for layer in range(L):
+        assert got[layer].tolist() == osel.select(q[layer], keys[layer], k_sel), layer
