@@ -385,7 +385,7 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
  * n_pages <= k_sel, every page.
  *   q          device fp16 [n_sets][n_q_heads][256] (each set's query).
  *   sums       device int64 [n_sets][sums_pages][n_kv_heads][256], sums_pages >= n_pages.
- *   n_pages    pages of the context (<= 32768); k_sel in 1..256.
+ *   n_pages    pages of the context (<= 32768); k_sel in 1..256; at most 8 KV heads.
  *   workspace  device, >= kv_select_workspace_bytes(n_pages, n_sets) bytes, 16-B aligned.
  */
 int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,

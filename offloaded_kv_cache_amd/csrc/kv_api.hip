@@ -507,6 +507,8 @@ int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, i
   if (n_pages < 0 || n_pages > select_max_pages())
     return fail(KV_EINVAL, "n_pages out of range (0..%d)", select_max_pages());
   if (k_sel < 1 || k_sel > select_max_k()) return fail(KV_EINVAL, "k_sel out of range (1..%d)", select_max_k());
+  if (shape->n_kv_heads > select_max_kv_heads())
+    return fail(KV_EUNSUPPORTED, "page selection takes at most %d KV heads", select_max_kv_heads());
   if (n_sets < 0 || n_sets > 65535) return fail(KV_EINVAL, "n_sets out of range (0..65535)");
   if (sums_pages < n_pages) return fail(KV_EINVAL, "sums_pages (%lld) below n_pages (%lld)",
                                         (long long)sums_pages, (long long)n_pages);

@@ -136,6 +136,7 @@ hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const
                          hipStream_t stream);
 int select_max_pages();
 int select_max_k();
+int select_max_kv_heads();
 
 constexpr int kGatherMaxBatch = 256;  // selections per gather launch (kernel-argument size)
 

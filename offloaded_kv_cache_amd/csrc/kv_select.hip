@@ -39,32 +39,50 @@ __global__ __launch_bounds__(kThreads) void key_sums_kernel(const uint16_t* __re
             (unsigned long long)acc);
 }
 
-// Score of page blockIdx.x of selection set blockIdx.y (a layer or a sequence).
+// Scores of a tile of kTilePages pages of selection set blockIdx.y (a layer or a
+// sequence). The set's query sums Q[g][e] are formed once into LDS; thread (page j of the
+// tile, part i) adds the products of its 16-element slice of every KV head, and one
+// thread per page adds the page's kParts partial sums (128-bit integers).
+constexpr int kTilePages = 16;
+constexpr int kParts = kThreads / kTilePages;            // 16 threads per page
+constexpr int kSlice = kHeadDim / kParts;                // 16 elements per thread and KV head
+constexpr int kMaxKvHeads = 8;
+
 __global__ __launch_bounds__(kThreads) void page_score_kernel(const uint16_t* __restrict__ q,
                                                              const int64_t* __restrict__ sums,
                                                              int64_t sums_pages, int n_pages,
                                                              int n_q_heads, int n_kv_heads,
                                                              i128* __restrict__ scores) {
-  __shared__ i128 red[kThreads];
-  const int e = threadIdx.x;
-  const int64_t page = blockIdx.x;
+  __shared__ int64_t qsum[kMaxKvHeads][kHeadDim];
+  __shared__ i128 part[kTilePages][kParts];
+  const int tid = threadIdx.x;
   q += (size_t)blockIdx.y * n_q_heads * kHeadDim;
   sums += (size_t)blockIdx.y * sums_pages * n_kv_heads * kHeadDim;
   scores += (size_t)blockIdx.y * n_pages;
   const int G = n_q_heads / n_kv_heads;
-  i128 acc = 0;
-  for (int g = 0; g < n_kv_heads; ++g) {
+  for (int g = 0; g < n_kv_heads; ++g) {  // Q[g][e] for e = tid
     int64_t qs = 0;
-    for (int i = 0; i < G; ++i) qs += f16_to_int(q[(g * G + i) * kHeadDim + e]);
-    acc += (i128)qs * (i128)sums[(page * n_kv_heads + g) * kHeadDim + e];
+    for (int i = 0; i < G; ++i) qs += f16_to_int(q[(g * G + i) * kHeadDim + tid]);
+    qsum[g][tid] = qs;
   }
-  red[e] = acc;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (e < s) red[e] += red[e + s];
-    __syncthreads();
+  const int j = tid / kParts, i = tid % kParts;
+  const int64_t page = (int64_t)blockIdx.x * kTilePages + j;
+  i128 acc = 0;
+  if (page < n_pages) {
+    for (int g = 0; g < n_kv_heads; ++g) {
+      const int64_t* sp = sums + (page * n_kv_heads + g) * kHeadDim + i * kSlice;
+#pragma unroll
+      for (int u = 0; u < kSlice; ++u) acc += (i128)qsum[g][i * kSlice + u] * (i128)sp[u];
+    }
   }
-  if (e == 0) scores[page] = red[0];
+  part[j][i] = acc;
+  __syncthreads();
+  if (i == 0 && page < n_pages) {
+    i128 t = part[j][0];
+    for (int u = 1; u < kParts; ++u) t += part[j][u];
+    scores[page] = t;
+  }
 }
 
 // The selection: the last page, then k - 1 rounds of "best page not yet taken".
@@ -142,6 +160,7 @@ __global__ __launch_bounds__(kThreads) void top_pages_kernel(const i128* __restr
 
 int select_max_pages() { return kMaxPages; }
 int select_max_k() { return kMaxSelect; }
+int select_max_kv_heads() { return kMaxKvHeads; }
 
 hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
                            int64_t* sums, hipStream_t stream) {
@@ -156,8 +175,9 @@ hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const
                          int64_t sums_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
                          hipStream_t stream) {
   if (n_pages <= 0 || n_sets <= 0) return hipSuccess;
-  hipLaunchKernelGGL(page_score_kernel, dim3((unsigned)n_pages, (unsigned)n_sets), dim3(kThreads), 0, stream,
-                     q, sums, sums_pages, n_pages, n_q_heads, n_kv_heads, (i128*)scores);
+  const unsigned tiles = (unsigned)((n_pages + kTilePages - 1) / kTilePages);
+  hipLaunchKernelGGL(page_score_kernel, dim3(tiles, (unsigned)n_sets), dim3(kThreads), 0, stream, q, sums,
+                     sums_pages, n_pages, n_q_heads, n_kv_heads, (i128*)scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(top_pages_kernel, dim3((unsigned)n_sets), dim3(kThreads), 0, stream, (const i128*)scores,
