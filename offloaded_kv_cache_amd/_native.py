@@ -53,6 +53,10 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
                           "(run `python offloaded_kv_cache_amd/build.py`)")
+    # torch first: its wheel bundles a HIP runtime under the same soname as the one the
+    # library links. Loaded first, the library would pull in a second runtime, and its
+    # launches would not see the device torch's runtime holds.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
     P, I32, I64, SZ, F32 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float
     sig = {

@@ -175,3 +175,16 @@ def test_split_pages_fill_the_gpu_once():
     assert K.decode_split_pages(q4, 1, 1) == 1
     with pytest.raises(K.KVError):
         K.decode_split_pages(q4, 2, 100, 201)   # total above batch x max
+
+
+def test_binding_shares_torchs_hip_runtime():
+    """Importing the package before torch still maps a single HIP runtime: two runtimes in
+    one process leave the library's launches without the device torch holds."""
+    import subprocess
+    import sys
+    code = ("import offloaded_kv_cache_amd, torch\n"
+            "print(len({l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
