@@ -150,14 +150,17 @@ __device__ inline float half_sum(float v, int lane) {
   return v;
 }
 
-// One butterfly stage (bit log2 M) of the Walsh-Hadamard transform on N values per lane.
+// One butterfly stage (bit log2 M) of the Walsh-Hadamard transform on N values per lane:
+// partner + v in the lower lane of a pair, partner - v in the upper one, each as one fma
+// with a sign of +-1 (the same rounding as the add or subtract).
 template <int M, int N>
 __device__ inline void butterfly(float (&v)[N], int lane) {
+  const float sg = (lane & M) ? -1.0f : 1.0f;
   float o[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) o[i] = xchgf<M>(v[i], lane);
 #pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = (lane & M) ? (o[i] - v[i]) : (v[i] + o[i]);
+  for (int i = 0; i < N; ++i) v[i] = fmaf(sg, v[i], o[i]);
 }
 
 // ---- Q.K operands --------------------------------------------------------
@@ -533,12 +536,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     }
     __syncthreads();
     const int e0 = tid & 63, k = (tid >> 6) & 3;  // bits 6 and 7: a 4-point transform across waves
+    const float sg1 = (k & 1) ? -1.0f : 1.0f, sg2 = (k & 2) ? -1.0f : 1.0f;
 #pragma unroll
     for (int hh = 0; hh < kMaxGroup; ++hh) {
       const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
                   x3 = lds.qs[hh][e0 + 192];
-      const float s01 = (k & 1) ? x0 - x1 : x0 + x1, s23 = (k & 1) ? x2 - x3 : x2 + x3;
-      qv[hh] = ((k & 2) ? s01 - s23 : s01 + s23) * 0.0625f;
+      const float s01 = fmaf(sg1, x1, x0), s23 = fmaf(sg1, x3, x2);
+      qv[hh] = fmaf(sg2, s23, s01) * 0.0625f;
     }
     __syncthreads();
   }
