@@ -189,6 +189,40 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
                         int32_t pages_per_split, void* stream);
 
 /*
+ * kv_decode_attention_mq - causal attention of each sequence's n_q newest tokens
+ * over the paged, quantized cache: the verification step of speculative decoding
+ * (smzdm roundup, post.smzdm.com/p/ad79lwwz, section "二、一周跨卡实测": MTP
+ * drafts of up to 3 tokens checked in one pass) and chunked prompt reading
+ * (prefill rates in the same table; Strata page, section "三种 KV 格式横向对比":
+ * prompt reading over the quantized formats).
+ *
+ * The n_q tokens must already be in the cache (kv_append_quantize of the chunk):
+ * with T = context_lens[b], query j (0 <= j < n_q) of sequence b sits at position
+ * T - n_q + j and attends to tokens 0 .. T - n_q + j, i.e. it is exactly
+ * kv_decode_attention with context length T - n_q + j + 1 (0 if that is < 1,
+ * which gives a zero output). n_q = 1 is kv_decode_attention.
+ *
+ *   q              device fp16 [batch][n_q][n_q_heads][256].
+ *   out            device fp32 [batch][n_q][n_q_heads][256].
+ *   workspace      as for kv_decode_attention, of at least
+ *                  kv_decode_workspace_bytes(shape, batch * n_q, max_context,
+ *                  pages_per_split) bytes; pages_per_split = 0 chooses as for
+ *                  batch * n_q sequences.
+ * Every other argument is that of kv_decode_attention (block_tables and
+ * context_lens have one row / entry per sequence). batch * n_q must be at most
+ * 65535. Each query row is its own work item; the rows of one sequence read the
+ * same pages at about the same time, so repeated reads are mostly served by the
+ * caches.
+ */
+int kv_decode_attention_mq(const kv_shape* shape, const void* q, int32_t batch, int32_t n_q,
+                           const void* pool, int64_t n_pool_pages,
+                           const int32_t* block_tables, int32_t max_pages,
+                           const int32_t* context_lens, int64_t max_context,
+                           float softmax_scale, float* out,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t pages_per_split, void* stream);
+
+/*
  * The pages per split that pages_per_split = 0 selects, for `batch` sequences of at
  * most `max_context` tokens whose lengths add up to `total_context` (0: assume every
  * sequence at max_context). The split count is chosen so that the grid about fills

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed",
-    "kv_decode_combine", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
+    "kv_decode_combine", "kv_decode_attention_mq", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
     "kv_select_workspace_bytes", "kv_select_pages",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
@@ -74,6 +74,8 @@ def _load():
                                         P, P, SZ, I32, P]),
         "kv_decode_split_timed": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                             P, P, SZ, I32, P, P, P]),
+        "kv_decode_attention_mq": (C.c_int, [C.POINTER(KVShape), P, I32, I32, P, I64, P, I32, P, I64,
+                                             F32, P, P, SZ, I32, P]),
         "kv_append_decode": (C.c_int, [C.POINTER(KVShape), P, P, P, I32, P, I64, P, I32, P, I64,
                                        F32, P, P, SZ, I32, P, P, P]),
         "kv_residency_reset": (C.c_int, [C.POINTER(KVResidency)]),
@@ -220,6 +222,27 @@ def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_contex
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
         softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream), *extra))
+
+
+def decode_attention_mq(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
+                        workspace, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
+                        stream=None):
+    """Causal attention of each sequence's n_q newest tokens (kv_decode_attention_mq):
+    ``q`` fp16 [B, n_q, Hq, 256], query j of sequence b at position context_lens[b] - n_q + j;
+    writes fp32 ``out`` [B, n_q, Hq, 256]. The workspace is sized for B * n_q sequences."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[2:] != (s.n_q_heads, s.head_dim) or out.shape != q.shape:
+        raise ValueError("q and out must be [batch, n_q, n_q_heads, head_dim]")
+    B, n_q = q.shape[0], q.shape[1]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
+    pb = page_bytes(s)
+    _check(lib.kv_decode_attention_mq(
+        C.byref(s), _ptr(q, torch.float16, name="q"), B, n_q, C.c_void_p(pool.data_ptr()),
+        pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
+        block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
+        softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream)))
 
 
 def append_decode(s: KVShape, k_new, v_new, q, pool, block_tables, context_lens, max_context: int,

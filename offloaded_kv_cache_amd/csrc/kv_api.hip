@@ -194,10 +194,13 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
                  const int32_t* context_lens, int64_t max_context, float softmax_scale, float* out,
                  void* workspace, size_t workspace_bytes, int32_t pages_per_split, void* stream,
                  void* start_event = nullptr, void* stop_event = nullptr,
-                 const void* k_new = nullptr, const void* v_new = nullptr) {
+                 const void* k_new = nullptr, const void* v_new = nullptr, int32_t n_q = 1) {
   if (int r = check_shape(shape)) return r;
-  if (batch < 0 || batch > 65535) return fail(KV_EINVAL, "batch out of range (%d)", batch);
+  if (n_q < 1) return fail(KV_EINVAL, "n_q must be >= 1 (got %d)", n_q);
+  if (batch < 0 || (int64_t)batch * n_q > 65535)
+    return fail(KV_EINVAL, "batch x n_q out of range (%d x %d)", batch, n_q);
   if (batch == 0) return ok();
+  const int32_t rows = batch * n_q;  // query rows: the kernels treat each as a sequence
   if (!q || !pool || !block_tables || !context_lens || !out || !workspace)
     return fail(KV_EINVAL, "NULL buffer");
   if (max_pages < 1) return fail(KV_EINVAL, "max_pages must be >= 1");
@@ -211,8 +214,8 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   const int64_t bound = max_context < (int64_t)max_pages * kPageTokens ? max_context
                                                                        : (int64_t)max_pages * kPageTokens;
   const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
-  const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, batch, max_pages_ctx);
-  const WsLayout w = workspace_layout(shape, batch, max_context, pps);
+  const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, rows, max_pages_ctx);
+  const WsLayout w = workspace_layout(shape, rows, max_context, pps);
   if (workspace_bytes < w.total)
     return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                 w.total);
@@ -221,7 +224,8 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.fmt = shape->format;
   a.n_q_heads = shape->n_q_heads;
   a.n_kv_heads = shape->n_kv_heads;
-  a.batch = batch;
+  a.batch = rows;
+  a.n_q = n_q;
   a.q = (const uint16_t*)q;
   a.pool = (const uint8_t*)pool;
   a.n_pool_pages = n_pool_pages;
@@ -259,6 +263,16 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch, con
   return decode_phase(3, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
                       max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
                       stream);
+}
+
+int kv_decode_attention_mq(const kv_shape* shape, const void* q, int32_t batch, int32_t n_q,
+                           const void* pool, int64_t n_pool_pages, const int32_t* block_tables,
+                           int32_t max_pages, const int32_t* context_lens, int64_t max_context,
+                           float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                           int32_t pages_per_split, void* stream) {
+  return decode_phase(3, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
+                      max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
+                      stream, nullptr, nullptr, nullptr, nullptr, n_q);
 }
 
 int kv_decode_split(const kv_shape* shape, const void* q, int32_t batch, const void* pool,

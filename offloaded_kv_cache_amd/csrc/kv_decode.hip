@@ -364,13 +364,16 @@ __device__ inline int32_t bt_row_entry(const int32_t* __restrict__ block_tables,
 // from a counter); otherwise workgroup i does item i only. APPEND: the call also
 // appends one token per sequence (k_new, v_new [batch][n_kv_heads][256] fp16, at
 // position context_lens[b] - 1), written through pool_w (the pool's address).
+// Rows b of q (batch of them) are n_q queries per sequence: row b is query
+// j = b % n_q of sequence b / n_q, whose context length T gives it the first
+// T - n_q + j + 1 tokens (causal attention of the sequence's n_q newest tokens).
 template <int KK, int VK, int NW, bool DYN, bool APPEND>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const uint16_t* __restrict__ q, const uint8_t* pool, int64_t n_pool_pages,
     const int32_t* __restrict__ block_tables, int max_pages, const int32_t* __restrict__ context_lens,
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
-    int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch,
+    int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch, int n_q,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint8_t* pool_w) {
   __shared__ __attribute__((aligned(16))) SplitLds<NW> lds;
   __shared__ int item_s;
@@ -412,13 +415,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     qv[hh] = hh < G ? x : 0.f;
   }
   const int p_begin = split * pages_per_split;
-  const int32_t phys_first = block_tables[(size_t)b * max_pages + min(p_begin, max_pages - 1)];
-  int T = context_lens[b];
+  const int bs = n_q == 1 ? b : b / n_q;            // the sequence of query row b
+  const int later = n_q == 1 ? 0 : n_q - 1 - (b - bs * n_q);  // queries after row b's
+  const int32_t phys_first = block_tables[(size_t)bs * max_pages + min(p_begin, max_pages - 1)];
+  int T = context_lens[bs];
   const bool t_in_range = T <= max_context && T >= 0;
   if (!t_in_range) {
     if (tid == 0 && split == 0 && g == 0) atomicOr(status, KV_STATUS_CONTEXT_CLAMPED);
     T = T < 0 ? 0 : max_context;
   }
+  T = T > later ? T - later : 0;
   const int n_pages = (T + kPageTokens - 1) / kPageTokens;
   const int p_end = min(n_pages, p_begin + pages_per_split);
   if (p_begin >= p_end) continue;  // uniform over the workgroup
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   uint16_t new_in[4] = {0, 0, 0, 0};
   if (APPEND && new_pg >= 0)
     enc::load_vals((wave & 1 ? v_new : k_new) + ((size_t)b * n_kv_heads + g) * kHeadDim, lane, new_in);
-  const int32_t phys_new = new_pg >= 0 ? bt_row_entry(block_tables, b, max_pages, new_pg) : -1;
+  const int32_t phys_new = new_pg >= 0 ? bt_row_entry(block_tables, bs, max_pages, new_pg) : -1;
   // (the appending workgroup, which also encodes the token, keeps it one page longer)
   const int boost_until = (!DYN && NW == 4 && ((int)blockIdx.x >= kComputeUnits || new_pg >= 0))
                               ? min(p_end, p_begin + (p_end - p_begin) / 2 + (new_pg >= 0 ? 1 : 0))
@@ -449,7 +455,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 
   const int64_t head_bytes = plane_bytes(KK) + plane_bytes(VK);
   const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
-  const int32_t* bt = block_tables + (size_t)b * max_pages;
+  const int32_t* bt = block_tables + (size_t)bs * max_pages;
 
   // Page base of logical page pg for this KV head (nullptr for an id outside the pool).
   auto page_base = [&](int pg) -> const uint8_t* {
@@ -969,7 +975,7 @@ constexpr int kCombineChunk = 1024;                            // split weights 
 __global__ __launch_bounds__(kCombineThreads) void decode_combine(
     const float* __restrict__ part_ml, const float* __restrict__ part_o,
     const int32_t* __restrict__ context_lens, int max_context, int n_q_heads,
-    int pages_per_split, int n_splits, float* __restrict__ out) {
+    int pages_per_split, int n_splits, int n_q, float* __restrict__ out) {
   __shared__ float wts[kCombineChunk];
   __shared__ float part[kCombineGroups][kCombineElems];
   __shared__ float red[2][kCombineThreads / 64];
@@ -985,8 +991,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
 #pragma unroll
   for (int u = 0; u < kCombineRun; ++u)
     v[u] = part_o[(base + min(sg * kCombineRun + u, n_splits - 1)) * kHeadDim + e];
-  int T = context_lens[b];
+  int T = context_lens[b / n_q];
   T = T < 0 ? 0 : (T > max_context ? max_context : T);
+  const int later = n_q - 1 - b % n_q;  // (as in the split kernel)
+  T = T > later ? T - later : 0;
   const int n_pages = (T + kPageTokens - 1) / kPageTokens;
   const int ns = min(n_splits, (n_pages + pages_per_split - 1) / pages_per_split);
   float o = 0.f, L = 0.f;
@@ -1050,7 +1058,7 @@ void launch_split_v(const DecodeArgs& a, dim3 grid, hipStream_t stream, hipEvent
                         stop, 0, a.q, a.pool, a.n_pool_pages, a.block_tables, a.max_pages,
                         a.context_lens, a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split,
                         a.n_splits, a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch,
-                        a.k_new, a.v_new, a.pool_w);
+                        a.n_q, a.k_new, a.v_new, a.pool_w);
 }
 
 template <int KK, int VK>
@@ -1084,7 +1092,7 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hip
   if (phase & 2) {
     dim3 grid((unsigned)a.n_q_heads, (unsigned)a.batch, kHeadDim / kCombineElems), block(kCombineThreads);
     hipLaunchKernelGGL(decode_combine, grid, block, 0, stream, a.part_ml, a.part_o, a.context_lens,
-                       a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits, a.out);
+                       a.max_context, a.n_q_heads, a.pages_per_split, a.n_splits, a.n_q, a.out);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -100,13 +100,15 @@ hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint1
 
 struct DecodeArgs {
   int fmt;
-  int n_q_heads, n_kv_heads, batch;
+  int n_q_heads, n_kv_heads;
+  int batch;                  // rows of q / out: sequences x queries per sequence
+  int n_q = 1;                // queries per sequence (rows b * n_q .. b * n_q + n_q - 1)
   const uint16_t* q;
   const uint8_t* pool;
   int64_t n_pool_pages;
   const int32_t* block_tables;
   int32_t max_pages;
-  const int32_t* context_lens;
+  const int32_t* context_lens;  // [batch / n_q]: query j of a sequence of length T sees T - n_q + j + 1 tokens
   int32_t max_context;        // clamp bound, already min(max_context, max_pages * 256)
   int32_t pages_per_split;
   int32_t n_splits;           // grid size along the context

@@ -20,6 +20,14 @@ the exact mathematics, rounded once per fp64 operation.
 
 Readings: scale = 1/sqrt(256) = 1/16 by default (the pages give none);
 q and k arrive after any positional encoding; T = 0 gives a zero output.
+
+Several new tokens per sequence (speculative drafts checked in one pass, or a
+chunk of a prompt; smzdm roundup post.smzdm.com/p/ad79lwwz, section
+"二、一周跨卡实测": MTP drafts and prefill rates): the n_q newest tokens of a
+sequence of T tokens are its queries, query j at position T - n_q + j, and
+each attends causally, to tokens 0 .. T - n_q + j (reading: the usual causal
+mask of a decoder; the pages give no other rule). Each query is therefore
+the decode attention above over its own prefix.
 """
 
 from __future__ import annotations
@@ -88,3 +96,18 @@ def decode_attention_chunked(q, get_kv, T: int, hkv: int, fmt: int,
             acc[g * G:(g + 1) * G] += p[g * G:(g + 1) * G, t0:t1] @ vh[:, g, :]
     out = acc / p.sum(axis=1, keepdims=True)
     return rotate(out) if rotates_output(fmt) else out
+
+
+def multi_query_attention(q, k_hat, v_hat, fmt: int, scale: float = DEFAULT_SCALE) -> np.ndarray:
+    """The n_q newest tokens of one sequence as queries. q [n_q, Hq, 256] (fp16 values);
+    k_hat, v_hat [T, Hkv, 256] float64 (T >= 0 tokens, the queries' own tokens included).
+
+    Query j sees tokens 0 .. T - n_q + j (none if that is negative). Returns [n_q, Hq, 256].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_q, T = q.shape[0], k_hat.shape[0]
+    out = np.zeros(q.shape)
+    for j in range(n_q):
+        seen = max(0, T - n_q + j + 1)
+        out[j] = decode_attention(q[j], k_hat[:seen], v_hat[:seen], fmt, scale)
+    return out
