@@ -59,7 +59,7 @@ def kv_bytes_per_token(fmt: str, n_kv_heads: int = 4) -> int:
     return n_kv_heads * sum(rec)
 
 
-def build_resident(args, wl, dev):
+def build_resident(args, wl, dev, per_step=1):
     import torch
 
     import kvsynth
@@ -69,7 +69,7 @@ def build_resident(args, wl, dev):
     B = len(lens)
     n_steps = args.warmup + args.steps
     end_lens = lens
-    start_lens = [max(1, T - n_steps) for T in end_lens]
+    start_lens = [max(1, T - n_steps * per_step) for T in end_lens]
     pages_per_seq = [-(-T // PAGE) for T in end_lens]
     n_pool = sum(pages_per_seq)
     max_pages = max(pages_per_seq)
@@ -191,6 +191,71 @@ def run_resident(args, wl, dev):
         pages_per_split=args.pages_per_split,
     )
     return res, (s, pools, tables, start_lens)
+
+
+def run_multi_query(args, wl, dev):
+    """Speculative verification: per layer, append the step's n_q new tokens (one chunk,
+    kv_append_quantize) and run their causal attention (kv_decode_attention_mq)."""
+    import torch
+
+    import kvsynth
+    import offloaded_kv_cache_amd as K
+
+    fmt, L, lens, cfg = wl["fmt"], wl["layers"], wl["lens"], wl["cfg"]
+    nq, B = args.queries, len(lens)
+    s, pools, tables, start_lens, max_pages, _ = build_resident(args, wl, dev, per_step=nq)
+    n_steps = args.warmup + args.steps
+    max_ctx = max(lens)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(kvsynth.torch_seed(cfg, 98))
+    q_all = torch.randn((n_steps, L, B, nq, 24, 256), generator=gen, device=dev).to(torch.float16)
+    knew = torch.randn((n_steps, L, B, nq, 4, 256), generator=gen, device=dev).to(torch.float16)
+    vnew = torch.randn((n_steps, L, B, nq, 4, 256), generator=gen, device=dev).to(torch.float16)
+    ctx = torch.tensor([[start_lens[b] + (st + 1) * nq for b in range(B)] for st in range(n_steps)],
+                       dtype=torch.int32, device=dev)
+    ws = K.paged.DecodeWorkspace(s, B, max_ctx, args.pages_per_split, device=dev, n_q=nq)
+    out = torch.empty((B, nq, 24, 256), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    per_tok = kv_bytes_per_token(fmt)
+    timed = []
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)] for _ in range(n_steps)]
+    for pair in (p for row in events for p in row):
+        for e in pair:
+            e.record(stream)
+
+    def step(st, timing):
+        for layer in range(L):
+            for b in range(B):
+                T = start_lens[b] + (st + 1) * nq
+                pools[layer].append(knew[st, layer, b], vnew[st, layer, b], T - nq, tables[layer][b].contiguous())
+            evs = events[st][layer] if timing and layer % args.event_every == 0 else None
+            if evs is not None:
+                evs[0].record(stream)
+            K.decode_attention_mq(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx, out,
+                                  ws.data, pages_per_split=args.pages_per_split, stream=stream)
+            if evs is not None:
+                evs[1].record(stream)
+                timed.append((evs[0], evs[1], sum(start_lens[b] + (st + 1) * nq for b in range(B)) * per_tok))
+
+    for st in range(args.warmup):
+        step(st, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for st in range(args.warmup, n_steps):
+        step(st, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ws.status() != 0:
+        raise RuntimeError(f"decode status word {ws.status()}")
+    kv_bytes = sum(sum(start_lens[b] + (st + 1) * nq for b in range(B)) * per_tok * L
+                   for st in range(args.warmup, n_steps))
+    call_ms = [a.elapsed_time(b) for a, b, _ in timed]
+    call_bytes = [x for _, _, x in timed]
+    achieved = sum(call_bytes) / (sum(call_ms) * 1e-3) / 1e9
+    return dict(value=kv_bytes / wall / 1e9, ms_per_step=wall / args.steps * 1e3,
+                call_us=sum(call_ms) / len(call_ms) * 1e3, call_bytes=sum(call_bytes) / len(call_bytes),
+                achieved=achieved, query_tokens_per_s=nq * B * args.steps / wall)
 
 
 def cpu_baseline(args, wl, dev, state):
@@ -505,6 +570,9 @@ def main():
     ap.add_argument("--selection", choices=["random", "qsa"], default="random",
                     help="streaming workload: pages drawn at random with the set miss rate, or chosen on "
                          "the GPU from each layer's query and per-page key sums (kv_select_pages)")
+    ap.add_argument("--queries", type=int, default=1, metavar="N",
+                    help="N > 1: speculative verification of N new tokens per step and layer (append "
+                         "of the N-token chunk, then kv_decode_attention_mq) instead of one decode token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -541,6 +609,26 @@ def main():
             "config": res["config"], "gather": res["gather"], "cpu_baseline": None}), flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if args.queries > 1:
+        res = run_multi_query(args, wl, dev)
+        fmt = wl["fmt"]
+        print(json.dumps({
+            "metric": f"KV GB/s streamed in causal multi-query attention ({args.queries} queries per "
+                      f"sequence) at {args.workload} shape",
+            "value": round(res["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": f"{fmt} KV, fp32 accumulate", "data": "synthetic",
+            "config": {"workload": f"{args.workload} shape, {args.queries} new tokens per step and layer "
+                                   "(chunk append + causal multi-query attention)",
+                       "layers": wl["layers"], "context": wl["lens"], "kv_format": fmt,
+                       "queries": args.queries, "pages_per_split": args.pages_per_split or "auto"},
+            "query_tokens_per_s": round(res["query_tokens_per_s"], 1),
+            "roofline": {"bound": "hbm", "kernel": "decode_split + decode_combine (one call)",
+                         "achieved": round(res["achieved"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(res["achieved"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "avg_launch_us": round(res["call_us"], 3), "bytes_per_launch": int(res["call_bytes"])},
+            "cpu_baseline": None}), flush=True)
+        return
     res, state = run_resident(args, wl, dev)
     cpu = None
     if not args.no_cpu_baseline:

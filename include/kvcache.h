@@ -189,6 +189,15 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
                         int32_t pages_per_split, void* stream);
 
 /*
+ * kv_decode_mq_workspace_bytes - bytes of workspace kv_decode_attention_mq needs for
+ * `batch` sequences of n_q queries each and at most `max_context` tokens, with the
+ * given pages_per_split (0 = the library's choice): kv_decode_workspace_bytes for
+ * batch * n_q sequences. Returns 0 for invalid arguments.
+ */
+size_t kv_decode_mq_workspace_bytes(const kv_shape* shape, int32_t batch, int32_t n_q,
+                                    int64_t max_context, int32_t pages_per_split);
+
+/*
  * kv_decode_attention_mq - causal attention of each sequence's n_q newest tokens
  * over the paged, quantized cache: the verification step of speculative decoding
  * (smzdm roundup, post.smzdm.com/p/ad79lwwz, section "二、一周跨卡实测": MTP
@@ -205,14 +214,14 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
  *   q              device fp16 [batch][n_q][n_q_heads][256].
  *   out            device fp32 [batch][n_q][n_q_heads][256].
  *   workspace      as for kv_decode_attention, of at least
- *                  kv_decode_workspace_bytes(shape, batch * n_q, max_context,
- *                  pages_per_split) bytes; pages_per_split = 0 chooses as for
- *                  batch * n_q sequences.
+ *                  kv_decode_mq_workspace_bytes(shape, batch, n_q, max_context,
+ *                  pages_per_split) bytes.
+ *   pages_per_split  pages per split, or 0 for the library's choice for this call.
  * Every other argument is that of kv_decode_attention (block_tables and
  * context_lens have one row / entry per sequence). batch * n_q must be at most
- * 65535. Each query row is its own work item; the rows of one sequence read the
- * same pages at about the same time, so repeated reads are mostly served by the
- * caches.
+ * 65535. Each query is a row of the decode path's split-K kernel (row b * n_q + j,
+ * with the context its position allows); the rows of one sequence read the same
+ * pages at about the same time, so repeated reads are mostly served by the caches.
  */
 int kv_decode_attention_mq(const kv_shape* shape, const void* q, int32_t batch, int32_t n_q,
                            const void* pool, int64_t n_pool_pages,

@@ -25,7 +25,7 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed",
-    "kv_decode_combine", "kv_decode_attention_mq", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
+    "kv_decode_combine", "kv_decode_attention_mq", "kv_decode_mq_workspace_bytes", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
     "kv_select_workspace_bytes", "kv_select_pages",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
@@ -74,6 +74,7 @@ def _load():
                                         P, P, SZ, I32, P]),
         "kv_decode_split_timed": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                             P, P, SZ, I32, P, P, P]),
+        "kv_decode_mq_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I32, I64, I32]),
         "kv_decode_attention_mq": (C.c_int, [C.POINTER(KVShape), P, I32, I32, P, I64, P, I32, P, I64,
                                              F32, P, P, SZ, I32, P]),
         "kv_append_decode": (C.c_int, [C.POINTER(KVShape), P, P, P, I32, P, I64, P, I32, P, I64,
@@ -178,6 +179,14 @@ def decode_workspace_bytes(s: KVShape, batch: int, max_context: int, pages_per_s
     return int(r)
 
 
+def decode_mq_workspace_bytes(s: KVShape, batch: int, n_q: int, max_context: int,
+                              pages_per_split: int = 0) -> int:
+    r = lib.kv_decode_mq_workspace_bytes(C.byref(s), batch, n_q, max_context, pages_per_split)
+    if r == 0:
+        raise KVError(KV_EINVAL, last_error())
+    return int(r)
+
+
 def decode_split_pages(s: KVShape, batch: int, max_context: int, total_context: int = 0) -> int:
     """Pages per split the library selects (for a batch whose lengths add up to total_context)."""
     r = lib.kv_decode_split_pages(C.byref(s), batch, max_context, total_context)
@@ -229,7 +238,7 @@ def decode_attention_mq(s: KVShape, q, pool, block_tables, context_lens, max_con
                         stream=None):
     """Causal attention of each sequence's n_q newest tokens (kv_decode_attention_mq):
     ``q`` fp16 [B, n_q, Hq, 256], query j of sequence b at position context_lens[b] - n_q + j;
-    writes fp32 ``out`` [B, n_q, Hq, 256]. The workspace is sized for B * n_q sequences."""
+    writes fp32 ``out`` [B, n_q, Hq, 256]. Workspace: decode_mq_workspace_bytes(s, B, n_q, ...)."""
     torch = _torch()
     if q.dim() != 4 or q.shape[2:] != (s.n_q_heads, s.head_dim) or out.shape != q.shape:
         raise ValueError("q and out must be [batch, n_q, n_q_heads, head_dim]")

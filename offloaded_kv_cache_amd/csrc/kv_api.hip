@@ -170,6 +170,20 @@ size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch, int64_t m
   return workspace_layout(shape, batch, max_context, pps).total;
 }
 
+size_t kv_decode_mq_workspace_bytes(const kv_shape* shape, int32_t batch, int32_t n_q, int64_t max_context,
+                                    int32_t pages_per_split) {
+  if (check_shape(shape)) return 0;
+  if (batch < 1 || n_q < 1 || (int64_t)batch * n_q > 65535 || max_context < 0 || max_context > 0x7FFFFFFF ||
+      pages_per_split < 0) {
+    fail(KV_EINVAL, "bad batch, n_q, max_context or pages_per_split");
+    return 0;
+  }
+  const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
+  const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, batch * n_q, max_pages_ctx);
+  ok();
+  return workspace_layout(shape, batch * n_q, max_context, pps).total;
+}
+
 int32_t kv_decode_split_pages(const kv_shape* shape, int32_t batch, int64_t max_context,
                               int64_t total_context) {
   if (check_shape(shape)) return 0;

@@ -32,11 +32,14 @@ class PagedPool:
 
 
 class DecodeWorkspace:
-    """A zero-filled decode workspace sized for (batch, max_context, pages_per_split)."""
+    """A zero-filled decode workspace sized for (batch, max_context, pages_per_split); with
+    n_q > 1, for kv_decode_attention_mq with n_q queries per sequence."""
 
-    def __init__(self, shape, batch: int, max_context: int, pages_per_split: int = 0, device="cuda"):
+    def __init__(self, shape, batch: int, max_context: int, pages_per_split: int = 0, device="cuda",
+                 n_q: int = 1):
         import torch
-        self.nbytes = N.decode_workspace_bytes(shape, batch, max_context, pages_per_split)
+        self.nbytes = (N.decode_workspace_bytes(shape, batch, max_context, pages_per_split) if n_q == 1
+                       else N.decode_mq_workspace_bytes(shape, batch, n_q, max_context, pages_per_split))
         self.data = torch.zeros(self.nbytes, dtype=torch.uint8, device=device)
         self.pages_per_split = pages_per_split
 
