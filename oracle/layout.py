@@ -10,8 +10,9 @@ any reference to how the GPU library computes offsets:
   Logical token p of a sequence lives in page ``block_table[p // 256]``,
   row ``p % 256``.
 * Plane sizes: int8 67,584 B (256 x 256 codes + 256 x 4 fp16 scales);
-  q4 36,864 B (256 x 128 code bytes + 256 x 8 fp16 scales). So a page is
-  540,672 B (int8), 294,912 B (q4_0) or 417,792 B (k8v4) for 4 KV heads.
+  q4 and fp4 36,864 B (256 x 128 code bytes + 256 x 8 fp16 scales). So a page
+  is 540,672 B (int8), 294,912 B (q4_0, fp4) or 417,792 B (k8v4) for 4 KV
+  heads. The fp4 record uses the q4 byte layout below (4-bit codes, 8 scales).
 * K plane, token-major. Codes: 256 rows (one per token) of 256 B (int8) or
   128 B (q4), then scales: 256 rows of 4 (int8) or 8 (q4) little-endian fp16.
   Inside a code row the bytes of each 32-element block are spread over four
@@ -34,7 +35,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .records import HEAD_DIM, KIND_INT8, KIND_Q4, kinds
+from .records import HEAD_DIM, KIND_FP4, KIND_INT8, KIND_Q4, kinds
 
 PAGE_TOKENS = 256
 
@@ -75,7 +76,7 @@ def _k_row_maps(kind: str):
     return lo, hi
 
 
-_KMAP = {k: _k_row_maps(k) for k in (KIND_INT8, KIND_Q4)}
+_KMAP = {k: _k_row_maps(k) for k in (KIND_INT8, KIND_Q4, KIND_FP4)}
 
 
 def _k_row_bytes(codes: np.ndarray, kind: str) -> np.ndarray:

@@ -1,4 +1,4 @@
-"""The int8 and q4_0 vector records (oracle).
+"""The int8, q4_0 and fp4 vector records (oracle).
 
 Strata page, section "三种 KV 格式横向对比": int8 (the default, 1,056 B per
 token per layer for the K and V of two KV heads, i.e. 264 B per 256-element
@@ -33,6 +33,23 @@ the exact remainder, never by adding 0.5 in floating point.
 A d that overflows fp16 (|a| or |m| beyond what fp16 can scale) is out of the
 method's domain; the rules above still give codes (0 for int8, 8 for q4_0),
 and the dequantized values are then not finite.
+
+fp4 record (a block-scaled 4-bit floating-point format; the smzdm roundup,
+post.smzdm.com/p/ad79lwwz, section "一、先修正一笔老账", lists NVFP4 KV among the
+formats of other engines at 288 B per position, i.e. 144 B per vector, and
+the builder declares its own layout). Declared here: on y = H x like q4_0,
+per block of 32 elements (8 blocks, 8 fp16 scales + 128 bytes of 4-bit
+codes, in q4_0's byte layout):
+  a = max |y_j|; a == 0 -> d = 0 and all codes 0. Otherwise the block
+  exponent e = floor(log2 a) - 2 (the shared-exponent rule of the OCP
+  microscaling formats, 2 being the largest exponent of the e2m1 element),
+  clamped to [-23, 13] so that every dequantized value is an fp16 number;
+  d = 2^e, stored as an fp16 (exactly).
+  Each |y_j| / d (exact: d is a power of two) is rounded to the nearest value
+  of the e2m1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6}, ties to the even grid index,
+  values above 6 to 6 (saturation). The code is the grid index (0..7), plus
+  8 (the sign bit) when y_j < 0 and the index is not 0.
+  Dequantized (rotated-domain) value: +-grid[code & 7] * d.
 """
 
 from __future__ import annotations
@@ -41,10 +58,13 @@ import numpy as np
 
 from .hadamard import rotate
 
-FMT_INT8, FMT_Q4_0, FMT_K8V4 = 0, 1, 2
-FORMATS = {"int8": FMT_INT8, "q4_0": FMT_Q4_0, "k8v4": FMT_K8V4}
+FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_FP4 = 0, 1, 2, 3
+FORMATS = {"int8": FMT_INT8, "q4_0": FMT_Q4_0, "k8v4": FMT_K8V4, "fp4": FMT_FP4}
 
-KIND_INT8, KIND_Q4 = "int8", "q4"
+KIND_INT8, KIND_Q4, KIND_FP4 = "int8", "q4", "fp4"
+ROTATED_KINDS = (KIND_Q4, KIND_FP4)
+FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+FP4_EMIN, FP4_EMAX = -23, 13
 
 HEAD_DIM = 256
 INT8_GROUP = 64
@@ -59,17 +79,19 @@ def kinds(fmt: int):
         return KIND_Q4, KIND_Q4
     if fmt == FMT_K8V4:
         return KIND_INT8, KIND_Q4
+    if fmt == FMT_FP4:
+        return KIND_FP4, KIND_FP4
     raise ValueError(f"unknown format {fmt}")
 
 
 def rotates_query(fmt: int) -> bool:
-    """The query is rotated exactly when K is stored rotated (q4_0 only)."""
-    return kinds(fmt)[0] == KIND_Q4
+    """The query is rotated exactly when K is stored rotated (q4_0, fp4)."""
+    return kinds(fmt)[0] in ROTATED_KINDS
 
 
 def rotates_output(fmt: int) -> bool:
     """The output is rotated back exactly when V is stored rotated."""
-    return kinds(fmt)[1] == KIND_Q4
+    return kinds(fmt)[1] in ROTATED_KINDS
 
 
 def fp16_rne(v) -> np.ndarray:
@@ -142,12 +164,54 @@ def dequantize_q4(codes, scales) -> np.ndarray:
     return (b * d[..., None]).reshape(c.shape)
 
 
+def fp4_index(v) -> np.ndarray:
+    """e2m1 grid index of magnitudes v >= 0 (exact values): nearest, ties to the even
+    index, saturating at 6. The midpoints between grid values are 0.25, 0.75, 1.25,
+    1.75, 2.5, 3.5 and 5; at a midpoint the even index wins, so the boundary belongs
+    to the lower value when that one has an even index."""
+    v = np.asarray(v, dtype=np.float64)
+    return ((v > 0.25).astype(np.int64) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) + (v > 2.5)
+            + (v >= 3.5) + (v > 5.0))
+
+
+def quantize_fp4_rotated(y) -> tuple[np.ndarray, np.ndarray]:
+    """fp4 record of already-rotated vectors y [..., 256] -> (codes uint8 0..15, scales fp16 [..., 8])."""
+    y = np.asarray(y, dtype=np.float64)
+    b = y.reshape(y.shape[:-1] + (HEAD_DIM // Q4_BLOCK, Q4_BLOCK))
+    a = np.max(np.abs(b), axis=-1)
+    _, ex = np.frexp(a)                        # a = m * 2^ex, m in [0.5, 1): floor(log2 a) = ex - 1
+    e = np.clip(ex - 1 - 2, FP4_EMIN, FP4_EMAX)
+    d = np.where(a > 0, np.ldexp(1.0, e), 0.0)
+    v = np.abs(b) / np.where(d > 0, d, 1.0)[..., None]  # exact: d is a power of two
+    idx = np.where(d[..., None] > 0, fp4_index(v), 0)
+    c = idx + 8 * ((b < 0) & (idx > 0))
+    return c.reshape(y.shape).astype(np.uint8), fp16_rne(d)
+
+
+def quantize_fp4(x) -> tuple[np.ndarray, np.ndarray]:
+    """fp4 record of vectors x [..., 256]: rotate by H, then quantize."""
+    return quantize_fp4_rotated(rotate(x))
+
+
+def dequantize_fp4(codes, scales) -> np.ndarray:
+    """Rotated-domain values +-grid[c & 7] * d of an fp4 record."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = FP4_GRID[c & 7] * np.where(c & 8, -1.0, 1.0)
+    d = np.asarray(scales, dtype=np.float64)
+    b = mag.reshape(c.shape[:-1] + (HEAD_DIM // Q4_BLOCK, Q4_BLOCK))
+    return (b * d[..., None]).reshape(c.shape)
+
+
 def encode(x, kind: str):
-    return quantize_int8(x) if kind == KIND_INT8 else quantize_q4(x)
+    if kind == KIND_INT8:
+        return quantize_int8(x)
+    return quantize_q4(x) if kind == KIND_Q4 else quantize_fp4(x)
 
 
 def decode(codes, scales, kind: str):
-    return dequantize_int8(codes, scales) if kind == KIND_INT8 else dequantize_q4(codes, scales)
+    if kind == KIND_INT8:
+        return dequantize_int8(codes, scales)
+    return dequantize_q4(codes, scales) if kind == KIND_Q4 else dequantize_fp4(codes, scales)
 
 
 def record_bytes(kind: str) -> int:
