@@ -34,8 +34,9 @@
  * Byte layout of a page (fixed by this library; the pages name pages, blocks
  * and slots but no layout): a page holds 256 consecutive tokens of one
  * sequence and one layer, for every KV head h in order, the K plane of head h
- * then its V plane. Plane sizes: int8 67,584 B, q4 36,864 B, so a page is
- * 540,672 B (int8), 294,912 B (q4_0) or 417,792 B (k8v4) for 4 KV heads.
+ * then its V plane. Plane sizes: int8 67,584 B, q4 and fp4 36,864 B, so a page
+ * is 540,672 B (int8), 294,912 B (q4_0, fp4) or 417,792 B (k8v4) for 4 KV
+ * heads. fp4 records use the q4 byte layout below (4-bit codes, 8 fp16 scales).
  *   K plane (token-major): 256 code rows (256 B int8 / 128 B q4) then 256 rows
  *     of fp16 scales (4 int8 groups of 64 / 8 q4 blocks of 32). In a code row,
  *     the bytes of the eight 32-element blocks are split into four slices and
@@ -53,6 +54,13 @@
  *     ties), d = fp16_rne(-m / 8), c = clamp(floor(y / d + 1/2) + 8, 0, 15),
  *     d == 0 gives c = 8; value (c - 8) * d. H[i][j] = (-1)^popcount(i&j)/16.
  *   k8v4: K as int8 (not rotated), V as rotated q4_0.
+ *   fp4 per 32 elements of y = H x (a declared block-scaled 4-bit float format;
+ *     smzdm roundup post.smzdm.com/p/ad79lwwz, section "一、先修正一笔老账", lists
+ *     NVFP4 KV at the same 144 B per vector): a = max|y|; a == 0 gives d = 0 and
+ *     c = 0; else d = 2^e, e = clamp(floor(log2 a) - 2, -23, 13) (stored as an
+ *     exact fp16); c = the e2m1 grid index (values 0, .5, 1, 1.5, 2, 3, 4, 6) of
+ *     |y| / d rounded to nearest, ties to the even index, saturating at 6, plus
+ *     8 when y < 0 and the index is not 0; value +-grid[c & 7] * d.
  */
 #ifndef KVCACHE_H
 #define KVCACHE_H
@@ -82,6 +90,7 @@ extern "C" {
 #define KV_FMT_INT8 0  /* K and V int8, per-64 fp16 scales, 264 B per vector        */
 #define KV_FMT_Q4_0 1  /* K and V rotated by H, q4_0 blocks, 144 B per vector       */
 #define KV_FMT_K8V4 2  /* K int8 (unrotated), V rotated q4_0: 408 B per KV head      */
+#define KV_FMT_FP4  3  /* K and V rotated by H, e2m1 codes, 2^e block scales, 144 B   */
 
 /* Shape of one layer's cache. Supported: head_dim == 256, page_tokens == 256,
  * n_kv_heads >= 1, n_q_heads a multiple of n_kv_heads with at most 8 query
@@ -151,8 +160,8 @@ size_t kv_decode_workspace_bytes(const kv_shape* shape, int32_t batch,
  *
  * For each sequence b and query head h (KV head g = h / (n_q_heads /
  * n_kv_heads)), over its T = context_lens[b] tokens:
- *   q' = H q if K is rotated (q4_0) else q;  s_t = softmax_scale * <q', k^_t>;
- *   o' = sum_t softmax(s)_t v^_t;  out = H o' if V is rotated (q4_0, k8v4).
+ *   q' = H q if K is rotated (q4_0, fp4) else q;  s_t = softmax_scale * <q', k^_t>;
+ *   o' = sum_t softmax(s)_t v^_t;  out = H o' if V is rotated (q4_0, k8v4, fp4).
  * k^ and v^ are the dequantized records. T == 0 gives a zero output.
  * The work is split along the context ("split-K"): each split of
  * pages_per_split pages writes a partial (max, sum, weighted values) that a
@@ -443,7 +452,8 @@ int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, i
  *   kv_host_f64_to_f16: round a double to fp16 bits once, nearest-even.
  *   kv_host_encode_vector: record of one fp16 vector x[256] (raw fp16 bits)
  *     as the append kernel writes it: kind 0 = int8 (codes int8 x256,
- *     scales fp16 x4), kind 1 = q4 of H x (codes 0..15 x256, scales x8). */
+ *     scales fp16 x4), kind 1 = q4 of H x (codes 0..15 x256, scales x8),
+ *     kind 2 = fp4 of H x (codes 0..15 x256, power-of-two scales x8). */
 uint16_t kv_host_f64_to_f16(double x);
 int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales);
 

@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkvcache.so")
 
 KV_OK, KV_EINVAL, KV_EUNSUPPORTED, KV_EALIGN, KV_ENOSLOTS, KV_EHIP, KV_ESMALL = 0, -1, -2, -3, -4, -5, -6
 KV_STATUS_BAD_PAGE_ID, KV_STATUS_CONTEXT_CLAMPED = 1, 2
-KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4 = 0, 1, 2
-FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4}
+KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4, KV_FMT_FP4 = 0, 1, 2, 3
+FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4, "fp4": KV_FMT_FP4}
 
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",

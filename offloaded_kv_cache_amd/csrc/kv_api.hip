@@ -44,7 +44,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int check_shape(const kv_shape* s) {
   if (!s) return fail(KV_EINVAL, "shape is NULL");
-  if (s->format != KV_FMT_INT8 && s->format != KV_FMT_Q4_0 && s->format != KV_FMT_K8V4)
+  if (s->format != KV_FMT_INT8 && s->format != KV_FMT_Q4_0 && s->format != KV_FMT_K8V4 &&
+      s->format != KV_FMT_FP4)
     return fail(KV_EINVAL, "unknown format %d", s->format);
   if (s->head_dim != kHeadDim) return fail(KV_EUNSUPPORTED, "head_dim must be 256 (got %d)", s->head_dim);
   if (s->page_tokens != kPageTokens)
@@ -572,7 +573,7 @@ int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint1
     }
     return ok();
   }
-  if (kind == kQ4) {
+  if (kind == kQ4 || kind == kFp4) {
     double y[kHeadDim];
     for (int e = 0; e < kHeadDim; ++e) y[e] = f16_to_f64(x[e]);
     for (int len = 1; len < kHeadDim; len <<= 1)  // Sylvester butterflies, exact in fp64
@@ -583,6 +584,16 @@ int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint1
           y[j + len] = a - b;
         }
     for (int e = 0; e < kHeadDim; ++e) y[e] *= 0.0625;
+    if (kind == kFp4) {
+      for (int blk = 0; blk < 8; ++blk) {
+        double a = 0.0;
+        for (int e = 32 * blk; e < 32 * blk + 32; ++e) a = (y[e] < 0 ? -y[e] : y[e]) > a ? (y[e] < 0 ? -y[e] : y[e]) : a;
+        const int ex = fp4_block_exp(a);
+        scales[blk] = a == 0.0 ? (uint16_t)0 : fp16_pow2_bits(ex);
+        for (int e = 32 * blk; e < 32 * blk + 32; ++e) codes[e] = (uint8_t)(a == 0.0 ? 0 : fp4_code(y[e], ex));
+      }
+      return ok();
+    }
     for (int blk = 0; blk < 8; ++blk) {
       double m = y[32 * blk];
       for (int e = 32 * blk + 1; e < 32 * blk + 32; ++e) {
@@ -595,7 +606,7 @@ int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint1
     }
     return ok();
   }
-  return fail(KV_EINVAL, "kind must be 0 (int8) or 1 (q4)");
+  return fail(KV_EINVAL, "kind must be 0 (int8), 1 (q4) or 2 (fp4)");
 }
 
 }  // extern "C"

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     vbyte[kk] = vplane + (size_t)(lane + 64 * kk) * code_row_bytes(VK) + 16 * (row_lo >> 5) + (row_lo & 15);
   // with one token of the pair outside the chunk, wave 2 keeps the other nibble
   uint8_t old[4] = {0, 0, 0, 0};
-  if (VK == kQ4 && wave == 2 && !(in_lo && in_hi)) {
+  if (four_bit(VK) && wave == 2 && !(in_lo && in_hi)) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) old[kk] = *vbyte[kk];
   }
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void append_kernel(
       }
     }
   }
-  if (VK == kQ4) {
+  if (four_bit(VK)) {
     __syncthreads();
     if (wave == 2) {
 #pragma unroll
@@ -111,6 +111,11 @@ hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint1
       break;
     case KV_FMT_Q4_0:
       hipLaunchKernelGGL((append_kernel<kQ4, kQ4>), grid, block, 0, stream, k, v, n_tokens,
+                         start_pos, block_table, g0, pool, n_pool_pages, page_bytes, n_kv_heads,
+                         status);
+      break;
+    case KV_FMT_FP4:
+      hipLaunchKernelGGL((append_kernel<kFp4, kFp4>), grid, block, 0, stream, k, v, n_tokens,
                          start_pos, block_table, g0, pool, n_pool_pages, page_bytes, n_kv_heads,
                          status);
       break;

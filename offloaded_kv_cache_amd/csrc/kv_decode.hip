@@ -190,7 +190,7 @@ struct KTile {
 // A wave owns tpw = 256 / (waves per workgroup) tokens of a page for Q.K.
 template <int KK>
 __device__ inline uint32_t ktile_code_off(int tpw, int wave, int t, int col, int grp) {
-  return (uint32_t)((tpw * wave + 16 * t + col) * code_row_bytes(KK) + (KK == kQ4 ? 32 : 64) * grp);
+  return (uint32_t)((tpw * wave + 16 * t + col) * code_row_bytes(KK) + (four_bit(KK) ? 32 : 64) * grp);
 }
 template <int KK>
 __device__ inline uint32_t ktile_scale_off(int tpw, int wave, int t, int col) {
@@ -202,7 +202,7 @@ __device__ inline KTile load_ktile(Rsrc r, uint32_t coff, uint32_t soff) {
   KTile t;
   t.c0 = ld16(r, coff);
   t.c1 = ld16(r, coff + 16);
-  if (KK == kQ4) {
+  if (four_bit(KK)) {
     t.c2 = t.c3 = (u4){0, 0, 0, 0};
     t.d = ld16(r, soff);
   } else {
@@ -219,10 +219,33 @@ __device__ inline float scale_at(u4 d, int j) {  // fp16 scale j of a packed row
   return (float)__builtin_bit_cast(_Float16, (uint16_t)((j & 1) ? (w >> 16) : (w & 0xFFFFu)));
 }
 
+// Eight fp4 codes of one dword (byte w: low nibble = slot 2w, high nibble = slot
+// 2w + 1) as fp16 values times the power of two of `scale` (the conversion uses its
+// exponent), exact for the values of an fp4 record.
+__device__ inline h8 fp4_vals(uint32_t x, float scale) {
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, scale, 0);
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, scale, 1);
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, scale, 2);
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, scale, 3);
+  return (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 // Scores of one tile for the lane's two heads (rows 4grp..4grp+3 = head 2grp
 // hi, lo, head 2grp+1 hi, lo), in units of q.k (before the softmax scale).
 template <int KK>
 __device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], h8 qc, float& s0, float& s1) {
+  if constexpr (KK == kFp4) {
+    // block j: the lane's eight elements (32j + 4grp + w and 32j + 16 + 4grp + w) as the
+    // exact fp16 values of the record (scaled conversion by the block's 2^e); no scaling
+    // or offset is left, so all eight blocks accumulate in one MFMA chain
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t w[8] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = mfma(qa[j], fp4_vals(w[j], scale_at(t.d, j)), acc);
+    s0 = acc[0] + acc[1];
+    s1 = acc[2] + acc[3];
+    return;
+  }
   float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;  // hi and lo rows, units of 2^-24
   if (KK == kQ4) {
     const uint32_t w[8] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3]};
@@ -274,7 +297,7 @@ __device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], h8 qc, float& 
 // column tiles), all 256 tokens, plus the scales the wave turns into B parts.
 template <int VK>
 struct VShare {
-  u4 c[4][VK == kQ4 ? 2 : 4];  // per column tile: the lane's 32 (q4) / 64 (int8) code bytes
+  u4 c[4][four_bit(VK) ? 2 : 4];  // per column tile: the lane's 32 (4-bit) / 64 (int8) code bytes
   u2 s0, s1;                   // q4: 4 + 4 token scales; int8: s0, s1 = 8 consecutive scales
 };
 
@@ -284,19 +307,19 @@ struct VShare {
 template <int KK, int VK>
 __device__ inline uint32_t vcode_off(int epw, int wave, int lane, int nt) {
   const int grp = lane >> 4, col = lane & 15;
-  return (uint32_t)(plane_bytes(KK) + (epw * wave + 16 * nt + col) * code_row_bytes(VK) + (VK == kQ4 ? 32 : 64) * grp);
+  return (uint32_t)(plane_bytes(KK) + (epw * wave + 16 * nt + col) * code_row_bytes(VK) + (four_bit(VK) ? 32 : 64) * grp);
 }
 template <int VK>
 __device__ inline void load_vcodes(VShare<VK>& v, Rsrc r, uint32_t off, int nt) {
 #pragma unroll
-  for (int u = 0; u < (VK == kQ4 ? 2 : 4); ++u) v.c[nt][u] = ld16(r, off + 16 * u);
+  for (int u = 0; u < (four_bit(VK) ? 2 : 4); ++u) v.c[nt][u] = ld16(r, off + 16 * u);
 }
 
 // Byte offset (from the head's K plane) of the scales the lane turns into B parts.
 template <int KK, int VK>
 __device__ inline uint32_t vscale_off(int epw, int wave, int lane) {
   const uint32_t vs = plane_bytes(KK) + kHeadDim * code_row_bytes(VK);  // V scales
-  if (VK == kQ4) {
+  if (four_bit(VK)) {
     // B-part entry (block of the wave bb, MFMA i, lane group gq): tokens t_lo..+3 and
     // t_lo+16..+19; lanes past the wave's blocks read its first block again
     const int nb = epw / 32, bb = (lane >> 5) < nb ? (lane >> 5) : 0, i = (lane >> 2) & 7, gq = lane & 3;
@@ -310,7 +333,7 @@ __device__ inline uint32_t vscale_off(int epw, int wave, int lane) {
 }
 template <int VK>
 __device__ inline void load_vscales(VShare<VK>& v, Rsrc r, uint32_t off) {
-  if (VK == kQ4) {
+  if (four_bit(VK)) {
     v.s0 = ld8(r, off);
     v.s1 = ld8(r, off + 32);
   } else {
@@ -528,7 +551,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 
   // (all eight head slots are transformed, unused ones hold zeros, so that each step's
   // exchanges are in flight together)
-  if (KK == kQ4) {
+  if (four_bit(KK)) {
     // butterflies inside the wave
     butterfly<1>(qv, lane);
     butterfly<2>(qv, lane);
@@ -557,8 +580,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
   }
   __syncthreads();
-  {
-    // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8)
+  if (KK != kFp4) {
+    // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8),
+    // for the code offsets (fp4 codes carry no offset)
     constexpr int nb = KK == kQ4 ? 8 : 4, bl = kHeadDim / nb;
     if (tid < kMaxGroup * nb) {
       const int hh = tid / nb, j = tid % nb;
@@ -586,7 +610,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   for (int jj = 0; jj < 8 / NW; ++jj) {
     const int j = (8 / NW) * wave + jj;
     float f[8];
-    if (KK == kQ4) {
+    if (KK == kFp4) {
+      // slots [e, e+16, e+1, e+17, e+2, e+18, e+3, e+19] with e = 32j + 4grp (byte w of the
+      // lane's dword: low nibble element e + w, high nibble e + 16 + w)
+      const f4 lo4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp);
+      const f4 hi4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp + 16);
+      f[0] = lo4[0]; f[1] = hi4[0]; f[2] = lo4[1]; f[3] = hi4[1];
+      f[4] = lo4[2]; f[5] = hi4[2]; f[6] = lo4[3]; f[7] = hi4[3];
+    } else if (KK == kQ4) {
       // slots [e, e+2, e+16, e+18, e+1, e+3, e+17, e+19] with e = 32j + 4grp; high-nibble slots hold q/16
       const f4 lo4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp);
       const f4 hi4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp + 16) * 0.0625f;
@@ -615,7 +646,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   h8 qc;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const float f = (s < (KK == kQ4 ? 8 : 4)) ? lds.bsum[a_head][s] : 0.f;
+    const float f = (KK != kFp4 && s < (KK == kQ4 ? 8 : 4)) ? lds.bsum[a_head][s] : 0.f;
     const _Float16 hi = (_Float16)f;
     const _Float16 lo = (_Float16)(f - (float)hi);
     qc[s] = (a_live && grp == 0) ? (a_part ? lo : hi) : (_Float16)0;
@@ -673,7 +704,24 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     bool fast;
     {
       h8* dp = lds.dpart[wave];
-      if (VK == kQ4) {
+      if constexpr (VK == kFp4) {
+        // the scales of the lane's entry (block bb of the wave, MFMA i, lane group gq) in
+        // B slot order [t, t+16, t+1, t+17, t+2, t+18, t+3, t+19] (0 past the context);
+        // the products code * 2^e are exact, so every page takes the one path
+        const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
+        const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
+        u4 wv = {vsh.s0[0], vsh.s0[1], vsh.s1[0], vsh.s1[1]};  // tokens t..t+3, t+16..t+19
+        if (bb >= EPW / 32) wv = (u4){0u, 0u, 0u, 0u};
+        if (valid < kPageTokens) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (t_lo + (u & 3) + 16 * (u >> 2) >= valid) wv[u >> 1] &= (u & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+        const u4 sv = {__builtin_amdgcn_perm(wv[2], wv[0], 0x05040100u), __builtin_amdgcn_perm(wv[2], wv[0], 0x07060302u),
+                       __builtin_amdgcn_perm(wv[3], wv[1], 0x05040100u), __builtin_amdgcn_perm(wv[3], wv[1], 0x07060302u)};
+        dp[(bb * 8 + i) * 4 + gq] = __builtin_bit_cast(h8, sv);
+        fast = true;
+      } else if (VK == kQ4) {
         const int bb = lane >> 5, i = (lane >> 2) & 7, gq = lane & 3;
         const int t_lo = 32 * (2 * gq + (i >> 2)) + 4 * (i & 3);
         // slot u = scale of token t_lo + (u & 3) + 16 (u >> 2): half (u & 1) of word u >> 1;
@@ -760,7 +808,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       // which a lane's V code bytes come (q4: 4 + 4 nibble tokens, int8: 8 bytes)
       const int token = TPW * wave + 16 * t + col, kg = token >> 6, o = token & 63;
       int i, slot;
-      if (VK == kQ4) {
+      if (VK == kFp4) {  // byte w of a dword: low nibble token t + w, high nibble t + 16 + w
+        i = 4 * (o >> 5) + ((o & 15) >> 2);
+        slot = 2 * (o & 3) + ((o >> 4) & 1);
+      } else if (VK == kQ4) {
         i = 4 * (o >> 5) + ((o & 15) >> 2);
         slot = 4 * ((o >> 4) & 1) + (o & 3);
       } else {
@@ -794,6 +845,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     const h8* dp = lds.dpart[wave];
 #pragma unroll
     for (int hf = 0; hf < HFN; ++hf) {
+      if constexpr (VK == kFp4) {
+        // B = code value (conversion at scale 1) times the token's 2^e: exact fp16
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const h8 pa = lds.afrag[i][lane];
+          const h8 sc = dp[(hf * 8 + i) * 4 + grp];
+          const h8 b0 = fp4_vals(vsh.c[2 * hf][i >> 2][i & 3], 1.0f) * sc;
+          const h8 b1 = fp4_vals(vsh.c[2 * hf + 1][i >> 2][i & 3], 1.0f) * sc;
+          oacc[2 * hf] = mfma(pa, b0, oacc[2 * hf]);
+          oacc[2 * hf + 1] = mfma(pa, b1, oacc[2 * hf + 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
       if (fast) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -858,6 +922,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      }
       // this half's code registers now take the next page's codes
       load_vcodes<VK>(vsh, nr, voff[2 * hf], 2 * hf);
       load_vcodes<VK>(vsh, nr, voff[2 * hf + 1], 2 * hf + 1);
@@ -878,7 +943,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int t = 0; t < NTW; ++t) po[r][t] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
-  if (VK == kQ4) {
+  if (four_bit(VK)) {
     // V is stored rotated: the partial is rotated back here (H is linear, so the merge of
     // rotated partials is the rotated merge). Element bits 0-3 (col) between lanes,
     // the tile bits inside the lane, the wave bits through LDS.
@@ -1085,6 +1150,7 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hip
     switch (a.fmt) {
       case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream, start, stop); break;
       case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream, start, stop); break;
+      case KV_FMT_FP4: e = launch_split<kFp4, kFp4>(a, stream, start, stop); break;
       default: e = launch_split<kInt8, kQ4>(a, stream, start, stop); break;
     }
     if (e != hipSuccess) return e;

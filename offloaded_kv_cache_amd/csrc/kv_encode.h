@@ -116,7 +116,7 @@ __device__ inline int q4_code_fast(double y, double d) {
 
 // The record of one vector: codes of the lane's elements and the scales.
 // int8: scale[k] is group k (elements 64k..64k+63 are exactly register k).
-// q4: scale of block (lane >> 5) + 2k lives in register k of every lane of
+// q4, fp4: scale of block (lane >> 5) + 2k lives in register k of every lane of
 // that half-wave.
 template <int KIND, bool DPP = true>
 __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code)[4],
@@ -134,6 +134,24 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
       scale[k] = DPP ? f64_to_f16_fast(a[k] / 127.0) : f64_to_f16_rne(a[k] / 127.0);
       const double d = f16_to_f64(scale[k]);
       code[k] = DPP ? int8_code_fast(x[k], d) : int8_code(x[k], d);
+    }
+  } else if (KIND == kFp4) {
+    wht256<DPP>(x, lane);
+    // per block (the 32 lanes of a half-wave, register k): largest |y|, its exponent,
+    // the power-of-two scale and the grid index of each element (exact comparisons)
+    double m[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
+    max_stage<1, DPP>(m, lane);
+    max_stage<2, DPP>(m, lane);
+    max_stage<4, DPP>(m, lane);
+    max_stage<8, DPP>(m, lane);
+    max_stage<16, DPP>(m, lane);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = fp4_block_exp(m[k]);
+      scale[k] = m[k] == 0.0 ? (uint16_t)0 : fp16_pow2_bits(e);
+      code[k] = m[k] == 0.0 ? 0 : fp4_code(x[k], e);
     }
   } else {
     wht256<DPP>(x, lane);

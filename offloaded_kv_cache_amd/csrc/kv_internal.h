@@ -17,19 +17,25 @@ constexpr int kPageTokens = 256;
 constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxGroup = 8;  // query heads per KV head handled by one MFMA row tile
 
-enum RecordKind : int { kInt8 = 0, kQ4 = 1 };
+enum RecordKind : int { kInt8 = 0, kQ4 = 1, kFp4 = 2 };
+// q4_0 and fp4 records: rotated by H, 4-bit codes in the same byte layout, 8 fp16 scales
+__host__ __device__ constexpr bool four_bit(int kind) { return kind != kInt8; }
 
 __host__ __device__ constexpr int code_row_bytes(int kind) { return kind == kInt8 ? 256 : 128; }
 __host__ __device__ constexpr int n_scales(int kind) { return kind == kInt8 ? 4 : 8; }
 __host__ __device__ constexpr int plane_bytes(int kind) {
   return kPageTokens * code_row_bytes(kind) + kPageTokens * n_scales(kind) * 2;
 }
-__host__ __device__ constexpr int k_kind(int fmt) { return fmt == KV_FMT_Q4_0 ? kQ4 : kInt8; }
-__host__ __device__ constexpr int v_kind(int fmt) { return fmt == KV_FMT_INT8 ? kInt8 : kQ4; }
+__host__ __device__ constexpr int k_kind(int fmt) {
+  return fmt == KV_FMT_Q4_0 ? kQ4 : (fmt == KV_FMT_FP4 ? kFp4 : kInt8);
+}
+__host__ __device__ constexpr int v_kind(int fmt) {
+  return fmt == KV_FMT_INT8 ? kInt8 : (fmt == KV_FMT_FP4 ? kFp4 : kQ4);
+}
 // Waves per workgroup of the split-K decode kernel: 4 (two workgroups per CU) for
 // 4-bit K; 8 (one workgroup per CU, half the registers per wave) for int8 K, whose
 // tiles are twice as large.
-__host__ __device__ constexpr int split_waves(int k_kind_) { return k_kind_ == kQ4 ? 4 : 8; }
+__host__ __device__ constexpr int split_waves(int k_kind_) { return four_bit(k_kind_) ? 4 : 8; }
 __host__ __device__ constexpr int64_t head_stride(int fmt) {
   return plane_bytes(k_kind(fmt)) + plane_bytes(v_kind(fmt));
 }
@@ -97,6 +103,29 @@ hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint1
                          int64_t n_tokens, int64_t start_pos, const int32_t* block_table,
                          int32_t n_table, uint8_t* pool, int64_t n_pool_pages,
                          int32_t* status, hipStream_t stream);
+
+// fp4 record helpers (rules in include/kvcache.h). a = max |y| of a block (exact, a
+// normal double or 0): the block exponent clamp(floor(log2 a) - 2, -23, 13).
+__host__ __device__ inline int fp4_block_exp(double a) {
+  const int ex = (int)((__builtin_bit_cast(uint64_t, a) >> 52) & 0x7FF) - 1023;  // floor(log2 a)
+  const int e = ex - 2;
+  return e < -23 ? -23 : (e > 13 ? 13 : e);
+}
+// 2^e as fp16 bits (exact for -24 <= e <= 15: normal from 2^-14, subnormal below).
+__host__ __device__ inline uint16_t fp16_pow2_bits(int e) {
+  return e >= -14 ? (uint16_t)((e + 15) << 10) : (uint16_t)(1u << (e + 24));
+}
+// 2^e as a double (exact).
+__host__ __device__ inline double f64_pow2(int e) {
+  return __builtin_bit_cast(double, (uint64_t)(e + 1023) << 52);
+}
+// Code of y in a block with exponent e (d = 2^e > 0): the e2m1 grid index of |y| / d,
+// nearest with ties to the even index, saturating at 6; plus 8 for y < 0 (index > 0).
+__host__ __device__ inline int fp4_code(double y, int e) {
+  const double v = (y < 0 ? -y : y) * f64_pow2(-e);  // exact
+  const int idx = (v > 0.25) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) + (v > 2.5) + (v >= 3.5) + (v > 5.0);
+  return idx + ((y < 0 && idx > 0) ? 8 : 0);
+}
 
 struct DecodeArgs {
   int fmt;

@@ -18,7 +18,7 @@ from gpu_helpers import Sequence, assert_close, fmt_id, oracle_out, oracle_recor
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["int8", "q4_0", "k8v4"]
+FMTS = ["int8", "q4_0", "k8v4", "fp4"]
 
 
 def to_dev(a, dev, dtype=None):
@@ -101,11 +101,34 @@ def rounding_edge_vectors(n_kv_heads=4):
     return np.stack(vs)
 
 
+def fp4_edge_vectors(n_kv_heads=4):
+    """fp4 block-scale and grid edge cases. With a + b = 1024 the block maximum is
+    64 = 4 d (d = 16) and the other element sits at (a - b) / 256 in units of d: the
+    grid midpoints 0.25, 0.75, 1.25, 1.75, 2.5 and 3.5 (ties to the even index). With
+    a + b = 1920 the maximum 7.5 d saturates and (a - b) = 1280 is the tie 5.0. A tiny
+    pair puts the block exponent below its floor (-23); a Sylvester row of 4096s gives
+    y = 65,536 in one slot, above the exponent's ceiling (13), so the codes saturate."""
+    pairs = [(544, 480), (608, 416), (672, 352), (736, 288), (832, 192), (960, 64),
+             (1600, 320), (2.0 ** -18, 2.0 ** -19), (2.0 ** -17, -(2.0 ** -20))]
+    vs = []
+    for a, b in pairs:
+        x = np.zeros((n_kv_heads, 256), np.float16)
+        x[:, 0], x[:, 1] = a, b
+        vs.append(x)
+    j = np.arange(256)
+    x = np.zeros((n_kv_heads, 256), np.float16)
+    for h in range(n_kv_heads):
+        kk = 3 + 41 * h
+        x[h] = 4096.0 * (1.0 - 2.0 * (np.array([bin(t & kk).count("1") for t in j]) & 1))
+    vs.append(x)
+    return np.stack(vs)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_append_rounding_edges_bitexact(gpu, fmt):
     """Scale and code rounding edge cases appended one token at a time and as a chunk,
     bit for bit against the oracle's records."""
-    sp = np.concatenate([rounding_edge_vectors(), special_vectors()])
+    sp = np.concatenate([rounding_edge_vectors(), special_vectors(), fp4_edge_vectors()])
     T = len(sp)
     s = K.shape(fmt)
     pb = K.page_bytes(s)

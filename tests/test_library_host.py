@@ -69,7 +69,7 @@ def test_f64_to_f16_matches_single_rounding():
     assert N.host_f64_to_f16(np.nan) & 0x7C00 == 0x7C00
 
 
-@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("kind", [0, 1, 2])
 def test_host_records_match_oracle(kind):
     rng = np.random.default_rng(10 + kind)
     xs = [(rng.standard_normal(256) * np.where(rng.random(256) < 0.03, 20, 1)).astype(np.float16)
@@ -86,8 +86,11 @@ def test_host_records_match_oracle(kind):
         if kind == 0:
             c, d = records.quantize_int8(x.astype(np.float64))
             assert np.array_equal(codes.view(np.int8), c)
-        else:
+        elif kind == 1:
             c, d = records.quantize_q4(x.astype(np.float64))
+            assert np.array_equal(codes, c)
+        else:
+            c, d = records.quantize_fp4(x.astype(np.float64))
             assert np.array_equal(codes, c)
         assert np.array_equal(scales.view(np.uint16), d.view(np.uint16))
 
