@@ -23,7 +23,8 @@ Other workloads (parity-test shapes, not the metric line): --workload c1
 (1 layer, 4,096 tokens, q4_0), c2 (16 layers, 32,768, int8), c4 (16 layers,
 4 sequences of 262,144 / 198,000 / 65,536 / 8,192 tokens, k8v4), c5
 (16 layers, 1,048,576-token int8 host pool, 128 resident slots per layer,
-2,048-token selection per step with ~30% misses, gathered zero-copy).
+2,048-token selection per step with ~30% misses, gathered zero-copy), c3fp4
+(the default shape with fp4 records: e2m1 codes, power-of-two block scales).
 """
 
 from __future__ import annotations
@@ -47,6 +48,7 @@ WORKLOADS = {
     "c2": dict(fmt="int8", layers=16, lens=[32768], cfg=2),
     "c3": dict(fmt="q4_0", layers=16, lens=[131072], cfg=3),
     "c4": dict(fmt="k8v4", layers=16, lens=[262144, 198000, 65536, 8192], cfg=4),
+    "c3fp4": dict(fmt="fp4", layers=16, lens=[131072], cfg=3),
 }
 
 
@@ -55,7 +57,7 @@ def log(*a):
 
 
 def kv_bytes_per_token(fmt: str, n_kv_heads: int = 4) -> int:
-    rec = {"int8": (264, 264), "q4_0": (144, 144), "k8v4": (264, 144)}[fmt]
+    rec = {"int8": (264, 264), "q4_0": (144, 144), "k8v4": (264, 144), "fp4": (144, 144)}[fmt]
     return n_kv_heads * sum(rec)
 
 
@@ -516,8 +518,9 @@ def counter_traffic(workload: str):
 
     The summary records the code hash (kernel_code_hash) of the kernel its counters
     were taken with; a kernel changed since then gives None."""
-    path = os.path.join(ROOT, "profiles", "decode_q4_0_128k_hbm_bytes.txt")
-    if workload != "c3" or not os.path.exists(path):
+    name = {"c3": "decode_q4_0_128k_hbm_bytes.txt", "c3fp4": "decode_fp4_128k_hbm_bytes.txt"}.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else None
+    if path is None or not os.path.exists(path):
         return None
     sha = traffic = None
     for line in open(path):
@@ -602,7 +605,7 @@ def main():
     if args.workload == "c5":
         res = run_streaming(args, dev)
         print(json.dumps({
-            "metric": "KV GB/s streamed in decode attention (% of 8 TB/s HBM) at 128K q4_0",
+            "metric": "KV GB/s streamed in decode attention (% of 8 TB/s HBM), c5 workload (pages gathered from a host pool)",
             "value": round(res["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "int8 KV, fp32 accumulate", "data": "synthetic",
@@ -634,8 +637,11 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, wl, dev, state)
     fmt = wl["fmt"]
+    metric = "KV GB/s streamed in decode attention (% of 8 TB/s HBM) at 128K q4_0"
+    if args.workload != "c3":
+        metric = f"KV GB/s streamed in decode attention (% of 8 TB/s HBM), {args.workload} workload"
     line = {
-        "metric": "KV GB/s streamed in decode attention (% of 8 TB/s HBM) at 128K q4_0",
+        "metric": metric,
         "value": round(res["value"], 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -646,12 +652,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"q4_0": "q4_0 KV, fp32 accumulate", "int8": "int8 KV, fp32 accumulate",
-                  "k8v4": "int8 K / q4_0 V, fp32 accumulate"}[fmt],
+                  "k8v4": "int8 K / q4_0 V, fp32 accumulate", "fp4": "fp4 (e2m1) KV, fp32 accumulate"}[fmt],
         "data": "synthetic",
         "config": {"workload": {"c1": "1 layer, 4,096-token q4_0 context",
                                 "c2": "16 layers, 32,768-token int8 context",
                                 "c3": "16 layers, 131,072-token q4_0 context (append 1 token + decode per layer)",
-                                "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4"}[args.workload],
+                                "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4",
+                                "c3fp4": "16 layers, 131,072-token fp4 context (append 1 token + decode per layer)"}[args.workload],
                    "layers": wl["layers"], "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256,
                    "page_tokens": 256, "batch": len(wl["lens"]), "context": wl["lens"],
                    "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto",
