@@ -13,6 +13,8 @@ any reference to how the GPU library computes offsets:
   q4 and fp4 36,864 B (256 x 128 code bytes + 256 x 8 fp16 scales). So a page
   is 540,672 B (int8), 294,912 B (q4_0, fp4) or 417,792 B (k8v4) for 4 KV
   heads. The fp4 record uses the q4 byte layout below (4-bit codes, 8 scales).
+  fp8: 66,048 B (256 x 256 codes + 256 x 1 fp16 scale), 528,384 B a page; its
+  code bytes are placed exactly like int8 codes, with one scale per token.
 * K plane, token-major. Codes: 256 rows (one per token) of 256 B (int8) or
   128 B (q4), then scales: 256 rows of 4 (int8) or 8 (q4) little-endian fp16.
   Inside a code row the bytes of each 32-element block are spread over four
@@ -22,8 +24,9 @@ any reference to how the GPU library computes offsets:
     int8: byte 64*s + 8*j + w (w = 0..7) = code[32j + 8s + w]
 * V plane, element-major (transposed). Codes: 256 rows (one per head
   element) holding that element for all 256 tokens, then scales: 8 (q4) or
-  4 (int8) rows of 256 fp16, one row per block / group, one entry per token.
-    int8: byte t of row e = code of token t, element e
+  4 (int8) rows of 256 fp16, one row per block / group, one entry per token
+  (fp8: one row).
+    int8, fp8: byte t of row e = code of token t, element e
     q4:   byte 16*G + i of row e (G = 0..7, i = 0..15) =
           code[token 32G + i] | code[token 32G + 16 + i] << 4 (element e)
 
@@ -35,17 +38,18 @@ from __future__ import annotations
 
 import numpy as np
 
-from .records import HEAD_DIM, KIND_FP4, KIND_INT8, KIND_Q4, kinds
+from .records import HEAD_DIM, KIND_FP4, KIND_FP8, KIND_INT8, KIND_Q4, kinds
 
 PAGE_TOKENS = 256
+BYTE_KINDS = (KIND_INT8, KIND_FP8)  # one byte per code
 
 
 def n_scales(kind: str) -> int:
-    return 4 if kind == KIND_INT8 else 8
+    return {KIND_INT8: 4, KIND_FP8: 1}.get(kind, 8)
 
 
 def code_row_bytes(kind: str) -> int:
-    return 256 if kind == KIND_INT8 else 128
+    return 256 if kind in BYTE_KINDS else 128
 
 
 def plane_bytes(kind: str) -> int:
@@ -59,7 +63,7 @@ def page_bytes(fmt: int, n_kv_heads: int) -> int:
 
 def _k_row_maps(kind: str):
     """For each byte of a K code row: the element(s) it holds (built from the loops of the spec)."""
-    if kind == KIND_INT8:
+    if kind in BYTE_KINDS:
         elem = np.zeros(256, np.int64)
         for s in range(4):
             for j in range(8):
@@ -76,7 +80,7 @@ def _k_row_maps(kind: str):
     return lo, hi
 
 
-_KMAP = {k: _k_row_maps(k) for k in (KIND_INT8, KIND_Q4, KIND_FP4)}
+_KMAP = {k: _k_row_maps(k) for k in (KIND_INT8, KIND_Q4, KIND_FP4, KIND_FP8)}
 
 
 def _k_row_bytes(codes: np.ndarray, kind: str) -> np.ndarray:
@@ -84,6 +88,8 @@ def _k_row_bytes(codes: np.ndarray, kind: str) -> np.ndarray:
     a, b = _KMAP[kind]
     if kind == KIND_INT8:
         return codes.astype(np.int8).view(np.uint8)[..., a]
+    if kind == KIND_FP8:
+        return codes.astype(np.uint8)[..., a]
     c = codes.astype(np.uint8)
     return c[..., a] | (c[..., b] << 4)
 
@@ -96,6 +102,9 @@ def _k_row_codes(rows: np.ndarray, kind: str) -> np.ndarray:
         out[..., a] = rows.view(np.int8)
         return out
     out = np.zeros(rows.shape[:-1] + (HEAD_DIM,), np.uint8)
+    if kind == KIND_FP8:
+        out[..., a] = rows
+        return out
     out[..., a] = rows & 0xF
     out[..., b] = rows >> 4
     return out
@@ -106,6 +115,8 @@ def _v_rows(codes_page: np.ndarray, kind: str) -> np.ndarray:
     t = codes_page.T  # [elem, tok]
     if kind == KIND_INT8:
         return np.ascontiguousarray(t.astype(np.int8).view(np.uint8))
+    if kind == KIND_FP8:
+        return np.ascontiguousarray(t.astype(np.uint8))
     c = t.astype(np.uint8)
     out = np.zeros((HEAD_DIM, 128), np.uint8)
     for g in range(8):
@@ -118,6 +129,8 @@ def _v_codes(rows: np.ndarray, kind: str) -> np.ndarray:
     """Inverse of ``_v_rows``: [256 elem, R] -> [256 tok, 256 elem]."""
     if kind == KIND_INT8:
         return np.ascontiguousarray(rows.view(np.int8).T)
+    if kind == KIND_FP8:
+        return np.ascontiguousarray(rows.T)
     c = np.zeros((HEAD_DIM, PAGE_TOKENS), np.uint8)
     for g in range(8):
         for i in range(16):
@@ -153,7 +166,7 @@ def pack_pages(k_codes, k_scales, v_codes, v_scales, fmt: int) -> np.ndarray:
             krow = _k_row_bytes(kc[sl, h], kk)  # [256, R]
             kcb = krow.size
             out[p, base:base + kcb] = krow.reshape(-1)
-            out[p, base + kcb:base + pk] = ks[sl, h].reshape(-1).view(np.uint8)
+            out[p, base + kcb:base + pk] = np.ascontiguousarray(ks[sl, h]).reshape(-1).view(np.uint8)
             vbase = base + pk
             vrow = _v_rows(vc[sl, h], vk)  # [256, R]
             vcb = vrow.size

@@ -1,4 +1,4 @@
-"""The int8, q4_0 and fp4 vector records (oracle).
+"""The int8, q4_0, fp4 and fp8 vector records (oracle).
 
 Strata page, section "三种 KV 格式横向对比": int8 (the default, 1,056 B per
 token per layer for the K and V of two KV heads, i.e. 264 B per 256-element
@@ -50,6 +50,21 @@ codes, in q4_0's byte layout):
   values above 6 to 6 (saturation). The code is the grid index (0..7), plus
   8 (the sign bit) when y_j < 0 and the index is not 0.
   Dequantized (rotated-domain) value: +-grid[code & 7] * d.
+
+fp8 record (the same roundup section lists an FP8 KV format at 516 B per
+position, i.e. 258 B per vector: 256 one-byte codes and one 2-byte scale).
+Declared here: not rotated (like int8), one scale for the whole vector, codes
+in the OCP FP8 E4M3 encoding (1 sign, 4 exponent bits with bias 7, 3 mantissa
+bits; exponent field 0 holds the subnormals m * 2^-9; 0x7F and 0xFF are NaN, so
+the largest value is 448 = 1.75 * 2^8; no infinities):
+  a = max |x_j|; d = fp16 round-to-nearest-even of the exact quotient a/448
+  (the quotient in fp64 is never within its rounding error of an fp16 tie
+  unless it is one: 448 = 7 * 64, and a/7 either terminates or repeats 001);
+  d == 0 -> all codes 0. Otherwise |x_j| / d (exact decision in fp64, as for
+  int8) goes to the nearest E4M3 magnitude, ties to the even code (even
+  mantissa), magnitudes beyond 448 to 448 (saturation); the sign bit 0x80 is
+  set when x_j < 0 and the magnitude code is not 0. Dequantized value
+  +-E4M3(code & 0x7F) * d.
 """
 
 from __future__ import annotations
@@ -58,10 +73,10 @@ import numpy as np
 
 from .hadamard import rotate
 
-FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_FP4 = 0, 1, 2, 3
-FORMATS = {"int8": FMT_INT8, "q4_0": FMT_Q4_0, "k8v4": FMT_K8V4, "fp4": FMT_FP4}
+FMT_INT8, FMT_Q4_0, FMT_K8V4, FMT_FP4, FMT_FP8 = 0, 1, 2, 3, 4
+FORMATS = {"int8": FMT_INT8, "q4_0": FMT_Q4_0, "k8v4": FMT_K8V4, "fp4": FMT_FP4, "fp8": FMT_FP8}
 
-KIND_INT8, KIND_Q4, KIND_FP4 = "int8", "q4", "fp4"
+KIND_INT8, KIND_Q4, KIND_FP4, KIND_FP8 = "int8", "q4", "fp4", "fp8"
 ROTATED_KINDS = (KIND_Q4, KIND_FP4)
 FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 FP4_EMIN, FP4_EMAX = -23, 13
@@ -81,6 +96,8 @@ def kinds(fmt: int):
         return KIND_INT8, KIND_Q4
     if fmt == FMT_FP4:
         return KIND_FP4, KIND_FP4
+    if fmt == FMT_FP8:
+        return KIND_FP8, KIND_FP8
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -202,20 +219,63 @@ def dequantize_fp4(codes, scales) -> np.ndarray:
     return (b * d[..., None]).reshape(c.shape)
 
 
+def e4m3_magnitudes() -> np.ndarray:
+    """Values of the 127 non-negative finite E4M3 codes 0x00..0x7E, in code order
+    (which is increasing order): exponent field e = code >> 3, mantissa m = code & 7;
+    e == 0: m * 2^-9, else (1 + m/8) * 2^(e - 7)."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+
+
+E4M3 = e4m3_magnitudes()
+FP8_MAX = float(E4M3[-1])  # 448
+
+
+def e4m3_code(v) -> np.ndarray:
+    """Magnitude code (0..126) of exact values v >= 0: the nearest E4M3 magnitude, ties
+    to the even code, beyond 448 -> 448."""
+    v = np.asarray(v, dtype=np.float64)
+    hi = np.clip(np.searchsorted(E4M3, v), 1, 126)   # E4M3[hi - 1] < v <= E4M3[hi] inside the range
+    lo = hi - 1
+    dl, dh = v - E4M3[lo], E4M3[hi] - v
+    pick_hi = (dh < dl) | ((dh == dl) & (hi % 2 == 0))
+    c = np.where(pick_hi, hi, lo)
+    return np.where(v >= FP8_MAX, 126, np.where(v <= 0, 0, c))
+
+
+def quantize_fp8(x) -> tuple[np.ndarray, np.ndarray]:
+    """fp8 record of vectors x [..., 256] -> (codes uint8 [..., 256], scales fp16 [..., 1])."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.max(np.abs(x), axis=-1, keepdims=True)
+    d16 = fp16_rne(a / FP8_MAX)
+    d = d16.astype(np.float64)
+    mag = np.where(d != 0, e4m3_code(np.abs(x) / np.where(d != 0, d, 1.0)), 0)
+    c = mag + 0x80 * ((x < 0) & (mag > 0))
+    return c.astype(np.uint8), d16
+
+
+def dequantize_fp8(codes, scales) -> np.ndarray:
+    """Values +-E4M3(c & 0x7F) * d of an fp8 record (codes 0x7F / 0xFF, NaN, never occur)."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = E4M3[np.minimum(c & 0x7F, 126)] * np.where(c & 0x80, -1.0, 1.0)
+    return mag * np.asarray(scales, dtype=np.float64)
+
+
 def encode(x, kind: str):
-    if kind == KIND_INT8:
-        return quantize_int8(x)
-    return quantize_q4(x) if kind == KIND_Q4 else quantize_fp4(x)
+    return {KIND_INT8: quantize_int8, KIND_Q4: quantize_q4, KIND_FP4: quantize_fp4,
+            KIND_FP8: quantize_fp8}[kind](x)
 
 
 def decode(codes, scales, kind: str):
-    if kind == KIND_INT8:
-        return dequantize_int8(codes, scales)
-    return dequantize_q4(codes, scales) if kind == KIND_Q4 else dequantize_fp4(codes, scales)
+    return {KIND_INT8: dequantize_int8, KIND_Q4: dequantize_q4, KIND_FP4: dequantize_fp4,
+            KIND_FP8: dequantize_fp8}[kind](codes, scales)
 
 
 def record_bytes(kind: str) -> int:
     """Bytes of one 256-element vector record: codes plus fp16 scales."""
     if kind == KIND_INT8:
         return HEAD_DIM + 2 * (HEAD_DIM // INT8_GROUP)
+    if kind == KIND_FP8:
+        return HEAD_DIM + 2
     return HEAD_DIM // 2 + 2 * (HEAD_DIM // Q4_BLOCK)
