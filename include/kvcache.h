@@ -34,9 +34,11 @@
  * Byte layout of a page (fixed by this library; the pages name pages, blocks
  * and slots but no layout): a page holds 256 consecutive tokens of one
  * sequence and one layer, for every KV head h in order, the K plane of head h
- * then its V plane. Plane sizes: int8 67,584 B, q4 and fp4 36,864 B, so a page
- * is 540,672 B (int8), 294,912 B (q4_0, fp4) or 417,792 B (k8v4) for 4 KV
- * heads. fp4 records use the q4 byte layout below (4-bit codes, 8 fp16 scales).
+ * then its V plane. Plane sizes: int8 67,584 B, q4 and fp4 36,864 B, fp8
+ * 66,048 B, so a page is 540,672 B (int8), 294,912 B (q4_0, fp4), 417,792 B
+ * (k8v4) or 528,384 B (fp8) for 4 KV heads. fp4 records use the q4 byte layout
+ * below (4-bit codes, 8 fp16 scales); fp8 records the int8 byte layout (one byte
+ * per code) with one fp16 scale per token (one scale row in the V plane).
  *   K plane (token-major): 256 code rows (256 B int8 / 128 B q4) then 256 rows
  *     of fp16 scales (4 int8 groups of 64 / 8 q4 blocks of 32). In a code row,
  *     the bytes of the eight 32-element blocks are split into four slices and
@@ -61,6 +63,13 @@
  *     exact fp16); c = the e2m1 grid index (values 0, .5, 1, 1.5, 2, 3, 4, 6) of
  *     |y| / d rounded to nearest, ties to the even index, saturating at 6, plus
  *     8 when y < 0 and the index is not 0; value +-grid[c & 7] * d.
+ *   fp8 per vector, not rotated (a declared block-scaled 8-bit float format; the
+ *     same roundup section lists FP8 KV at 516 B per position, 258 B per vector):
+ *     d = fp16_rne(max|x| / 448), d == 0 gives c = 0; else c = the OCP E4M3 code
+ *     (1 sign, 4 exponent bits of bias 7, 3 mantissa bits; 0x7F / 0xFF are NaN
+ *     and never written) of |x| / d rounded to nearest, ties to the even code,
+ *     beyond 448 to 448, with the sign bit when x < 0 and the magnitude is not
+ *     0; value +-E4M3(c) * d.
  */
 #ifndef KVCACHE_H
 #define KVCACHE_H
@@ -91,6 +100,7 @@ extern "C" {
 #define KV_FMT_Q4_0 1  /* K and V rotated by H, q4_0 blocks, 144 B per vector       */
 #define KV_FMT_K8V4 2  /* K int8 (unrotated), V rotated q4_0: 408 B per KV head      */
 #define KV_FMT_FP4  3  /* K and V rotated by H, e2m1 codes, 2^e block scales, 144 B   */
+#define KV_FMT_FP8  4  /* K and V E4M3 codes, one fp16 scale per vector, 258 B       */
 
 /* Shape of one layer's cache. Supported: head_dim == 256, page_tokens == 256,
  * n_kv_heads >= 1, n_q_heads a multiple of n_kv_heads with at most 8 query
@@ -453,7 +463,8 @@ int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, i
  *   kv_host_encode_vector: record of one fp16 vector x[256] (raw fp16 bits)
  *     as the append kernel writes it: kind 0 = int8 (codes int8 x256,
  *     scales fp16 x4), kind 1 = q4 of H x (codes 0..15 x256, scales x8),
- *     kind 2 = fp4 of H x (codes 0..15 x256, power-of-two scales x8). */
+ *     kind 2 = fp4 of H x (codes 0..15 x256, power-of-two scales x8),
+ *     kind 3 = fp8 (E4M3 codes x256, one scale). */
 uint16_t kv_host_f64_to_f16(double x);
 int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint16_t* scales);
 

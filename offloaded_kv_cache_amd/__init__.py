@@ -9,7 +9,7 @@ not been built (``python offloaded_kv_cache_amd/build.py``).
 """
 
 from ._native import (  # noqa: F401
-    FORMATS, KV_FMT_FP4, KV_FMT_INT8, KV_FMT_K8V4, KV_FMT_Q4_0, KV_STATUS_BAD_PAGE_ID,
+    FORMATS, KV_FMT_FP4, KV_FMT_FP8, KV_FMT_INT8, KV_FMT_K8V4, KV_FMT_Q4_0, KV_STATUS_BAD_PAGE_ID,
     KV_STATUS_CONTEXT_CLAMPED, KVError, KVShape, Residency, append_decode, append_quantize,
     decode_attention, decode_attention_mq, decode_mq_workspace_bytes, decode_split_pages, decode_workspace_bytes, gather_pages, gather_pages_layers,
     host_encode_vector,

@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkvcache.so")
 
 KV_OK, KV_EINVAL, KV_EUNSUPPORTED, KV_EALIGN, KV_ENOSLOTS, KV_EHIP, KV_ESMALL = 0, -1, -2, -3, -4, -5, -6
 KV_STATUS_BAD_PAGE_ID, KV_STATUS_CONTEXT_CLAMPED = 1, 2
-KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4, KV_FMT_FP4 = 0, 1, 2, 3
-FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4, "fp4": KV_FMT_FP4}
+KV_FMT_INT8, KV_FMT_Q4_0, KV_FMT_K8V4, KV_FMT_FP4, KV_FMT_FP8 = 0, 1, 2, 3, 4
+FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4, "fp4": KV_FMT_FP4,
+           "fp8": KV_FMT_FP8}
 
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
@@ -410,5 +411,5 @@ def host_encode_vector(kind: int, x: np.ndarray):
     scales = np.zeros(8, np.uint16)
     _check(lib.kv_host_encode_vector(kind, xb.ctypes.data_as(C.c_void_p),
                                      codes.ctypes.data_as(C.c_void_p), scales.ctypes.data_as(C.c_void_p)))
-    n = 4 if kind == 0 else 8
+    n = {0: 4, 3: 1}.get(kind, 8)
     return codes, scales[:n].view(np.float16)

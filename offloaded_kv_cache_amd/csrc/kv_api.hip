@@ -45,7 +45,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_shape(const kv_shape* s) {
   if (!s) return fail(KV_EINVAL, "shape is NULL");
   if (s->format != KV_FMT_INT8 && s->format != KV_FMT_Q4_0 && s->format != KV_FMT_K8V4 &&
-      s->format != KV_FMT_FP4)
+      s->format != KV_FMT_FP4 && s->format != KV_FMT_FP8)
     return fail(KV_EINVAL, "unknown format %d", s->format);
   if (s->head_dim != kHeadDim) return fail(KV_EUNSUPPORTED, "head_dim must be 256 (got %d)", s->head_dim);
   if (s->page_tokens != kPageTokens)
@@ -573,6 +573,18 @@ int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint1
     }
     return ok();
   }
+  if (kind == kFp8) {
+    double a = 0.0;
+    for (int e = 0; e < kHeadDim; ++e) {
+      const double v = f16_to_f64(x[e]);
+      const double av = v < 0 ? -v : v;
+      if (av > a) a = av;
+    }
+    scales[0] = f64_to_f16_rne(a / 448.0);
+    const double d = f16_to_f64(scales[0]);
+    for (int e = 0; e < kHeadDim; ++e) codes[e] = (uint8_t)fp8_code(f16_to_f64(x[e]), d);
+    return ok();
+  }
   if (kind == kQ4 || kind == kFp4) {
     double y[kHeadDim];
     for (int e = 0; e < kHeadDim; ++e) y[e] = f16_to_f64(x[e]);
@@ -606,7 +618,7 @@ int kv_host_encode_vector(int32_t kind, const uint16_t* x, uint8_t* codes, uint1
     }
     return ok();
   }
-  return fail(KV_EINVAL, "kind must be 0 (int8), 1 (q4) or 2 (fp4)");
+  return fail(KV_EINVAL, "kind must be 0 (int8), 1 (q4), 2 (fp4) or 3 (fp8)");
 }
 
 }  // extern "C"

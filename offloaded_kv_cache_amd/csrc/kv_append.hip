@@ -70,9 +70,9 @@ __global__ __launch_bounds__(256) void append_kernel(
     } else {
       enc::encode<VK, false>(v + src, lane, code, scale);
       enc::write_v_scales<VK>(vplane, row, lane, scale);
-      if (VK == kInt8) {
+      if (!four_bit(VK)) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) vplane[(size_t)(lane + 64 * kk) * code_row_bytes(VK) + row] = (uint8_t)(int8_t)code[kk];
+        for (int kk = 0; kk < 4; ++kk) vplane[(size_t)(lane + 64 * kk) * code_row_bytes(VK) + row] = (uint8_t)code[kk];
       } else if (upper) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) vcode_hi[lane + 64 * kk] = (uint8_t)code[kk];
@@ -116,6 +116,11 @@ hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint1
       break;
     case KV_FMT_FP4:
       hipLaunchKernelGGL((append_kernel<kFp4, kFp4>), grid, block, 0, stream, k, v, n_tokens,
+                         start_pos, block_table, g0, pool, n_pool_pages, page_bytes, n_kv_heads,
+                         status);
+      break;
+    case KV_FMT_FP8:
+      hipLaunchKernelGGL((append_kernel<kFp8, kFp8>), grid, block, 0, stream, k, v, n_tokens,
                          start_pos, block_table, g0, pool, n_pool_pages, page_bytes, n_kv_heads,
                          status);
       break;

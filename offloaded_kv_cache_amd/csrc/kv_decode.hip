@@ -105,6 +105,9 @@ __device__ inline u4 ld16(Rsrc r, uint32_t off) {
 __device__ inline u2 ld8(Rsrc r, uint32_t off) {
   return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ inline uint32_t ld2(Rsrc r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
 
 // A value kept in a VGPR, opaque to constant folding, so that (x & m) | v
 // becomes one v_and_or_b32 inside the hot loops.
@@ -182,7 +185,8 @@ __device__ inline h8 k_codes_i8(uint32_t x0, uint32_t x1) {
 // One 16-token tile of a K plane, as loaded by one lane (token = its column).
 struct KTile {
   u4 c0, c1, c2, c3;  // code bytes of the lane's slice (q4: c0, c1; int8: all four)
-  u4 d;               // the token's scales (q4: 8 fp16; int8: 4 fp16 in d.xy, d.zw = 0)
+  u4 d;               // the token's scales (q4: 8 fp16; int8: 4 fp16 in d.xy, d.zw = 0;
+                      // fp8: fp16 0 of d.x = the K scale, fp16 1 = the same token's V scale)
 };
 
 // Byte offsets (from the head's K plane) of the lane's part of K tile t (loop
@@ -205,6 +209,11 @@ __device__ inline KTile load_ktile(Rsrc r, uint32_t coff, uint32_t soff) {
   if (four_bit(KK)) {
     t.c2 = t.c3 = (u4){0, 0, 0, 0};
     t.d = ld16(r, soff);
+  } else if (KK == kFp8) {
+    t.c2 = ld16(r, coff + 32);
+    t.c3 = ld16(r, coff + 48);
+    // the V plane's scale row sits plane_bytes(kFp8) after the K plane's scale rows
+    t.d = (u4){ld2(r, soff) | (ld2(r, soff + plane_bytes(kFp8)) << 16), 0u, 0u, 0u};
   } else {
     t.c2 = ld16(r, coff + 32);
     t.c3 = ld16(r, coff + 48);
@@ -229,6 +238,15 @@ __device__ inline h8 fp4_vals(uint32_t x, float scale) {
   const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, scale, 3);
   return (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
+// Eight E4M3 codes (x0 bytes 0..3, x1 bytes 4..7) as their fp16 values, in order (the
+// conversion at scale 1 is exact: every E4M3 value is an fp16 number).
+__device__ inline h8 fp8_vals(uint32_t x0, uint32_t x1) {
+  const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x0, 1.0f, false);
+  const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x0, 1.0f, true);
+  const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x1, 1.0f, false);
+  const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x1, 1.0f, true);
+  return (h8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 // Scores of one tile for the lane's two heads (rows 4grp..4grp+3 = head 2grp
 // hi, lo, head 2grp+1 hi, lo), in units of q.k (before the softmax scale).
@@ -244,6 +262,19 @@ __device__ inline void qk_tile(const KTile& t, const h8 (&qa)[8], h8 qc, float& 
     for (int j = 0; j < 8; ++j) acc = mfma(qa[j], fp4_vals(w[j], scale_at(t.d, j)), acc);
     s0 = acc[0] + acc[1];
     s1 = acc[2] + acc[3];
+    return;
+  }
+  if constexpr (KK == kFp8) {
+    // the codes' exact fp16 values in one MFMA chain over the 256 elements (int8's slot
+    // order), then the token's one scale
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t w[16] = {t.c0[0], t.c0[1], t.c0[2], t.c0[3], t.c1[0], t.c1[1], t.c1[2], t.c1[3],
+                            t.c2[0], t.c2[1], t.c2[2], t.c2[3], t.c3[0], t.c3[1], t.c3[2], t.c3[3]};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = mfma(qa[j], fp8_vals(w[2 * j], w[2 * j + 1]), acc);
+    const float d = scale_at(t.d, 0);
+    s0 = d * (acc[0] + acc[1]);
+    s1 = d * (acc[2] + acc[3]);
     return;
   }
   float a0 = 0.f, b0 = 0.f, a1 = 0.f, b1 = 0.f;  // hi and lo rows, units of 2^-24
@@ -333,7 +364,10 @@ __device__ inline uint32_t vscale_off(int epw, int wave, int lane) {
 }
 template <int VK>
 __device__ inline void load_vscales(VShare<VK>& v, Rsrc r, uint32_t off) {
-  if (four_bit(VK)) {
+  if (VK == kFp8) {
+    // (fp8: the token's V scale comes with its K tile and is applied on the P side)
+    v.s0 = v.s1 = (u2){0u, 0u};
+  } else if (four_bit(VK)) {
     v.s0 = ld8(r, off);
     v.s1 = ld8(r, off + 32);
   } else {
@@ -376,6 +410,7 @@ struct SplitLds {
   float lsum[NW][kMaxGroup];
   float qs[kMaxGroup][kQsStride];
   float bsum[kMaxGroup][8];
+  float wdmax[NW];  // fp8: each wave's largest V scale of the page
 };
 
 __device__ inline int32_t bt_row_entry(const int32_t* __restrict__ block_tables, int b, int max_pages, int pg) {
@@ -580,9 +615,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
   }
   __syncthreads();
-  if (KK != kFp4) {
+  if (KK == kInt8 || KK == kQ4) {
     // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8),
-    // for the code offsets (fp4 codes carry no offset)
+    // for the code offsets (fp4 and fp8 codes carry no offset)
     constexpr int nb = KK == kQ4 ? 8 : 4, bl = kHeadDim / nb;
     if (tid < kMaxGroup * nb) {
       const int hh = tid / nb, j = tid % nb;
@@ -646,7 +681,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   h8 qc;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    const float f = (KK != kFp4 && s < (KK == kQ4 ? 8 : 4)) ? lds.bsum[a_head][s] : 0.f;
+    const float f = ((KK == kInt8 || KK == kQ4) && s < (KK == kQ4 ? 8 : 4)) ? lds.bsum[a_head][s] : 0.f;
     const _Float16 hi = (_Float16)f;
     const _Float16 lo = (_Float16)(f - (float)hi);
     qc[s] = (a_live && grp == 0) ? (a_part ? lo : hi) : (_Float16)0;
@@ -657,6 +692,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
   // per-lane running state for the two heads of its row group (rows 4grp..4grp+3)
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  // fp8: the accumulators hold the output in units of dunit (a power of two, the
+  // previous page's largest V scale rounded down), so that p * d / dunit stays in fp16 range
+  float dunit = 1.f;
   f4 oacc[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -679,6 +717,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 
     // ---------------- Q.K of the wave's TPW tokens, wave maximum per head
     float xs[KT][2];
+    float vd[KT];  // fp8: V scale of the lane's token of tile t (0 past the context)
     float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
@@ -686,6 +725,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       float s0, s1;
       qk_tile<KK>(kt[t], qa, qc, s0, s1);
       const bool ok = row < valid;
+      vd[t] = (VK == kFp8 && ok) ? scale_at(kt[t].d, 1) : 0.f;
       xs[t][0] = ok ? s0 * scale_log2 : -INFINITY;
       xs[t][1] = ok ? s1 * scale_log2 : -INFINITY;
       mx0 = fmaxf(mx0, xs[t][0]);
@@ -699,12 +739,21 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       lds.wmax[wave][h0] = mx0;
       lds.wmax[wave][h1] = mx1;
     }
+    if constexpr (VK == kFp8) {
+      float dmx = vd[0];
+#pragma unroll
+      for (int t = 1; t < KT; ++t) dmx = fmaxf(dmx, vd[t]);
+      dmx = half_max(dmx, lane);
+      if (lane == 0) lds.wdmax[wave] = dmx;
+    }
 
     // ---------------- B parts of the wave's V scales (0 past the context)
     bool fast;
     {
       h8* dp = lds.dpart[wave];
-      if constexpr (VK == kFp4) {
+      if constexpr (VK == kFp8) {
+        fast = true;  // no B parts: the V scale goes with the probability
+      } else if constexpr (VK == kFp4) {
         // the scales of the lane's entry (block bb of the wave, MFMA i, lane group gq) in
         // B slot order [t, t+16, t+1, t+17, t+2, t+18, t+3, t+19] (0 past the context);
         // the products code * 2^e are exact, so every page takes the one path
@@ -787,6 +836,19 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
       pm1 = fmaxf(pm1, lds.wmax[w][h1]);
     }
     const float mn0 = fmaxf(m_run[0], pm0), mn1 = fmaxf(m_run[1], pm1);
+    // fp8: the page's unit (largest V scale of the page rounded down to a power of two;
+    // 1 without tokens in context), its inverse, and the change of unit of the accumulators
+    float vinv = 1.f, vratio = 1.f;
+    if constexpr (VK == kFp8) {
+      float dm = lds.wdmax[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) dm = fmaxf(dm, lds.wdmax[w]);
+      const uint32_t eb = dm > 0.f ? (__builtin_bit_cast(uint32_t, dm) >> 23) : 127u;  // fp16 scales: normal fp32
+      const float unit = __builtin_bit_cast(float, eb << 23);
+      vinv = __builtin_bit_cast(float, (254u - eb) << 23);
+      vratio = dunit * vinv;
+      dunit = unit;
+    }
     // reference point of the exponentials: the new maximum, or 0 while no token of
     // the split is in context (then every score and the old maximum are -inf, and
     // 2^(-inf) = 0 leaves the zero state unchanged)
@@ -819,7 +881,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
         slot = o & 7;
       }
       const int base_idx = (i * 64 + 16 * kg) * 8 + slot;
-      const float ps0 = p0 * kPScale, ps1 = p1 * kPScale;
+      // (fp8: times the token's V scale in the page's unit, in [0, 2): exact)
+      const float pk = VK == kFp8 ? kPScale * (vd[t] * vinv) : kPScale;
+      const float ps0 = p0 * pk, ps1 = p1 * pk;
       const _Float16 hi0 = (_Float16)ps0, hi1 = (_Float16)ps1;
       const _Float16 lo0 = (_Float16)(ps0 - (float)hi0), lo1 = (_Float16)(ps1 - (float)hi1);
       // rows of heads >= G (zero query) are written too: they only feed output rows
@@ -831,21 +895,45 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
     }
     l_run[0] = l_run[0] * al0 + sum0;
     l_run[1] = l_run[1] * al1 + sum1;
+    const float ao0 = al0 * vratio, ao1 = al1 * vratio;
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      oacc[t][0] *= al0;
-      oacc[t][1] *= al0;
-      oacc[t][2] *= al1;
-      oacc[t][3] *= al1;
+      oacc[t][0] *= ao0;
+      oacc[t][1] *= ao0;
+      oacc[t][2] *= ao1;
+      oacc[t][3] *= ao1;
     }
     __syncthreads();  // (B) probabilities of all 256 tokens visible
 
     // ---------------- P.V for the wave's EPW head elements, in halves of two column tiles
     // (one q4 block each); after a half, its code registers take the next page's codes.
     const h8* dp = lds.dpart[wave];
+    if (VK == kFp8 && valid < kPageTokens) {
+      // E4M3 has NaN codes and 0 * NaN is NaN: bytes of rows past the context (stale or
+      // never written) are cleared. Byte b of word w of slice u: token 64grp + 16u + 4w + b.
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int n = valid - (64 * grp + 16 * u + 4 * w);
+            vsh.c[nt][u][w] &= n >= 4 ? ~0u : (n <= 0 ? 0u : (1u << (8 * n)) - 1u);
+          }
+    }
 #pragma unroll
     for (int hf = 0; hf < HFN; ++hf) {
-      if constexpr (VK == kFp4) {
+      if constexpr (VK == kFp8) {
+        // B = the codes' exact fp16 values; the V scales are in the probabilities
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const h8 pa = lds.afrag[i][lane];
+          const u4 w0 = vsh.c[2 * hf][i >> 1], w1 = vsh.c[2 * hf + 1][i >> 1];
+          oacc[2 * hf] = mfma(pa, fp8_vals(w0[2 * (i & 1)], w0[2 * (i & 1) + 1]), oacc[2 * hf]);
+          oacc[2 * hf + 1] = mfma(pa, fp8_vals(w1[2 * (i & 1)], w1[2 * (i & 1) + 1]), oacc[2 * hf + 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else if constexpr (VK == kFp4) {
         // B = code value (conversion at scale 1) times the token's 2^e: exact fp16
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -942,7 +1030,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) po[r][t] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * kPScaleInv;
+    for (int t = 0; t < NTW; ++t) po[r][t] = (oacc[t][2 * r] + oacc[t][2 * r + 1]) * (kPScaleInv * dunit);
   if (four_bit(VK)) {
     // V is stored rotated: the partial is rotated back here (H is linear, so the merge of
     // rotated partials is the rotated merge). Element bits 0-3 (col) between lanes,
@@ -1151,6 +1239,7 @@ hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hip
       case KV_FMT_INT8: e = launch_split<kInt8, kInt8>(a, stream, start, stop); break;
       case KV_FMT_Q4_0: e = launch_split<kQ4, kQ4>(a, stream, start, stop); break;
       case KV_FMT_FP4: e = launch_split<kFp4, kFp4>(a, stream, start, stop); break;
+      case KV_FMT_FP8: e = launch_split<kFp8, kFp8>(a, stream, start, stop); break;
       default: e = launch_split<kInt8, kQ4>(a, stream, start, stop); break;
     }
     if (e != hipSuccess) return e;

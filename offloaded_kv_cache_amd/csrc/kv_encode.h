@@ -116,6 +116,7 @@ __device__ inline int q4_code_fast(double y, double d) {
 
 // The record of one vector: codes of the lane's elements and the scales.
 // int8: scale[k] is group k (elements 64k..64k+63 are exactly register k).
+// fp8: every scale[k] is the vector's one scale.
 // q4, fp4: scale of block (lane >> 5) + 2k lives in register k of every lane of
 // that half-wave.
 template <int KIND, bool DPP = true>
@@ -134,6 +135,20 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
       scale[k] = DPP ? f64_to_f16_fast(a[k] / 127.0) : f64_to_f16_rne(a[k] / 127.0);
       const double d = f16_to_f64(scale[k]);
       code[k] = DPP ? int8_code_fast(x[k], d) : int8_code(x[k], d);
+    }
+  } else if (KIND == kFp8) {
+    // one scale for the vector: the largest |x| over the wave's four registers
+    double a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
+    wave_max4<DPP>(a, lane);
+    const double amax = fmax(fmax(a[0], a[1]), fmax(a[2], a[3]));
+    const uint16_t s = DPP ? f64_to_f16_fast(amax / 448.0) : f64_to_f16_rne(amax / 448.0);
+    const double d = f16_to_f64(s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      scale[k] = s;
+      code[k] = fp8_code(x[k], d);
     }
   } else if (KIND == kFp4) {
     wht256<DPP>(x, lane);
@@ -210,14 +225,16 @@ __device__ inline void write_k_row(uint8_t* __restrict__ plane, int row, int lan
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
     const int j = e >> 5, r = e & 31;
-    if (KIND == kInt8) {
-      codes[64 * (r >> 3) + 8 * j + (r & 7)] = (uint8_t)(int8_t)code[k];
+    if (!four_bit(KIND)) {
+      codes[64 * (r >> 3) + 8 * j + (r & 7)] = (uint8_t)code[k];
     } else {
       const int partner = (int)xchg32<16>((uint32_t)code[k], lane);  // element e ^ 16, same block
       if (r < 16) codes[32 * (r >> 2) + 4 * j + (r & 3)] = (uint8_t)(code[k] | (partner << 4));
     }
   }
-  if (KIND == kInt8) {
+  if (KIND == kFp8) {
+    if (lane == 0) scales[0] = scale[0];
+  } else if (KIND == kInt8) {
     if (lane < 4) {
       uint16_t s = scale[0];
       if (lane == 1) s = scale[1];
@@ -235,7 +252,9 @@ template <int KIND>
 __device__ inline void write_v_scales(uint8_t* __restrict__ plane, int row, int lane,
                                       const uint16_t (&scale)[4]) {
   uint16_t* sc = reinterpret_cast<uint16_t*>(plane + kHeadDim * code_row_bytes(KIND));
-  if (KIND == kInt8) {
+  if (KIND == kFp8) {
+    if (lane == 0) sc[row] = scale[0];
+  } else if (KIND == kInt8) {
     if (lane == 0) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) sc[k * kPageTokens + row] = scale[k];
@@ -246,7 +265,7 @@ __device__ inline void write_v_scales(uint8_t* __restrict__ plane, int row, int 
   }
 }
 
-// V codes of one token, written alone. int8: one byte per element. 4-bit: each
+// V codes of one token, written alone. int8, fp8: one byte per element. 4-bit: each
 // byte of the element-major V plane pairs tokens 32G+i (low nibble) and 32G+16+i
 // (high nibble); the token's nibble is replaced by an atomic AND then OR on the
 // containing dword, so the partner's nibble is kept without a read round trip
@@ -257,8 +276,8 @@ __device__ inline void write_v_codes_one(uint8_t* __restrict__ plane, int row, i
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
-    if (KIND == kInt8) {
-      plane[(size_t)e * code_row_bytes(KIND) + row] = (uint8_t)(int8_t)code[k];
+    if (!four_bit(KIND)) {
+      plane[(size_t)e * code_row_bytes(KIND) + row] = (uint8_t)code[k];
     } else {
       const size_t off = (size_t)e * code_row_bytes(KIND) + 16 * (row >> 5) + (row & 15);
       uint32_t* w = reinterpret_cast<uint32_t*>(plane + (off & ~(size_t)3));

@@ -17,20 +17,21 @@ constexpr int kPageTokens = 256;
 constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
 constexpr int kMaxGroup = 8;  // query heads per KV head handled by one MFMA row tile
 
-enum RecordKind : int { kInt8 = 0, kQ4 = 1, kFp4 = 2 };
-// q4_0 and fp4 records: rotated by H, 4-bit codes in the same byte layout, 8 fp16 scales
-__host__ __device__ constexpr bool four_bit(int kind) { return kind != kInt8; }
+enum RecordKind : int { kInt8 = 0, kQ4 = 1, kFp4 = 2, kFp8 = 3 };
+// q4_0 and fp4 records: rotated by H, 4-bit codes in the same byte layout, 8 fp16 scales;
+// int8 and fp8 records: one byte per code in the same byte layout, not rotated
+__host__ __device__ constexpr bool four_bit(int kind) { return kind == kQ4 || kind == kFp4; }
 
-__host__ __device__ constexpr int code_row_bytes(int kind) { return kind == kInt8 ? 256 : 128; }
-__host__ __device__ constexpr int n_scales(int kind) { return kind == kInt8 ? 4 : 8; }
+__host__ __device__ constexpr int code_row_bytes(int kind) { return four_bit(kind) ? 128 : 256; }
+__host__ __device__ constexpr int n_scales(int kind) { return kind == kInt8 ? 4 : (kind == kFp8 ? 1 : 8); }
 __host__ __device__ constexpr int plane_bytes(int kind) {
   return kPageTokens * code_row_bytes(kind) + kPageTokens * n_scales(kind) * 2;
 }
 __host__ __device__ constexpr int k_kind(int fmt) {
-  return fmt == KV_FMT_Q4_0 ? kQ4 : (fmt == KV_FMT_FP4 ? kFp4 : kInt8);
+  return fmt == KV_FMT_Q4_0 ? kQ4 : (fmt == KV_FMT_FP4 ? kFp4 : (fmt == KV_FMT_FP8 ? kFp8 : kInt8));
 }
 __host__ __device__ constexpr int v_kind(int fmt) {
-  return fmt == KV_FMT_INT8 ? kInt8 : (fmt == KV_FMT_FP4 ? kFp4 : kQ4);
+  return fmt == KV_FMT_INT8 ? kInt8 : (fmt == KV_FMT_FP4 ? kFp4 : (fmt == KV_FMT_FP8 ? kFp8 : kQ4));
 }
 // Waves per workgroup of the split-K decode kernel: 4 (two workgroups per CU) for
 // 4-bit K; 8 (one workgroup per CU, half the registers per wave) for int8 K, whose
@@ -125,6 +126,28 @@ __host__ __device__ inline int fp4_code(double y, int e) {
   const double v = (y < 0 ? -y : y) * f64_pow2(-e);  // exact
   const int idx = (v > 0.25) + (v >= 0.75) + (v > 1.25) + (v >= 1.75) + (v > 2.5) + (v >= 3.5) + (v > 5.0);
   return idx + ((y < 0 && idx > 0) ? 8 : 0);
+}
+
+// fp8 record helpers (rules in include/kvcache.h). Code of x for the stored scale d > 0:
+// |x| / d (an exact decision in fp64) to the nearest E4M3 magnitude, ties to the even
+// mantissa, beyond 448 to 448; sign bit 0x80 for x < 0 unless the magnitude is 0.
+// E4M3: magnitudes below 2^-6 are multiples of 2^-9 (exponent field 0); from 2^E
+// (E >= -6) on, multiples of 2^(E-3) with exponent field E + 7.
+__host__ __device__ inline int fp8_code(double x, double d) {
+  if (d == 0.0) return 0;
+  const double v = (x < 0 ? -x : x) / d;
+  if (v >= 464.0) return x < 0 ? 0xFE : 0x7E;                // at and past the last midpoint
+  const int ex = (int)((__builtin_bit_cast(uint64_t, v) >> 52) & 0x7FF) - 1023;  // floor(log2 v)
+  const bool sub = v < 0x1p-6;
+  const int ue = sub ? -9 : ex - 3;                           // unit 2^ue
+  const double n = v * __builtin_bit_cast(double, (uint64_t)(1023 - ue) << 52);  // v / 2^ue, exact
+  double r = __builtin_floor(n);
+  const double f = n - r;
+  if (f > 0.5 || (f == 0.5 && __builtin_fmod(r, 2.0) == 1.0)) r += 1.0;
+  // subnormal: r in [0, 8] (8 = the least normal, field 1); normal: r in [8, 16]
+  int c = sub ? (int)r : ((ex + 7) << 3) + (int)r - 8;
+  if (c > 0x7E) c = 0x7E;
+  return (x < 0 && c > 0) ? (c | 0x80) : c;
 }
 
 struct DecodeArgs {

@@ -19,7 +19,7 @@ from gpu_helpers import Sequence, assert_close, oracle_out
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["int8", "q4_0", "k8v4", "fp4"]
+FMTS = ["int8", "q4_0", "k8v4", "fp4", "fp8"]
 
 
 def to_dev(a, dev):

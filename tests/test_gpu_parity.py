@@ -18,7 +18,7 @@ from gpu_helpers import Sequence, assert_close, fmt_id, oracle_out, oracle_recor
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["int8", "q4_0", "k8v4", "fp4"]
+FMTS = ["int8", "q4_0", "k8v4", "fp4", "fp8"]
 
 
 def to_dev(a, dev, dtype=None):
@@ -124,11 +124,38 @@ def fp4_edge_vectors(n_kv_heads=4):
     return np.stack(vs)
 
 
+def fp8_edge_vectors(n_kv_heads=4):
+    """E4M3 edge cases. With the largest element 448 (d = 1) or 896 (d = 2), the other
+    elements sit on every midpoint between neighbouring E4M3 magnitudes (ties to the
+    even code), with both signs; a vector of 627 * 2^-24 has the subnormal scale 2^-24
+    and saturates; one just below fp16's largest value has d = 146.25."""
+    e = np.arange(127)
+    ex, m = e >> 3, e & 7
+    mag = np.where(ex == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(ex - 7.0))
+    mids = (mag[1:] + mag[:-1]) / 2                                   # 126 ties
+    vs = []
+    for top in (448.0, 896.0):
+        x = np.zeros((n_kv_heads, 256))
+        x[:, 0] = top
+        x[:, 1:127] = mids * (top / 448.0)
+        x[:, 127:253] = -mids * (top / 448.0)
+        x[:, 253] = -top
+        vs.append(x.astype(np.float16))
+    x = np.zeros((n_kv_heads, 256))
+    x[:, 0], x[:, 1], x[:, 2] = 627 * 2.0 ** -24, -300 * 2.0 ** -24, 2.0 ** -24
+    vs.append(x.astype(np.float16))
+    x = np.zeros((n_kv_heads, 256))
+    x[:, 0], x[:, 1], x[:, 2] = 65504.0, -65504.0, 146.0
+    vs.append(x.astype(np.float16))
+    return np.stack(vs)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_append_rounding_edges_bitexact(gpu, fmt):
     """Scale and code rounding edge cases appended one token at a time and as a chunk,
     bit for bit against the oracle's records."""
-    sp = np.concatenate([rounding_edge_vectors(), special_vectors(), fp4_edge_vectors()])
+    sp = np.concatenate([rounding_edge_vectors(), special_vectors(), fp4_edge_vectors(),
+                         fp8_edge_vectors()])
     T = len(sp)
     s = K.shape(fmt)
     pb = K.page_bytes(s)
@@ -331,6 +358,36 @@ def test_decode_extreme_scales(gpu, fmt):
         got, status = run_decode(gpu, fmt, seqs, q, pps, seed=5 + pps)
         assert status == 0
         assert_close(got, oracle_out(q, seqs, fmt), what=f"{fmt} pps {pps}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_ignores_stale_rows(gpu, fmt):
+    """Rows past the context on a sequence's last page may hold anything (records of an
+    earlier sequence, NaN scales, the E4M3 NaN code 0x7F): the output depends only on the
+    tokens in context."""
+    T = 300
+    seq = Sequence(29, 0, 0, T, fmt)
+    kk, vk = records.kinds(fmt_id(fmt))
+    pad = 512 - T
+
+    def junk(a, kind, is_code):
+        if is_code:
+            val = {records.KIND_INT8: 127, records.KIND_FP8: 0x7F}.get(kind, 15)
+        else:
+            val = np.nan
+        return np.concatenate([a, np.full((pad,) + a.shape[1:], val, a.dtype)])
+
+    kc, ks, vc, vs = seq.rec
+    seq.pages = layout.pack_pages(junk(kc, kk, True), junk(ks, kk, False), junk(vc, vk, True),
+                                  junk(vs, vk, False), fmt_id(fmt))
+    assert seq.pages.shape[0] == seq.n_pages == 2
+    q = kvsynth.q_np(29, 0, 1)
+    want = oracle_out(q, [seq], fmt)
+    for pps in (0, 1):
+        got, status = run_decode(gpu, fmt, [seq], q, pps, seed=11 + pps)
+        assert status == 0
+        assert np.isfinite(got).all()
+        assert_close(got, want, what=f"{fmt} pps {pps}")
 
 
 MERGE_CASES = [

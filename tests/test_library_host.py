@@ -69,7 +69,7 @@ def test_f64_to_f16_matches_single_rounding():
     assert N.host_f64_to_f16(np.nan) & 0x7C00 == 0x7C00
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2])
+@pytest.mark.parametrize("kind", [0, 1, 2, 3])
 def test_host_records_match_oracle(kind):
     rng = np.random.default_rng(10 + kind)
     xs = [(rng.standard_normal(256) * np.where(rng.random(256) < 0.03, 20, 1)).astype(np.float16)
@@ -89,8 +89,12 @@ def test_host_records_match_oracle(kind):
         elif kind == 1:
             c, d = records.quantize_q4(x.astype(np.float64))
             assert np.array_equal(codes, c)
-        else:
+        elif kind == 2:
             c, d = records.quantize_fp4(x.astype(np.float64))
+            assert np.array_equal(codes, c)
+        else:
+            c, d = records.quantize_fp8(x.astype(np.float64))
+            d = d.reshape(-1)
             assert np.array_equal(codes, c)
         assert np.array_equal(scales.view(np.uint16), d.view(np.uint16))
 
@@ -191,3 +195,30 @@ def test_binding_shares_torchs_hip_runtime():
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_host_fp8_codes_at_every_tie():
+    """The library's E4M3 rounding (shared by its kernels) at every midpoint between
+    neighbouring magnitudes, just beside each, with both signs, and with a subnormal
+    scale that saturates, against the oracle."""
+    mids = (records.E4M3[1:] + records.E4M3[:-1]) / 2
+    for top in (448.0, 896.0):
+        for nudge in (0.0, -1.0, 1.0):
+            x = np.zeros(256)
+            x[0] = top
+            v = mids * (top / 448.0)
+            if nudge:
+                v = np.nextafter(v.astype(np.float16), np.float16(nudge * np.inf)).astype(np.float64)
+            x[1:127] = v
+            x[127:253] = -v
+            x16 = x.astype(np.float16)
+            codes, scales = N.host_encode_vector(3, x16)
+            c, d = records.quantize_fp8(x16.astype(np.float64))
+            assert np.array_equal(codes, c), (top, nudge)
+            assert scales.view(np.uint16)[0] == d.view(np.uint16)[0]
+    x = np.zeros(256, np.float16)
+    x[0], x[1] = np.float16(627 * 2.0 ** -24), np.float16(-300 * 2.0 ** -24)
+    codes, scales = N.host_encode_vector(3, x)
+    assert float(scales[0]) == 2.0 ** -24 and codes[0] == 0x7E      # 627 saturates
+    assert codes[1] == 0x80 | 0x79                                    # 300 -> 288 = 1.125 * 2^8
+    assert np.array_equal(codes, records.quantize_fp8(x.astype(np.float64))[0])
