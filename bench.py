@@ -24,7 +24,8 @@ Other workloads (parity-test shapes, not the metric line): --workload c1
 4 sequences of 262,144 / 198,000 / 65,536 / 8,192 tokens, k8v4), c5
 (16 layers, 1,048,576-token int8 host pool, 128 resident slots per layer,
 2,048-token selection per step with ~30% misses, gathered zero-copy), c3fp4
-(the default shape with fp4 records: e2m1 codes, power-of-two block scales).
+(the default shape with fp4 records: e2m1 codes, power-of-two block scales), c3fp8
+(the default shape with fp8 records: E4M3 codes, one scale per vector).
 """
 
 from __future__ import annotations
@@ -49,6 +50,7 @@ WORKLOADS = {
     "c3": dict(fmt="q4_0", layers=16, lens=[131072], cfg=3),
     "c4": dict(fmt="k8v4", layers=16, lens=[262144, 198000, 65536, 8192], cfg=4),
     "c3fp4": dict(fmt="fp4", layers=16, lens=[131072], cfg=3),
+    "c3fp8": dict(fmt="fp8", layers=16, lens=[131072], cfg=3),
 }
 
 
@@ -57,7 +59,7 @@ def log(*a):
 
 
 def kv_bytes_per_token(fmt: str, n_kv_heads: int = 4) -> int:
-    rec = {"int8": (264, 264), "q4_0": (144, 144), "k8v4": (264, 144), "fp4": (144, 144)}[fmt]
+    rec = {"int8": (264, 264), "q4_0": (144, 144), "k8v4": (264, 144), "fp4": (144, 144), "fp8": (258, 258)}[fmt]
     return n_kv_heads * sum(rec)
 
 
@@ -518,7 +520,8 @@ def counter_traffic(workload: str):
 
     The summary records the code hash (kernel_code_hash) of the kernel its counters
     were taken with; a kernel changed since then gives None."""
-    name = {"c3": "decode_q4_0_128k_hbm_bytes.txt", "c3fp4": "decode_fp4_128k_hbm_bytes.txt"}.get(workload)
+    name = {"c3": "decode_q4_0_128k_hbm_bytes.txt", "c3fp4": "decode_fp4_128k_hbm_bytes.txt",
+            "c3fp8": "decode_fp8_128k_hbm_bytes.txt"}.get(workload)
     path = os.path.join(ROOT, "profiles", name) if name else None
     if path is None or not os.path.exists(path):
         return None
@@ -652,13 +655,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"q4_0": "q4_0 KV, fp32 accumulate", "int8": "int8 KV, fp32 accumulate",
-                  "k8v4": "int8 K / q4_0 V, fp32 accumulate", "fp4": "fp4 (e2m1) KV, fp32 accumulate"}[fmt],
+                  "k8v4": "int8 K / q4_0 V, fp32 accumulate", "fp4": "fp4 (e2m1) KV, fp32 accumulate",
+                  "fp8": "fp8 (e4m3) KV, fp32 accumulate"}[fmt],
         "data": "synthetic",
         "config": {"workload": {"c1": "1 layer, 4,096-token q4_0 context",
                                 "c2": "16 layers, 32,768-token int8 context",
                                 "c3": "16 layers, 131,072-token q4_0 context (append 1 token + decode per layer)",
                                 "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4",
-                                "c3fp4": "16 layers, 131,072-token fp4 context (append 1 token + decode per layer)"}[args.workload],
+                                "c3fp4": "16 layers, 131,072-token fp4 context (append 1 token + decode per layer)",
+                                "c3fp8": "16 layers, 131,072-token fp8 context (append 1 token + decode per layer)"}[args.workload],
                    "layers": wl["layers"], "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256,
                    "page_tokens": 256, "batch": len(wl["lens"]), "context": wl["lens"],
                    "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto",
