@@ -1,6 +1,7 @@
 """Parity at full benchmark sizes, in the launch configuration the benchmark uses.
 
-* 131,072-token q4_0 layer (24 query / 4 KV heads): the cache is written by the
+* One layer of 131,072 tokens in q4_0 (24 query / 4 KV heads), and the same in
+  fp4 and fp8, and one layer of 32,768 int8 tokens: the cache is written by the
   append kernel in 2,048-token chunks through a shuffled block table, decoded
   with the automatic split count; one KV head's six query heads are checked
   against the fp64 oracle, and sampled pages of that head are checked byte for
@@ -84,19 +85,23 @@ def head_oracle(q_heads, rec, fmt):
     return attention.decode_attention(q_heads, kh, vh, fmt_id(fmt))
 
 
-def test_q4_0_131072_layer_sampled(gpu):
-    fmt, T, cfg, g = "q4_0", 131072, 3, 1
+LAYERS = [("q4_0", 131072, 3), ("fp4", 131072, 3), ("fp8", 131072, 3), ("int8", 32768, 2)]
+
+
+@pytest.mark.parametrize("fmt, T, cfg", LAYERS, ids=[f"{f}_{t}" for f, t, _ in LAYERS])
+def test_one_layer_sampled(gpu, fmt, T, cfg):
+    g = 1
     q = kvsynth.q_np(cfg, 0, 1)
     s, pool, bt, heads = build_pool(gpu, fmt, cfg, [T], seed=31, g=g)
     got = decode(gpu, s, pool, bt, q, [T])
     rec = head_records(*heads[0], fmt)
     want = head_oracle(q[0, 6 * g:6 * g + 6], rec, fmt)
-    assert_close(got[0, 6 * g:6 * g + 6], want, what="q4_0 131072, KV head 1")
+    assert_close(got[0, 6 * g:6 * g + 6], want, what=f"{fmt} {T}, KV head 1")
     # sampled pages of the checked head, byte for byte
     one_head = layout.pack_pages(*rec, fmt_id(fmt))      # pages of a 1-KV-head layout
     hs = one_head.shape[1]                                # bytes of one head's K + V planes
     pb = K.page_bytes(s)
-    for p in (0, 1, 255, 511):
+    for p in (0, 1, T // 512, T // 256 - 1):
         phys = int(bt[0, p])
         dev = pool.data[phys * pb + g * hs: phys * pb + (g + 1) * hs].cpu().numpy()
         assert np.array_equal(dev, one_head[p]), f"page {p}"
