@@ -73,6 +73,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
@@ -1137,9 +1138,10 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
   const int e = kCombineElems * blockIdx.z + el;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t base = ((size_t)b * n_q_heads + h) * (size_t)n_splits;
-  // issued before the context length is known: split tid's maximum and the first
-  // pass of partials (indices clamped to the grid's splits)
-  const float m_first = part_ml[2 * (base + min(tid, n_splits - 1))];
+  // issued before the context length is known: split tid's maximum and weight sum, and
+  // the first pass of partials (indices clamped to the grid's splits)
+  const f2 ml_first = *reinterpret_cast<const f2*>(part_ml + 2 * (base + min(tid, n_splits - 1)));
+  const float m_first = ml_first[0], l_first = ml_first[1];
   float v[kCombineRun];
 #pragma unroll
   for (int u = 0; u < kCombineRun; ++u)
@@ -1165,10 +1167,12 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine(
       const int cnt = min(kCombineChunk, ns - s0);
       __syncthreads();
       for (int s = tid; s < cnt; s += kCombineThreads) {
-        const float ms = (s0 == 0 && s == tid) ? m_first : part_ml[2 * (base + s0 + s)];
+        const bool first = s0 == 0 && s == tid;  // (loaded at the start)
+        const float ms = first ? m_first : part_ml[2 * (base + s0 + s)];
+        const float ls = first ? l_first : part_ml[2 * (base + s0 + s) + 1];
         const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
         wts[s] = w;
-        L += w * part_ml[2 * (base + s0 + s) + 1];
+        L += w * ls;
       }
       __syncthreads();
       for (int p0 = 0; p0 < cnt; p0 += kCombinePass) {
