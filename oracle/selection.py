@@ -3,7 +3,7 @@
 KV-offload news page (rebasdaily.com topic page on Qwen3.8-Flash-Next KV
 offload), section "新招不是全搬，而是分层放": with most of the KV cache in system
 memory, attention runs over a fixed budget of 2,048 selected tokens (QSA), and
-the page's account of the rule breaks off. This build declares a plain rule,
+the page's account of the rule breaks off. A plain rule is declared here instead,
 written here step by step:
 
 1. Key sums. For page p (tokens 256p .. 256p+255 of the sequence), KV head g and
