@@ -3,8 +3,8 @@
 KV-offload news page (rebasdaily.com topic page on Qwen3.8-Flash-Next KV
 offload), section "新招不是全搬，而是分层放": with most of the KV cache in system
 memory, attention runs over a fixed budget of 2,048 selected tokens (QSA), and
-the page's account of the rule breaks off. A plain rule is declared here instead,
-written here step by step:
+the page's account of the rule breaks off. A plain rule is declared instead,
+written out step by step:
 
 1. Key sums. For page p (tokens 256p .. 256p+255 of the sequence), KV head g and
    element e: S[p][g][e] = sum over the page's tokens of k[t][g][e] * 2^24. fp16
