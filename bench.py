@@ -305,7 +305,7 @@ def cpu_baseline(args, wl, dev, state):
         attention.decode_attention_chunked(q, get_kv, T, 4, fmt_id)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= args.cpu_seconds or reps >= 8:
+        if el >= args.cpu_seconds or reps >= 64:
             break
     gbs = T * kv_bytes_per_token(fmt) * reps / el / 1e9
     return dict(value=gbs, unit="GB/s", cores=threads or os.cpu_count(), kind="oracle",
