@@ -119,14 +119,16 @@ const char* kv_last_error(void);
 /* Library version as "major.minor.patch". */
 const char* kv_version(void);
 
-/* Bytes of one page for `shape` (540672 / 294912 / 417792 for 4 KV heads),
- * or a negative status if the shape is invalid or unsupported. */
+/* Bytes of one page for `shape` (int8 540672, q4_0 and fp4 294912, k8v4 417792,
+ * fp8 528384 for 4 KV heads), or a negative status if the shape is invalid or
+ * unsupported. */
 int64_t kv_page_bytes(const kv_shape* shape);
 
 /*
  * kv_append_quantize - quantize-on-append (Strata page, section "4-bit KV
  * 缓存：先旋转，再压到 4-bit": K and V are rotated and stored as q4_0 blocks as
- * they are written; section "三种 KV 格式横向对比" for int8 and k8v4).
+ * they are written; section "三种 KV 格式横向对比" for int8 and k8v4; the fp4 and
+ * fp8 records follow the rules above).
  *
  * Writes the records of tokens [start_pos, start_pos + n_tokens) of one
  * sequence into its pages: token p goes to page block_table[p / 256], row
