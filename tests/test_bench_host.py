@@ -1,0 +1,43 @@
+"""Host-side checks of bench.py (no GPU): the one-GPU refusal and the kernel code hash
+that ties a counter summary under profiles/ to the kernel it measured."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = run_bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
+
+
+def test_kernel_hash_ignores_comments(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) {\n  return x + 1;  // one\n}\n/* block */\n")
+    h1 = bench.kernel_code_hash([str(src)])
+    src.write_text("int f(int x) {   return x + 1;  // two, longer\n}\n")
+    assert bench.kernel_code_hash([str(src)]) == h1
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_code_hash([str(src)]) != h1
+
+
+def test_counter_summaries_name_their_kernel_hash():
+    """Every committed HBM-byte summary records the code hash it was taken with, and the
+    bytes per launch that bench.py reports as `traffic`."""
+    prof = os.path.join(ROOT, "profiles")
+    names = [n for n in os.listdir(prof) if n.endswith("_hbm_bytes.txt")]
+    assert names
+    for n in names:
+        text = open(os.path.join(prof, n)).read()
+        assert "kernel code sha256" in text and "traffic bytes per launch:" in text, n
+        assert "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text, n
