@@ -427,7 +427,12 @@ __device__ inline int32_t bt_row_entry(const int32_t* __restrict__ block_tables,
 // j = b % n_q of sequence b / n_q, whose context length T gives it the first
 // T - n_q + j + 1 tokens (causal attention of the sequence's n_q newest tokens).
 template <int KK, int VK, int NW, bool DYN, bool APPEND>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void decode_split(
+// (The counter-fed q4 form is bounded for one workgroup per CU: bounded for two, it needs
+// more than the 256 registers a wave then gets and spills to scratch memory; bounded for
+// one, it keeps its values in VGPRs and AGPRs and, although only one of its workgroups
+// then fits on a CU, measured 5-9% faster. Its grid is unchanged: workgroups past the
+// resident ones start as others finish and take items from the same counter.)
+__global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) void decode_split(
     const uint16_t* __restrict__ q, const uint8_t* pool, int64_t n_pool_pages,
     const int32_t* __restrict__ block_tables, int max_pages, const int32_t* __restrict__ context_lens,
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
