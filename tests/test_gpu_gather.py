@@ -22,7 +22,7 @@ def to_dev(a, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-@pytest.mark.parametrize("fmt", ["int8", "k8v4"])
+@pytest.mark.parametrize("fmt", ["int8", "k8v4", "fp4", "fp8"])
 @pytest.mark.parametrize("miss_rate", [0.0, 0.3, 1.0])
 def test_gather_then_attend_equals_resident(gpu, fmt, miss_rate):
     n_pages, n_slots, n_sel, steps = 40, 12, 8, 6
@@ -122,7 +122,7 @@ def draw_selections(L, n_pages, n_slots, n_sel, steps, seed):
     return sels
 
 
-@pytest.mark.parametrize("fmt", ["int8", "k8v4"])
+@pytest.mark.parametrize("fmt", ["int8", "k8v4", "fp8"])
 def test_gather_layers_equals_per_layer_gathers(gpu, fmt):
     """kv_gather_pages_layers (one launch for every layer) leaves the same tables, slots
     and block tables as kv_gather_pages per layer, and attention over them is identical."""
