@@ -258,7 +258,9 @@ def quantize_fp8(x) -> tuple[np.ndarray, np.ndarray]:
 def dequantize_fp8(codes, scales) -> np.ndarray:
     """Values +-E4M3(c & 0x7F) * d of an fp8 record (codes 0x7F / 0xFF, NaN, never occur)."""
     c = np.asarray(codes, dtype=np.int64)
-    mag = E4M3[np.minimum(c & 0x7F, 126)] * np.where(c & 0x80, -1.0, 1.0)
+    if np.any((c & 0x7F) == 0x7F):
+        raise ValueError("E4M3 NaN code (0x7F / 0xFF) in an fp8 record")
+    mag = E4M3[c & 0x7F] * np.where(c & 0x80, -1.0, 1.0)
     return mag * np.asarray(scales, dtype=np.float64)
 
 

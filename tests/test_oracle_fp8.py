@@ -134,3 +134,10 @@ def test_not_rotated():
     got = attention.decode_attention(q, kh, kh, R.FMT_FP8)
     want = attention.decode_attention(q, kh, kh, R.FMT_INT8)
     assert np.array_equal(got, want)
+
+
+def test_nan_codes_are_refused():
+    c = np.zeros((1, 256), np.uint8)
+    c[0, 5] = 0xFF
+    with pytest.raises(ValueError):
+        R.dequantize_fp8(c, np.ones((1, 1), np.float16))
