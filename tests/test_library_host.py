@@ -11,7 +11,7 @@ import pytest
 
 import offloaded_kv_cache_amd as K
 from offloaded_kv_cache_amd import _native as N
-from oracle import records
+from oracle import layout, records
 from oracle.residency import ClockTable
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kvcache.h")
@@ -36,6 +36,11 @@ def test_version_and_page_bytes():
     assert K.page_bytes(K.shape("int8")) == 540672
     assert K.page_bytes(K.shape("q4_0")) == 294912
     assert K.page_bytes(K.shape("k8v4")) == 417792
+    assert K.page_bytes(K.shape("fp4")) == 294912
+    assert K.page_bytes(K.shape("fp8")) == 528384
+    # the library's page size equals the oracle layout's for every format
+    for name, fmt in records.FORMATS.items():
+        assert K.page_bytes(K.shape(name)) == layout.page_bytes(fmt, 4), name
 
 
 @pytest.mark.parametrize("bad, code", [
@@ -50,7 +55,7 @@ def test_shape_validation(bad, code):
     s = N.KVShape(args["n_q_heads"], args["n_kv_heads"], args["head_dim"], args["page_tokens"], 1)
     assert N.lib.kv_page_bytes(C.byref(s)) == code
     assert N.last_error()
-    s.format = 7
+    s.format = 5                       # one past the last format
     s.head_dim, s.page_tokens, s.n_q_heads, s.n_kv_heads = 256, 256, 24, 4
     assert N.lib.kv_page_bytes(C.byref(s)) == N.KV_EINVAL
 
