@@ -141,3 +141,25 @@ def test_nan_codes_are_refused():
     c[0, 5] = 0xFF
     with pytest.raises(ValueError):
         R.dequantize_fp8(c, np.ones((1, 1), np.float16))
+
+
+def test_scale_rounding_exhaustive_against_rationals():
+    """d = fp16 round-to-nearest-even of the exact rational a / 448, for every positive
+    finite fp16 amax a (31,743 values, subnormals included): the oracle's scale is pinned
+    against an exact rounding written from IEEE 754 binary16, not against its own formula.
+    A scale formed by an fp32 reciprocal multiply, a * (1/448), differs on 39 of these
+    values and fails here. A plain fp32 division a / 448 happens to round to the same
+    fp16 for every value, so a GPU encoder may use either fp32 or fp64 division."""
+    from fractions import Fraction
+
+    from test_oracle_pins import fp16_values_positive, fraction_to_fp16_rne
+
+    a = fp16_values_positive().astype(np.float64)
+    x = np.zeros((a.size, 256))
+    x[:, 7] = a                       # one nonzero element: amax = a
+    x[::2, 7] *= -1                   # the sign of the largest element does not matter
+    _, d = R.quantize_fp8(x)
+    want = np.array([fraction_to_fp16_rne(Fraction(float(v)) / 448) for v in a], np.float64)
+    assert np.array_equal(d[:, 0].astype(np.float64), want)
+    # subnormal fp16 scales are part of the sweep
+    assert np.count_nonzero((want > 0) & (want < 2.0 ** -14)) > 100
