@@ -150,6 +150,22 @@ def _ptr(t, dtype=None, device=True, name="tensor"):
     return C.c_void_p(t.data_ptr())
 
 
+def _buf(t, name, pinned_ok=False):
+    """Address of a byte buffer (pool, workspace, slots): a contiguous uint8 tensor in
+    device memory (or, where the C ABI accepts it, pinned host memory). Anything else is
+    refused here, before a kernel could be handed a host address."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must be torch.uint8, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        raise ValueError(f"{name} must be in device memory" + (" or pinned host memory" if pinned_ok else ""))
+    return C.c_void_p(t.data_ptr())
+
+
 def _stream(stream):
     torch = _torch()
     if stream is None:
@@ -169,7 +185,7 @@ def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=
     _check(lib.kv_append_quantize(
         C.byref(s), _ptr(k, torch.float16, name="k"), _ptr(v, torch.float16, name="v"),
         n, start_pos, _ptr(block_table, torch.int32, name="block_table"), block_table.numel(),
-        C.c_void_p(pool.data_ptr()), pool.numel() // pb,
+        _buf(pool, "pool", pinned_ok=True), pool.numel() // pb,
         _ptr(status, torch.int32, name="status"), _stream(stream)))
 
 
@@ -227,11 +243,11 @@ def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_contex
         raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
     pb = page_bytes(s)
     _check(fn(
-        C.byref(s), _ptr(q, torch.float16, name="q"), B, C.c_void_p(pool.data_ptr()),
+        C.byref(s), _ptr(q, torch.float16, name="q"), B, _buf(pool, "pool"),
         pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
-        softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream), *extra))
+        softmax_scale, _ptr(out, torch.float32, name="out"), _buf(workspace, "workspace"),
+        workspace.numel(), pages_per_split, _stream(stream), *extra))
 
 
 def decode_attention_mq(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
@@ -248,11 +264,11 @@ def decode_attention_mq(s: KVShape, q, pool, block_tables, context_lens, max_con
         raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
     pb = page_bytes(s)
     _check(lib.kv_decode_attention_mq(
-        C.byref(s), _ptr(q, torch.float16, name="q"), B, n_q, C.c_void_p(pool.data_ptr()),
+        C.byref(s), _ptr(q, torch.float16, name="q"), B, n_q, _buf(pool, "pool"),
         pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
-        softmax_scale, _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream)))
+        softmax_scale, _ptr(out, torch.float32, name="out"), _buf(workspace, "workspace"),
+        workspace.numel(), pages_per_split, _stream(stream)))
 
 
 def append_decode(s: KVShape, k_new, v_new, q, pool, block_tables, context_lens, max_context: int,
@@ -279,11 +295,11 @@ def append_decode(s: KVShape, k_new, v_new, q, pool, block_tables, context_lens,
     pb = page_bytes(s)
     _check(lib.kv_append_decode(
         C.byref(s), _ptr(k_new, torch.float16, name="k_new"), _ptr(v_new, torch.float16, name="v_new"),
-        _ptr(q, torch.float16, name="q"), B, C.c_void_p(pool.data_ptr()), pool.numel() // pb,
+        _ptr(q, torch.float16, name="q"), B, _buf(pool, "pool"), pool.numel() // pb,
         _ptr(block_tables, torch.int32, name="block_tables"), block_tables.shape[1],
         _ptr(context_lens, torch.int32, name="context_lens"), max_context, softmax_scale,
-        _ptr(out, torch.float32, name="out"), C.c_void_p(workspace.data_ptr()),
-        workspace.numel() * workspace.element_size(), pages_per_split, _stream(stream),
+        _ptr(out, torch.float32, name="out"), _buf(workspace, "workspace"),
+        workspace.numel(), pages_per_split, _stream(stream),
         C.c_void_p(ev[0]), C.c_void_p(ev[1])))
 
 
@@ -327,7 +343,7 @@ def gather_pages(s: KVShape, table: Residency, selection, host_pool, slot_pool, 
         raise ValueError("host_pool must be pinned host memory")
     nm = C.c_int32(0)
     _check(lib.kv_gather_pages(C.byref(s), C.byref(table.c), sel.ctypes.data_as(C.c_void_p), sel.size,
-                               C.c_void_p(host_pool.data_ptr()), C.c_void_p(slot_pool.data_ptr()),
+                               _buf(host_pool, "host_pool", pinned_ok=True), _buf(slot_pool, "slot_pool"),
                                _ptr(out_block_table, torch.int32, name="out_block_table"),
                                C.byref(nm), _stream(stream)))
     return nm.value
@@ -349,8 +365,8 @@ def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, 
         if not h.is_pinned():
             raise ValueError("host pools must be pinned host memory")
     arr = (KVResidency * L)(*[t.c for t in tables])
-    hp = (C.c_void_p * L)(*[h.data_ptr() for h in host_pools])
-    sp = (C.c_void_p * L)(*[p.data_ptr() for p in slot_pools])
+    hp = (C.c_void_p * L)(*[_buf(h, "host pool", pinned_ok=True).value for h in host_pools])
+    sp = (C.c_void_p * L)(*[_buf(p, "slot pool").value for p in slot_pools])
     nm = np.zeros(L, np.int32)
     _check(lib.kv_gather_pages_layers(C.byref(s), L, arr, sel.ctypes.data_as(C.c_void_p), sel.shape[1],
                                       C.cast(hp, C.c_void_p), C.cast(sp, C.c_void_p),
@@ -396,7 +412,7 @@ def select_pages(s: KVShape, q, sums, n_pages: int, k_sel: int, out_selection, w
     _check(lib.kv_select_pages(C.byref(s), _ptr(q, torch.float16, name="q"), _ptr(sums, torch.int64, name="sums"),
                                sums.shape[-3], n_pages, k_sel, n_sets,
                                _ptr(out_selection, torch.int32, name="out_selection"),
-                               C.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                               _buf(workspace, "workspace"), workspace.numel(),
                                _stream(stream)))
 
 

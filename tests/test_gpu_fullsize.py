@@ -30,10 +30,13 @@ pytestmark = pytest.mark.gpu
 CHUNK = 2048
 
 
-def build_pool(gpu, fmt, cfg, lens, seed, g):
+def build_pool(gpu, fmt, cfg, lens, seed, g, filled=None):
     """Draw each sequence's K, V on the GPU in CHUNK-token pieces, append them into one
-    pool with a shuffled block table, and return head g's fp16 K and V per sequence."""
+    pool with a shuffled block table, and return head g's fp16 K and V per sequence
+    (g = None: every KV head). The pool has room for lens[b] tokens of sequence b;
+    filled[b] (default lens[b]) of them are appended."""
     s = K.shape(fmt)
+    filled = lens if filled is None else filled
     pages = [-(-T // 256) for T in lens]
     n_pool = sum(pages)
     perm = kvsynth.permutation_np(seed, n_pool)
@@ -42,7 +45,8 @@ def build_pool(gpu, fmt, cfg, lens, seed, g):
     gain = kvsynth.gain_torch(cfg, 0, s.n_kv_heads, gpu)
     heads = []
     off = 0
-    for b, (T, n) in enumerate(zip(lens, pages)):
+    hs = slice(None) if g is None else slice(g, g + 1)
+    for b, (T, n) in enumerate(zip(filled, pages)):
         bt[b, :n] = perm[off:off + n]
         off += n
         row = torch.from_numpy(bt[b]).to(gpu)
@@ -52,8 +56,8 @@ def build_pool(gpu, fmt, cfg, lens, seed, g):
         for t0 in range(0, T, CHUNK):
             kd, vd = kvsynth.kv_tokens_torch(gen, min(CHUNK, T - t0), gain, gpu)
             pool.append(kd, vd, t0, row)
-            kh.append(kd[:, g:g + 1].cpu().numpy())
-            vh.append(vd[:, g:g + 1].cpu().numpy())
+            kh.append(kd[:, hs].cpu().numpy())
+            vh.append(vd[:, hs].cpu().numpy())
         heads.append((np.concatenate(kh), np.concatenate(vh)))
     torch.cuda.synchronize()
     return s, pool, bt, heads
@@ -117,3 +121,81 @@ def test_k8v4_four_sequences_sampled(gpu):
         rec = head_records(kh, vh, fmt)
         want = head_oracle(q[b, 6 * g:6 * g + 6], rec, fmt)
         assert_close(got[b, 6 * g:6 * g + 6], want, what=f"k8v4 sequence {b} ({lens[b]} tokens)")
+
+
+def test_k8v4_benchmark_step_all_heads(gpu):
+    """The four-sequence k8v4 step exactly as the benchmark runs it: splits sized from the
+    batch's total length (more work items than resident workgroups, so the counter-fed
+    kernel form), each sequence's newest token appended inside the split kernel. Every KV
+    head of every sequence is checked against the oracle, and the output and the pool are
+    bit for bit those of the separate calls (append kernel, then decode attention)."""
+    fmt, cfg = "k8v4", 4
+    lens = [262144, 198000, 65536, 8192]
+    s = K.shape(fmt)
+    pps = K.decode_split_pages(s, len(lens), max(lens), sum(lens))
+    n_splits = -(-(-(-max(lens) // 256)) // pps)
+    cus = torch.cuda.get_device_properties(gpu).multi_processor_count
+    assert n_splits * s.n_kv_heads * len(lens) > cus, "not the counter-fed form"
+    q = kvsynth.q_np(cfg, 1, len(lens))
+    s, pool, bt, heads = build_pool(gpu, fmt, cfg, lens, seed=43, g=None, filled=[T - 1 for T in lens])
+    rng = np.random.default_rng(4343)
+    kn = (rng.standard_normal((len(lens), 4, 256)) * 2).astype(np.float16)
+    vn = (rng.standard_normal((len(lens), 4, 256)) * 2).astype(np.float16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    btd, ctx, qd = dev(bt), dev(np.array(lens, np.int32)), dev(q)
+    max_ctx = max(lens)
+    before = pool.data.clone()
+    ws = K.paged.DecodeWorkspace(s, len(lens), max_ctx, pps, device=gpu)
+    out = torch.empty((len(lens), 24, 256), dtype=torch.float32, device=gpu)
+    K.append_decode(s, dev(kn), dev(vn), qd, pool.data, btd, ctx, max_ctx, out, ws.data, pages_per_split=pps)
+    # the separate calls on the pool as it was before the step
+    for b, T in enumerate(lens):
+        K.append_quantize(s, dev(kn[b:b + 1]), dev(vn[b:b + 1]), T - 1, btd[b].contiguous(), before)
+    ws2 = K.paged.DecodeWorkspace(s, len(lens), max_ctx, pps, device=gpu)
+    out2 = torch.empty_like(out)
+    K.decode_attention(s, qd, before, btd, ctx, max_ctx, out2, ws2.data, pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert ws.status() == 0 and ws2.status() == 0
+    assert not ws.data[4:12].cpu().numpy().any(), "work counters not reset"
+    assert torch.equal(pool.data, before), "pool bytes differ from the separate append"
+    got = out.cpu().numpy()
+    assert np.array_equal(got, out2.cpu().numpy()), "output differs from the separate calls"
+    del before
+
+    def oracle_head(bg):
+        b, g = bg
+        kh, vh = heads[b]
+        k = np.concatenate([kh[:, g:g + 1], kn[b:b + 1, g:g + 1]])
+        v = np.concatenate([vh[:, g:g + 1], vn[b:b + 1, g:g + 1]])
+        return head_oracle(q[b, 6 * g:6 * g + 6], head_records(k, v, fmt), fmt)
+
+    # (sequence, KV head) pairs on a few host threads: numpy's large array operations
+    # release the interpreter lock
+    from concurrent.futures import ThreadPoolExecutor
+    pairs = [(b, g) for b in range(len(lens)) for g in range(4)]
+    with ThreadPoolExecutor(4) as ex:
+        for (b, g), want in zip(pairs, ex.map(oracle_head, pairs)):
+            assert_close(got[b, 6 * g:6 * g + 6], want, what=f"k8v4 sequence {b} ({lens[b]} tokens), KV head {g}")
+
+
+def test_combine_over_more_than_1024_splits(gpu):
+    """262,400 q4_0 tokens at one page per split: 1,025 splits, so the merge runs over two
+    chunks of split weights. One KV head against the oracle; the one-call decode bitwise
+    equal to the split and combine called as two phases."""
+    fmt, cfg, g, T = "q4_0", 3, 2, 262400
+    q = kvsynth.q_np(cfg, 2, 1)
+    s, pool, bt, heads = build_pool(gpu, fmt, cfg, [T], seed=47, g=g)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    btd, ctx, qd = dev(bt), dev(np.array([T], np.int32)), dev(q)
+    outs = []
+    for phases in (("all",), ("split", "combine")):
+        ws = K.paged.DecodeWorkspace(s, 1, T, 1, device=gpu)
+        out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+        for ph in phases:
+            K.decode_attention(s, qd, pool.data, btd, ctx, T, out, ws.data, pages_per_split=1, phase=ph)
+        torch.cuda.synchronize()
+        assert ws.status() == 0
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    want = head_oracle(q[0, 6 * g:6 * g + 6], head_records(*heads[0], fmt), fmt)
+    assert_close(outs[0][0, 6 * g:6 * g + 6], want, what="q4_0 262,400 tokens at 1,025 splits")

@@ -227,3 +227,34 @@ def test_host_fp8_codes_at_every_tie():
     assert float(scales[0]) == 2.0 ** -24 and codes[0] == 0x7E      # 627 saturates
     assert codes[1] == 0x80 | 0x79                                    # 300 -> 288 = 1.125 * 2^8
     assert np.array_equal(codes, records.quantize_fp8(x.astype(np.float64))[0])
+
+
+def test_binding_refuses_host_buffers_before_any_launch():
+    """A pool, workspace or slot pool in ordinary host memory is refused by the binding
+    (ValueError) before the C ABI is called, so no kernel is ever handed a host address;
+    a wrong dtype is a TypeError."""
+    import torch
+
+    host = torch.zeros(1024, dtype=torch.uint8)
+    for name in ("pool", "workspace", "slot_pool"):
+        with pytest.raises(ValueError, match="device memory"):
+            N._buf(host, name)
+    with pytest.raises(ValueError, match="pinned host memory"):
+        N._buf(host, "pool", pinned_ok=True)       # the append path also takes pinned memory
+    with pytest.raises(TypeError):
+        N._buf(torch.zeros(16, dtype=torch.float32), "workspace")
+    with pytest.raises(ValueError, match="contiguous"):
+        N._buf(torch.zeros((8, 8), dtype=torch.uint8).t(), "pool")
+    # whole calls with host tensors stop in the binding as well
+    s = K.shape("q4_0")
+    q = torch.zeros((1, 24, 256), dtype=torch.float16)
+    out = torch.zeros((1, 24, 256), dtype=torch.float32)
+    bt = torch.zeros((1, 1), dtype=torch.int32)
+    ctx = torch.ones(1, dtype=torch.int32)
+    pool = torch.zeros(K.page_bytes(s), dtype=torch.uint8)
+    ws = torch.zeros(K.decode_workspace_bytes(s, 1, 256), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        K.decode_attention(s, q, pool, bt, ctx, 256, out, ws)
+    with pytest.raises(ValueError):
+        K.append_decode(s, torch.zeros((1, 4, 256), dtype=torch.float16),
+                        torch.zeros((1, 4, 256), dtype=torch.float16), q, pool, bt, ctx, 256, out, ws)
