@@ -154,7 +154,7 @@ DYN_CASES = [
     ("mixed_total_b", [12289, 1, 5000, 257, 700], None),  # rows 0, 0, 136, 0 and 187 of a page
     ("T40000_pps1", [40000], 1),
     ("T39937_pps1", [39937], 1),   # the token in row 0 of a page that starts a split
-    ("T33000_pps2", [33000], 2),
+    ("T66000_pps2", [66000], 2),   # 129 splits x 4 KV heads
 ]
 
 
