@@ -27,6 +27,8 @@
  *     anything is enqueued.
  *   - The library allocates no device or host memory; every buffer belongs
  *     to the caller and must stay alive until the enqueued work completes.
+ *     (One exception: the fixed device array of kv_decode_attention_noalloc,
+ *     part of the library's code object, not allocated by any call.)
  *   - Pointers named "device" must be device memory (or device-accessible
  *     pinned host memory); pointers named "host" are read on the host during
  *     the call. Device buffers must be 16-byte aligned (KV_EALIGN otherwise).
@@ -208,6 +210,34 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch,
                         float softmax_scale, float* out,
                         void* workspace, size_t workspace_bytes,
                         int32_t pages_per_split, void* stream);
+
+/*
+ * kv_decode_attention_noalloc - kv_decode_attention for callers that cannot allocate
+ * device memory: code being recorded into a HIP graph, tight serving loops, and
+ * harnesses that forbid allocation. The same kernels and the same result, bit for
+ * bit, as kv_decode_attention with the same arguments, but the split partials and
+ * work counters live in a device array of the library (KV_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends) instead of a caller workspace. The call itself
+ * allocates nothing.
+ *
+ *   status   device int32 or NULL: KV_STATUS_* bits are OR-ed into it (as into a
+ *            workspace's status word); NULL = not reported.
+ * Every other argument is that of kv_decode_attention. The array of the current
+ * device (hipGetDevice, which must be the device of `stream`) is used; its address
+ * is looked up on the first call on each device, which also enqueues a small
+ * kernel that clears its header. Returns KV_ESMALL, enqueuing nothing, when the
+ * partials would need more than KV_NOALLOC_SCRATCH_BYTES (that is, when
+ * kv_decode_workspace_bytes for the same arguments exceeds it). All calls on one
+ * GPU share the array and the last call's partials stay in it: calls that overlap
+ * on one GPU (unordered streams, or other threads) race and give wrong results.
+ */
+#define KV_NOALLOC_SCRATCH_BYTES 16777216
+int kv_decode_attention_noalloc(const kv_shape* shape, const void* q, int32_t batch,
+                                const void* pool, int64_t n_pool_pages,
+                                const int32_t* block_tables, int32_t max_pages,
+                                const int32_t* context_lens, int64_t max_context,
+                                float softmax_scale, float* out, int32_t* status,
+                                int32_t pages_per_split, void* stream);
 
 /*
  * kv_decode_mq_workspace_bytes - bytes of workspace kv_decode_attention_mq needs for

@@ -25,7 +25,7 @@ FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4, "fp4":
 EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
-    "kv_decode_split_timed",
+    "kv_decode_split_timed", "kv_decode_attention_noalloc",
     "kv_decode_combine", "kv_decode_attention_mq", "kv_decode_mq_workspace_bytes", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
     "kv_select_workspace_bytes", "kv_select_pages",
     "kv_residency_reset",
@@ -75,6 +75,8 @@ def _load():
                                         P, P, SZ, I32, P]),
         "kv_decode_split_timed": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
                                             P, P, SZ, I32, P, P, P]),
+        "kv_decode_attention_noalloc": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
+                                                  P, P, I32, P]),
         "kv_decode_mq_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I32, I64, I32]),
         "kv_decode_attention_mq": (C.c_int, [C.POINTER(KVShape), P, I32, I32, P, I64, P, I32, P, I64,
                                              F32, P, P, SZ, I32, P]),
@@ -248,6 +250,29 @@ def decode_attention(s: KVShape, q, pool, block_tables, context_lens, max_contex
         block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
         softmax_scale, _ptr(out, torch.float32, name="out"), _buf(workspace, "workspace"),
         workspace.numel(), pages_per_split, _stream(stream), *extra))
+
+
+NOALLOC_SCRATCH_BYTES = 16777216  # KV_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,
+                             status=None, softmax_scale: float = 1.0 / 16.0, pages_per_split: int = 0,
+                             stream=None):
+    """kv_decode_attention_noalloc: decode_attention without a workspace (the library's own
+    device array holds the partials). ``status``: device int32 [1] or None."""
+    torch = _torch()
+    B = q.shape[0]
+    if q.shape != (B, s.n_q_heads, s.head_dim) or out.shape != (B, s.n_q_heads, s.head_dim):
+        raise ValueError("q and out must be [batch, n_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [batch, max_pages] and context_lens [batch]")
+    pb = page_bytes(s)
+    _check(lib.kv_decode_attention_noalloc(
+        C.byref(s), _ptr(q, torch.float16, name="q"), B, _buf(pool, "pool"),
+        pool.numel() // pb, _ptr(block_tables, torch.int32, name="block_tables"),
+        block_tables.shape[1], _ptr(context_lens, torch.int32, name="context_lens"), max_context,
+        softmax_scale, _ptr(out, torch.float32, name="out"), _ptr(status, torch.int32, name="status"),
+        pages_per_split, _stream(stream)))
 
 
 def decode_attention_mq(s: KVShape, q, pool, block_tables, context_lens, max_context: int, out,

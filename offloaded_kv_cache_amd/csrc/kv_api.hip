@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -204,19 +205,51 @@ int32_t kv_decode_split_pages(const kv_shape* shape, int32_t batch, int64_t max_
 
 namespace {
 
+// Device memory of kv_decode_attention_noalloc: split partials, work counters and a status
+// word, in place of a caller workspace (laid out as one). Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it.
+static __device__ __align__(256) uint8_t scratch[KV_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices];  // the device address of each device's copy, once looked up
+
+// The current device's copy of `scratch` (the device of the caller's stream). Its address
+// is looked up once per device, with that device current; host code uses only that
+// address, never the array's name (a host-side stand-in). The first lookup also enqueues
+// the clearing of the header (status word, work counters) on `stream`; every later call
+// leaves the counters at zero, as the decode kernels do with a workspace.
+int scratch_of_device(hipStream_t stream, uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KV_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress of the scratch array");
+    e = launch_zero_words(static_cast<uint32_t*>(p), 64, stream);  // the 256-byte header
+    if (e != hipSuccess) return hip_fail(e, "scratch header clear");
+    g_scratch[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return KV_OK;
+}
+
 int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch, const void* pool,
                  int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
                  const int32_t* context_lens, int64_t max_context, float softmax_scale, float* out,
                  void* workspace, size_t workspace_bytes, int32_t pages_per_split, void* stream,
                  void* start_event = nullptr, void* stop_event = nullptr,
-                 const void* k_new = nullptr, const void* v_new = nullptr, int32_t n_q = 1) {
+                 const void* k_new = nullptr, const void* v_new = nullptr, int32_t n_q = 1,
+                 bool noalloc = false, int32_t* status = nullptr) {
   if (int r = check_shape(shape)) return r;
   if (n_q < 1) return fail(KV_EINVAL, "n_q must be >= 1 (got %d)", n_q);
   if (batch < 0 || (int64_t)batch * n_q > 65535)
     return fail(KV_EINVAL, "batch x n_q out of range (%d x %d)", batch, n_q);
   if (batch == 0) return ok();
   const int32_t rows = batch * n_q;  // query rows: the kernels treat each as a sequence
-  if (!q || !pool || !block_tables || !context_lens || !out || !workspace)
+  if (!q || !pool || !block_tables || !context_lens || !out || (!workspace && !noalloc))
     return fail(KV_EINVAL, "NULL buffer");
   if (max_pages < 1) return fail(KV_EINVAL, "max_pages must be >= 1");
   if (max_context < 0 || max_context > 0x7FFFFFFF) return fail(KV_EINVAL, "max_context out of range");
@@ -224,16 +257,24 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   if (pages_per_split < 0) return fail(KV_EINVAL, "pages_per_split must be >= 0");
   if (!(softmax_scale == softmax_scale)) return fail(KV_EINVAL, "softmax_scale is NaN");
   if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
-    return fail(KV_EALIGN, "misaligned buffer (q, pool, out: 16 B; workspace: 256 B)");
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(status, 4))
+    return fail(KV_EALIGN, "misaligned buffer (q, pool, out: 16 B; workspace: 256 B; status: 4 B)");
   const int64_t bound = max_context < (int64_t)max_pages * kPageTokens ? max_context
                                                                        : (int64_t)max_pages * kPageTokens;
   const int64_t max_pages_ctx = (max_context + kPageTokens - 1) / kPageTokens;
   const int32_t pps = pages_per_split ? pages_per_split : auto_pages_per_split(shape, rows, max_pages_ctx);
   const WsLayout w = workspace_layout(shape, rows, max_context, pps);
-  if (workspace_bytes < w.total)
+  if (noalloc) {
+    if (w.total > KV_NOALLOC_SCRATCH_BYTES)
+      return fail(KV_ESMALL, "the call needs %zu bytes of split partials, beyond the library's %d-byte scratch array",
+                  w.total, KV_NOALLOC_SCRATCH_BYTES);
+    uint8_t* sp = nullptr;
+    if (int r = scratch_of_device((hipStream_t)stream, &sp)) return r;
+    workspace = sp;
+  } else if (workspace_bytes < w.total) {
     return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
                 w.total);
+  }
   uint8_t* ws = (uint8_t*)workspace;
   DecodeArgs a;
   a.fmt = shape->format;
@@ -252,7 +293,7 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.n_splits = w.n_splits;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
-  a.status = (int32_t*)ws;
+  a.status = status ? status : (int32_t*)ws;
   a.sched = (uint32_t*)(ws + 4);
   a.part_ml = (float*)(ws + w.ml_off);
   a.part_o = (float*)(ws + w.o_off);
@@ -278,6 +319,15 @@ int kv_decode_attention(const kv_shape* shape, const void* q, int32_t batch, con
   return decode_phase(3, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
                       max_context, softmax_scale, out, workspace, workspace_bytes, pages_per_split,
                       stream);
+}
+
+int kv_decode_attention_noalloc(const kv_shape* shape, const void* q, int32_t batch, const void* pool,
+                                int64_t n_pool_pages, const int32_t* block_tables, int32_t max_pages,
+                                const int32_t* context_lens, int64_t max_context, float softmax_scale,
+                                float* out, int32_t* status, int32_t pages_per_split, void* stream) {
+  return decode_phase(3, shape, q, batch, pool, n_pool_pages, block_tables, max_pages, context_lens,
+                      max_context, softmax_scale, out, nullptr, 0, pages_per_split, stream, nullptr,
+                      nullptr, nullptr, nullptr, 1, true, status);
 }
 
 int kv_decode_attention_mq(const kv_shape* shape, const void* q, int32_t batch, int32_t n_q,

@@ -1238,7 +1238,16 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t star
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void zero_words(uint32_t* __restrict__ p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, int n_words, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_words, dim3(1), dim3(64), 0, stream, p, n_words);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream, hipEvent_t start,
                          hipEvent_t stop) {

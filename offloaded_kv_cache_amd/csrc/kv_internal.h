@@ -182,6 +182,10 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int phase, hipStream_t stream,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
+// Sets n_words 32-bit words at p to zero with a small kernel on `stream` (a kernel rather
+// than a memset, so that it can also be recorded into a HIP graph).
+hipError_t launch_zero_words(uint32_t* p, int n_words, hipStream_t stream);
+
 // Page selection (kv_select.hip).
 hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
                            int64_t* sums, hipStream_t stream);

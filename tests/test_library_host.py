@@ -258,3 +258,30 @@ def test_binding_refuses_host_buffers_before_any_launch():
     with pytest.raises(ValueError):
         K.append_decode(s, torch.zeros((1, 4, 256), dtype=torch.float16),
                         torch.zeros((1, 4, 256), dtype=torch.float16), q, pool, bt, ctx, 256, out, ws)
+
+
+def test_noalloc_refuses_what_its_array_cannot_hold():
+    """kv_decode_attention_noalloc checks its arguments and the size of the partials before
+    it touches the device: beyond KV_NOALLOC_SCRATCH_BYTES it returns KV_ESMALL."""
+    s = K.shape("q4_0")
+    P = C.c_void_p
+    lib = N.lib
+    assert N.NOALLOC_SCRATCH_BYTES == 16 << 20
+    r = lib.kv_decode_attention_noalloc(C.byref(s), None, 1, None, 1, None, 1, None, 4096, 0.0625, None,
+                                        None, 0, None)
+    assert r == N.KV_EINVAL
+    r = lib.kv_decode_attention_noalloc(C.byref(s), P(256), 1, P(256), 16, P(256), 16, P(256), 4096, 0.0625,
+                                        P(256), P(258), 0, None)
+    assert r == N.KV_EALIGN                          # a misaligned status word
+    # the largest context that fits at one page per split, then one page (one split) more
+    ctx = 256
+    while K.decode_workspace_bytes(s, 1, ctx + 256, 1) <= N.NOALLOC_SCRATCH_BYTES:
+        ctx += 256
+    assert K.decode_workspace_bytes(s, 1, ctx, 1) <= N.NOALLOC_SCRATCH_BYTES
+    r = lib.kv_decode_attention_noalloc(C.byref(s), P(256), 1, P(256), 4096, P(256), 4096, P(256), ctx + 256,
+                                        0.0625, P(256), None, 1, None)
+    assert r == N.KV_ESMALL and "scratch" in N.last_error()
+    # a batch far beyond the array at the library's own split size
+    r = lib.kv_decode_attention_noalloc(C.byref(s), P(256), 4096, P(256), 4096, P(256), 4096, P(256), 1 << 20,
+                                        0.0625, P(256), None, 0, None)
+    assert r == N.KV_ESMALL
