@@ -97,12 +97,11 @@ def build_resident(args, wl, dev, per_step=1):
             for t0 in range(0, start_lens[b], chunk):
                 n = min(chunk, start_lens[b] - t0)
                 k, v = kvsynth.kv_tokens_torch(gen, n, gain, dev)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                pool.append(k, v, t0, row)
-                e1.record()
+                # the append kernel's own start and end (events recorded by its launch)
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                pool.append(k, v, t0, row, events=ev if n == chunk else None)
                 if n == chunk:
-                    append_ev.append((e0, e1))
+                    append_ev.append(ev)
         pools.append(pool)
         tables.append(bt)
         torch.cuda.synchronize()

@@ -157,6 +157,20 @@ int kv_append_quantize(const kv_shape* shape, const void* k, const void* v,
                        int32_t* status, void* stream);
 
 /*
+ * kv_append_quantize with measurement events: identical work and checks, and the
+ * append kernel is launched with hipExtLaunchKernelGGL so that `start_event` and
+ * `stop_event` (hipEvent_t created by the caller, may be NULL) are recorded when the
+ * kernel itself starts and ends on `stream` (its duration without the queueing gap in
+ * front of it, as a kernel trace reports it). Nothing is recorded for n_tokens == 0.
+ */
+int kv_append_quantize_timed(const kv_shape* shape, const void* k, const void* v,
+                             int64_t n_tokens, int64_t start_pos,
+                             const int32_t* block_table, int32_t n_table,
+                             void* pool, int64_t n_pool_pages,
+                             int32_t* status, void* stream,
+                             void* start_event, void* stop_event);
+
+/*
  * kv_decode_workspace_bytes - bytes of workspace kv_decode_attention needs
  * for `batch` sequences of at most `max_context` tokens, with the given
  * pages_per_split (0 = the library's choice, as in kv_decode_attention).

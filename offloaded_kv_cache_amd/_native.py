@@ -23,7 +23,7 @@ FORMATS = {"int8": KV_FMT_INT8, "q4_0": KV_FMT_Q4_0, "k8v4": KV_FMT_K8V4, "fp4":
            "fp8": KV_FMT_FP8}
 
 EXPORTED_SYMBOLS = (
-    "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize",
+    "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize", "kv_append_quantize_timed",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed", "kv_decode_attention_noalloc",
     "kv_decode_combine", "kv_decode_attention_mq", "kv_decode_mq_workspace_bytes", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
@@ -65,6 +65,7 @@ def _load():
         "kv_version": (C.c_char_p, []),
         "kv_page_bytes": (I64, [C.POINTER(KVShape)]),
         "kv_append_quantize": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, P, I32, P, I64, P, P]),
+        "kv_append_quantize_timed": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, P, I32, P, I64, P, P, P, P]),
         "kv_decode_workspace_bytes": (SZ, [C.POINTER(KVShape), I32, I64, I32]),
         "kv_decode_split_pages": (I32, [C.POINTER(KVShape), I32, I64, I64]),
         "kv_decode_attention": (C.c_int, [C.POINTER(KVShape), P, I32, P, I64, P, I32, P, I64, F32,
@@ -175,8 +176,22 @@ def _stream(stream):
     return C.c_void_p(stream.cuda_stream)
 
 
-def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=None, stream=None):
-    """Quantize-on-append of tokens [start_pos, start_pos + k.shape[0]) of one sequence."""
+def _event_ptrs(events):
+    if events is None:
+        return ()
+    ev = []
+    for e in events:
+        if not e.cuda_event:
+            e.record()  # creates the underlying event
+        ev.append(C.c_void_p(e.cuda_event))
+    return tuple(ev)
+
+
+def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=None, stream=None,
+                    events=None):
+    """Quantize-on-append of tokens [start_pos, start_pos + k.shape[0]) of one sequence.
+    ``events`` = (start, stop) torch.cuda.Event pair: recorded at the append kernel's own
+    start and end (kv_append_quantize_timed)."""
     torch = _torch()
     n = k.shape[0]
     if k.shape != v.shape or k.dim() != 3 or k.shape[1] != s.n_kv_heads or k.shape[2] != s.head_dim:
@@ -184,11 +199,14 @@ def append_quantize(s: KVShape, k, v, start_pos: int, block_table, pool, status=
     pb = page_bytes(s)
     if pool.numel() % pb:
         raise ValueError("pool size is not a whole number of pages")
-    _check(lib.kv_append_quantize(
+    fn, ev = lib.kv_append_quantize, _event_ptrs(events)
+    if ev:
+        fn = lib.kv_append_quantize_timed
+    _check(fn(
         C.byref(s), _ptr(k, torch.float16, name="k"), _ptr(v, torch.float16, name="v"),
         n, start_pos, _ptr(block_table, torch.int32, name="block_table"), block_table.numel(),
         _buf(pool, "pool", pinned_ok=True), pool.numel() // pb,
-        _ptr(status, torch.int32, name="status"), _stream(stream)))
+        _ptr(status, torch.int32, name="status"), _stream(stream), *ev))
 
 
 def decode_workspace_bytes(s: KVShape, batch: int, max_context: int, pages_per_split: int = 0) -> int:

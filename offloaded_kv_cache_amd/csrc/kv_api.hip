@@ -139,6 +139,14 @@ int64_t kv_page_bytes(const kv_shape* shape) {
 int kv_append_quantize(const kv_shape* shape, const void* k, const void* v, int64_t n_tokens,
                        int64_t start_pos, const int32_t* block_table, int32_t n_table, void* pool,
                        int64_t n_pool_pages, int32_t* status, void* stream) {
+  return kv_append_quantize_timed(shape, k, v, n_tokens, start_pos, block_table, n_table, pool, n_pool_pages,
+                                  status, stream, nullptr, nullptr);
+}
+
+int kv_append_quantize_timed(const kv_shape* shape, const void* k, const void* v, int64_t n_tokens,
+                             int64_t start_pos, const int32_t* block_table, int32_t n_table, void* pool,
+                             int64_t n_pool_pages, int32_t* status, void* stream, void* start_event,
+                             void* stop_event) {
   if (int r = check_shape(shape)) return r;
   if (n_tokens < 0 || start_pos < 0) return fail(KV_EINVAL, "negative n_tokens or start_pos");
   if (n_tokens == 0) return ok();
@@ -154,7 +162,8 @@ int kv_append_quantize(const kv_shape* shape, const void* k, const void* v, int6
     return fail(KV_EINVAL, "too many tokens in one call");
   hipError_t e = launch_append(shape->format, shape->n_kv_heads, (const uint16_t*)k,
                                (const uint16_t*)v, n_tokens, start_pos, block_table, n_table,
-                               (uint8_t*)pool, n_pool_pages, status, (hipStream_t)stream);
+                               (uint8_t*)pool, n_pool_pages, status, (hipStream_t)stream,
+                               (hipEvent_t)start_event, (hipEvent_t)stop_event);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   return ok();
 }

@@ -32,13 +32,16 @@ __device__ inline double xchg_enc(double v, int lane) {
   return __shfl_xor(v, M);
 }
 
+// (partner + y in the lower lane of a pair, partner - y in the upper one, each as one fma
+// with a sign of +-1: the product is exact, and so is the sum, whose exact value is
+// representable, so the result is the exact butterfly)
 template <int M, bool DPP>
 __device__ inline void wht_stage(double (&y)[4], int lane) {
-  const bool upper = lane & M;
+  const double sg = (lane & M) ? -1.0 : 1.0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const double o = xchg_enc<M, DPP>(y[k], lane);
-    y[k] = upper ? (o - y[k]) : (y[k] + o);
+    y[k] = __builtin_fma(sg, y[k], o);
   }
 }
 template <int M, bool DPP>
@@ -214,13 +217,11 @@ __device__ inline void encode(const uint16_t* __restrict__ src, int lane, int (&
   encode_vals<KIND, DPP>(in, lane, code, scale);
 }
 
-// K plane row of a token (token-major, slice-permuted code bytes).
+// K plane row of a token (token-major, slice-permuted code bytes): its code bytes at
+// `codes`, its n_scales(KIND) fp16 scales at `scales` (in the plane, or a staging copy).
 template <int KIND>
-__device__ inline void write_k_row(uint8_t* __restrict__ plane, int row, int lane,
-                                   const int (&code)[4], const uint16_t (&scale)[4]) {
-  uint8_t* codes = plane + (size_t)row * code_row_bytes(KIND);
-  uint16_t* scales = reinterpret_cast<uint16_t*>(plane + kPageTokens * code_row_bytes(KIND)) +
-                     row * n_scales(KIND);
+__device__ inline void write_k_row_at(uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, int lane,
+                                      const int (&code)[4], const uint16_t (&scale)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = lane + 64 * k;
@@ -246,6 +247,14 @@ __device__ inline void write_k_row(uint8_t* __restrict__ plane, int row, int lan
 #pragma unroll
     for (int k = 0; k < 4; ++k) scales[(lane >> 5) + 2 * k] = scale[k];
   }
+}
+
+template <int KIND>
+__device__ inline void write_k_row(uint8_t* __restrict__ plane, int row, int lane, const int (&code)[4],
+                                   const uint16_t (&scale)[4]) {
+  write_k_row_at<KIND>(plane + (size_t)row * code_row_bytes(KIND),
+                       reinterpret_cast<uint16_t*>(plane + kPageTokens * code_row_bytes(KIND)) + row * n_scales(KIND),
+                       lane, code, scale);
 }
 
 template <int KIND>

@@ -103,7 +103,8 @@ __host__ __device__ inline int q4_code(double y, double d) {
 hipError_t launch_append(int fmt, int n_kv_heads, const uint16_t* k, const uint16_t* v,
                          int64_t n_tokens, int64_t start_pos, const int32_t* block_table,
                          int32_t n_table, uint8_t* pool, int64_t n_pool_pages,
-                         int32_t* status, hipStream_t stream);
+                         int32_t* status, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 
 // fp4 record helpers (rules in include/kvcache.h). a = max |y| of a block (exact, a
 // normal double or 0): the block exponent clamp(floor(log2 a) - 2, -23, 13).

@@ -27,8 +27,8 @@ class PagedPool:
     def page(self, i: int):
         return self.data[i * self.page_bytes:(i + 1) * self.page_bytes]
 
-    def append(self, k, v, start_pos: int, block_table, status=None, stream=None):
-        N.append_quantize(self.shape, k, v, start_pos, block_table, self.data, status, stream)
+    def append(self, k, v, start_pos: int, block_table, status=None, stream=None, events=None):
+        N.append_quantize(self.shape, k, v, start_pos, block_table, self.data, status, stream, events)
 
 
 class DecodeWorkspace:
