@@ -64,13 +64,16 @@ int check_shape(const kv_shape* s) {
 
 int64_t page_bytes_of(const kv_shape* s) { return (int64_t)s->n_kv_heads * head_stride(s->format); }
 
+std::mutex g_cu_mu;
+int g_cus[64];  // per device, 0 until read
+
 // Pages per split chosen so that the grid fills the 256 compute units once: two
 // 4-wave workgroups per CU, or one 8-wave workgroup (int8 K), over all the
 // (sequence, KV head, split) items of `total_pages` pages. Each sequence's last
 // split may be partial, so the other batch - 1 sequences keep one workgroup per KV
 // head in reserve (a second, nearly empty round of workgroups would double the time).
 int32_t pages_per_split_for(const kv_shape* s, int32_t batch, int64_t total_pages) {
-  const int64_t target = kComputeUnits * (8 / split_waves(k_kind(s->format)));
+  const int64_t target = (int64_t)device_compute_units() * (8 / split_waves(k_kind(s->format)));
   int64_t room = target - (int64_t)(batch - 1) * s->n_kv_heads;
   if (room < s->n_kv_heads) room = s->n_kv_heads;
   int64_t pps = (total_pages * s->n_kv_heads + room - 1) / room;
@@ -123,6 +126,24 @@ int validate_selection(const kv_residency* t, const int32_t* selection, int32_t 
 }
 
 }  // namespace
+
+int kvc::device_compute_units() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (!g_cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return kDefaultComputeUnits;
+    }
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
 
 extern "C" {
 
@@ -300,6 +321,7 @@ int decode_phase(int phase, const kv_shape* shape, const void* q, int32_t batch,
   a.max_context = (int32_t)bound;
   a.pages_per_split = pps;
   a.n_splits = w.n_splits;
+  a.n_cus = device_compute_units();
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.status = status ? status : (int32_t*)ws;

@@ -438,7 +438,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
     int max_context, int n_q_heads, int n_kv_heads, int pages_per_split, int n_splits,
     float scale_log2, float* __restrict__ part_ml, float* __restrict__ part_o,
     int32_t* __restrict__ status, uint32_t* __restrict__ sched, int batch, int n_q,
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint8_t* pool_w) {
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint8_t* pool_w, int n_cus) {
   __shared__ __attribute__((aligned(16))) SplitLds<NW> lds;
   __shared__ int item_s;
   constexpr int TPW = kPageTokens / NW, KT = TPW / 16;  // Q.K: tokens and tiles per wave
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
     enc::load_vals((wave & 1 ? v_new : k_new) + ((size_t)b * n_kv_heads + g) * kHeadDim, lane, new_in);
   const int32_t phys_new = new_pg >= 0 ? bt_row_entry(block_tables, bs, max_pages, new_pg) : -1;
   // (the appending workgroup, which also encodes the token, keeps it one page longer)
-  const int boost_until = (!DYN && NW == 4 && ((int)blockIdx.x >= kComputeUnits || new_pg >= 0))
+  const int boost_until = (!DYN && NW == 4 && ((int)blockIdx.x >= n_cus || new_pg >= 0))
                               ? min(p_end, p_begin + (p_end - p_begin) / 2 + (new_pg >= 0 ? 1 : 0))
                               : p_begin;
   if (boost_until > p_begin) __builtin_amdgcn_s_setprio(1);
@@ -1220,7 +1220,7 @@ void launch_split_v(const DecodeArgs& a, dim3 grid, hipStream_t stream, hipEvent
                         stop, 0, a.q, a.pool, a.n_pool_pages, a.block_tables, a.max_pages,
                         a.context_lens, a.max_context, a.n_q_heads, a.n_kv_heads, a.pages_per_split,
                         a.n_splits, a.scale_log2, a.part_ml, a.part_o, a.status, a.sched, a.batch,
-                        a.n_q, a.k_new, a.v_new, a.pool_w);
+                        a.n_q, a.k_new, a.v_new, a.pool_w, a.n_cus);
 }
 
 template <int KK, int VK>
@@ -1228,7 +1228,7 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream, hipEvent_t star
   constexpr int NW = split_waves(KK);
   // one round of resident workgroups (two 4-wave or one 8-wave per CU), at most one per item
   const int64_t items = (int64_t)a.n_splits * a.n_kv_heads * a.batch;
-  const int64_t resident = kComputeUnits * (8 / NW);
+  const int64_t resident = (int64_t)a.n_cus * (8 / NW);
   const dim3 grid((unsigned)(items < resident ? items : resident));
   const bool dyn = items > resident, app = a.k_new != nullptr;
   if (dyn && app) launch_split_v<KK, VK, true, true>(a, grid, stream, start, stop);

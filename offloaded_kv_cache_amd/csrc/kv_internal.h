@@ -14,7 +14,12 @@ namespace kvc {
 
 constexpr int kHeadDim = 256;
 constexpr int kPageTokens = 256;
-constexpr int kComputeUnits = 256;  // MI355X: 8 XCDs x 32 CUs
+constexpr int kDefaultComputeUnits = 256;  // MI355X (8 XCDs x 32 CUs): used when no device is visible
+
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount, read once per
+// device); kDefaultComputeUnits when no device can be queried (host-only use of the sizing
+// functions). The split sizes and grids are chosen from it.
+int device_compute_units();
 constexpr int kMaxGroup = 8;  // query heads per KV head handled by one MFMA row tile
 
 enum RecordKind : int { kInt8 = 0, kQ4 = 1, kFp4 = 2, kFp8 = 3 };
@@ -165,6 +170,7 @@ struct DecodeArgs {
   int32_t max_context;        // clamp bound, already min(max_context, max_pages * 256)
   int32_t pages_per_split;
   int32_t n_splits;           // grid size along the context
+  int32_t n_cus = kDefaultComputeUnits;  // compute units of the device (grid sizing)
   float scale_log2;           // softmax_scale * log2(e)
   float* out;
   int32_t* status;

@@ -328,6 +328,27 @@ def test_decode_split_timed_matches_split(gpu):
     assert_close(outs[1], oracle_out(q, seqs, fmt))
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_append_timed_matches_append(gpu, fmt):
+    """kv_append_quantize_timed writes the same bytes as kv_append_quantize (a ragged chunk
+    of 700 tokens from position 45, so both edge groups are partly covered) and records
+    its events."""
+    s = K.shape(fmt)
+    k, v = kvsynth.kv_tokens_np(27, 0, 0, 0, 745)
+    bt = to_dev(np.array([2, 0, 3, 1], np.int32), gpu)
+    pools = []
+    for timed in (False, True):
+        pool = K.paged.PagedPool(fmt, 4, device=gpu)
+        pool.data.copy_(torch.from_numpy(np.random.default_rng(5).integers(0, 256, pool.data.numel(), dtype=np.uint8)))
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+        pool.append(to_dev(k[45:], gpu), to_dev(v[45:], gpu), 45, bt, events=ev)
+        torch.cuda.synchronize()
+        if timed:
+            assert ev[0].elapsed_time(ev[1]) > 0
+        pools.append(pool.data.cpu().numpy())
+    assert np.array_equal(pools[0], pools[1])
+
+
 def extreme_v(v, fmt):
     """Plant V vectors whose scales leave the folded-constant range: a huge one
     (q4: y = H v has one element 32,000, so d = -4,000; int8: one element 8,000,
