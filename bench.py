@@ -46,12 +46,51 @@ PAGE = 256
 
 WORKLOADS = {
     "c1": dict(fmt="q4_0", layers=1, lens=[4096], cfg=1),
+    # the same 4,096-token layer in 112 copies (528 MB, more than the 256 MB Infinity Cache),
+    # attended in turn: every launch reads its pages from HBM
+    "c1cold": dict(fmt="q4_0", layers=112, lens=[4096], cfg=1),
     "c2": dict(fmt="int8", layers=16, lens=[32768], cfg=2),
     "c3": dict(fmt="q4_0", layers=16, lens=[131072], cfg=3),
-    "c4": dict(fmt="k8v4", layers=16, lens=[262144, 198000, 65536, 8192], cfg=4),
+    # the headline shape at the top of the 128K-1M context range
+    "c3m": dict(fmt="q4_0", layers=16, lens=[1048576], cfg=3),
+    "c4": dict(fmt="k8v4", layers=16, lens=[262144, 198000, 65536, 8192], cfg=4, cpu_seq=2),
     "c3fp4": dict(fmt="fp4", layers=16, lens=[131072], cfg=3),
     "c3fp8": dict(fmt="fp8", layers=16, lens=[131072], cfg=3),
 }
+
+WORKLOAD_TEXT = {
+    "c1": "1 layer, 4,096-token q4_0 context (warm: the layer's 4.7 MB stay in the Infinity Cache)",
+    "c1cold": "112 copies of a 1-layer 4,096-token q4_0 context attended in turn (cold: 528 MB, read from HBM)",
+    "c2": "16 layers, 32,768-token int8 context",
+    "c3": "16 layers, 131,072-token q4_0 context (append 1 token + decode per layer)",
+    "c3m": "16 layers, 1,048,576-token q4_0 context (append 1 token + decode per layer)",
+    "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4",
+    "c3fp4": "16 layers, 131,072-token fp4 context (append 1 token + decode per layer)",
+    "c3fp8": "16 layers, 131,072-token fp8 context (append 1 token + decode per layer)",
+}
+
+
+def host_info():
+    """The host the oracle runs on: CPU model, usable cores, BLAS library and its threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            blas = {"library": pools[0].get("internal_api"), "version": pools[0].get("version"),
+                    "threads": max(i.get("num_threads", 1) for i in pools)}
+    except Exception:
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "blas": blas}
 
 
 def log(*a):
@@ -272,9 +311,10 @@ def cpu_baseline(args, wl, dev, state):
     fmt, cfg = wl["fmt"], wl["cfg"]
     fmt_id = records.FORMATS[fmt]
     kk, vk = records.kinds(fmt_id)
-    T = min(args.cpu_tokens, wl["lens"][0])
+    seq = wl.get("cpu_seq", 0)
+    T = min(args.cpu_tokens, wl["lens"][seq])
     gen = torch.Generator(device=dev)
-    gen.manual_seed(kvsynth.torch_seed(cfg, 0, 0))
+    gen.manual_seed(kvsynth.torch_seed(cfg, 0, seq))
     gain = kvsynth.gain_torch(cfg, 0, 4, dev)
     ks, vs = [], []
     for t0 in range(0, T, 2048):
@@ -284,11 +324,8 @@ def cpu_baseline(args, wl, dev, state):
     k = np.concatenate(ks)
     v = np.concatenate(vs)
     q = torch.randn((1, 24, 256), generator=gen, device=dev).to(torch.float16).cpu().numpy()[0]
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = None
+    host = host_info()
+    threads = (host["blas"] or {}).get("threads") or 1
     # records (the append side), then the timed attention sample: dequantize + attention
     t0 = time.perf_counter()
     kc, ksc = records.encode(k[:2048].astype(np.float64), kk)
@@ -307,14 +344,57 @@ def cpu_baseline(args, wl, dev, state):
         if el >= args.cpu_seconds or reps >= 64:
             break
     gbs = T * kv_bytes_per_token(fmt) * reps / el / 1e9
-    return dict(value=gbs, unit="GB/s", cores=threads or os.cpu_count(), kind="oracle",
-                sample=f"1 layer x {T} tokens of the same workload, fp64 dequantize + attention, "
-                       f"{reps} pass(es) in {el:.1f} s; oracle quantizer on a 2,048-token chunk "
-                       f"(4 KV heads, K and V): {quant_s:.2f} s",
-                host_cpus=len(os.sched_getaffinity(0)))
+    which = f"sequence {seq} ({wl['lens'][seq]:,} tokens) of the {len(wl['lens'])}" if len(wl["lens"]) > 1 else "the"
+    return dict(value=gbs, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"1 layer x {T:,} tokens of {which} workload's sequence(s), fp64 dequantize + attention "
+                       f"(numpy: BLAS products on {threads} thread(s), elementwise work on 1), {reps} pass(es) "
+                       f"in {el:.1f} s; the rate applies to every layer and sequence alike; oracle quantizer "
+                       f"on a 2,048-token chunk (4 KV heads, K and V): {quant_s:.2f} s",
+                host=host)
 
 
 C5 = dict(fmt="int8", layers=16, host_tokens=1048576, slots=128, n_sel=8, miss=0.3, cfg=5)
+
+
+def cpu_baseline_streaming(args):
+    """The oracle's streaming step on the host: per layer, the CLOCK step of a selection of 8
+    pages (oracle/residency.py) and fp64 attention over the 2,048 selected tokens, for the 16
+    layers of a step, repeated for the time budget."""
+    import numpy as np
+
+    import kvsynth
+    from oracle import attention, records
+    from oracle.residency import ClockTable
+
+    c = C5
+    n_pages = args.host_tokens // PAGE
+    fmt_id = records.FORMATS[c["fmt"]]
+    kk, vk = records.kinds(fmt_id)
+    ctx = c["n_sel"] * PAGE
+    k, v = kvsynth.kv_tokens_np(c["cfg"], 0, 0, 0, ctx)
+    kc, ksc = records.encode(k.astype(np.float64), kk)
+    vc, vsc = records.encode(v.astype(np.float64), vk)
+    q = kvsynth.q_np(c["cfg"], 0, 1)[0]
+    rng = np.random.default_rng(1000 * c["cfg"] + 1)
+    tables = [ClockTable(c["slots"], n_pages) for _ in range(c["layers"])]
+    host = host_info()
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        for layer in range(c["layers"]):
+            tables[layer].select(rng.choice(n_pages, c["n_sel"], replace=False))
+            attention.decode_attention(q, records.decode(kc, ksc, kk), records.decode(vc, vsc, vk), fmt_id)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= args.cpu_seconds or steps >= 1000:
+            break
+    gbs = steps * c["layers"] * ctx * kv_bytes_per_token(c["fmt"]) / el / 1e9
+    threads = (host["blas"] or {}).get("threads") or 1
+    return dict(value=gbs, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{steps} streaming step(s) of 16 layers x (CLOCK step of 8 pages + fp64 dequantize and "
+                       f"attention over the {ctx:,} selected int8 tokens) in {el:.1f} s (numpy: BLAS products on "
+                       f"{threads} thread(s), elementwise work on 1)",
+                host=host)
 
 
 def streaming_selection(rng, table, n_pages, n_sel, miss):
@@ -533,6 +613,55 @@ def counter_traffic(workload: str):
     return traffic if sha == kernel_code_hash() else None
 
 
+def _short_kernel(name: str) -> str:
+    import re
+    m = re.search(r"(decode_split<[^>]*>|append_kernel<[^>]*>|decode_combine|gather\w*|select\w*|key_sums\w*|copyBuffer)",
+                  name)
+    return m.group(1) if m else name[:60]
+
+
+def summarize_trace(root: str, last: int):
+    """Kernel durations from a rocprofv3 --kernel-trace -f csv directory: every dispatch of each
+    kernel of this library, then the last `last` dispatches of each decode kernel (the timed
+    steps)."""
+    import csv
+    import glob
+    import statistics as st
+    by = {}
+    for f in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = _short_kernel(r["Kernel_Name"])
+            by.setdefault(k, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    lines = ["  kernel                                    calls    avg us    min us    max us"]
+    for k, v in sorted(by.items()):
+        d = [(b - a) / 1000 for a, b in v]
+        lines.append(f"  {k:40s} {len(d):6d} {st.mean(d):9.2f} {min(d):9.2f} {max(d):9.2f}")
+    lines.append(f"last {last} dispatches of each decode kernel:")
+    for k, v in sorted(by.items()):
+        if "decode" in k:
+            d = [(b - a) / 1000 for a, b in sorted(v)[-last:]]
+            lines.append(f"  {k:40s} n={len(d)} mean {st.mean(d):9.2f} us  median {st.median(d):9.2f}  "
+                         f"min {min(d):8.2f}  max {max(d):8.2f}")
+    return "\n".join(lines)
+
+
+def summarize_counters(root: str):
+    """Per kernel, the mean per dispatch of each counter of a rocprofv3 --pmc -f csv directory."""
+    import csv
+    import glob
+    agg = {}
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            agg.setdefault(_short_kernel(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+    lines = []
+    for k, d in sorted(agg.items()):
+        lines.append(f"{k}")
+        for c, v in sorted(d.items()):
+            lines.append(f"    {c:32s} mean per dispatch {sum(v) / len(v):16.1f}  (dispatches {len(v)})")
+    return "\n".join(lines)
+
+
 def copy_calibration(args, dev):
     """A plain copy of known size: its counter readings scale the decode kernel's."""
     import torch
@@ -583,6 +712,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-hash", action="store_true",
                     help="print the code hash of the decode kernel source (comments removed) and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print kernel durations from a rocprofv3 --kernel-trace -f csv output directory and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-dispatch counter means from a rocprofv3 --pmc -f csv output directory and exit")
+    ap.add_argument("--last", type=int, default=80, help="with --summarize-trace: decode dispatches of the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB --steps times "
                          "(reference kernel for calibrating HBM byte counters) and exit")
@@ -591,6 +725,12 @@ def main():
         args.steps = 100 if args.workload == "c5" else 30
     if args.kernel_hash:
         print(kernel_code_hash())
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.last))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: it measures the single-GPU decode path "
@@ -611,7 +751,8 @@ def main():
             "value": round(res["value"], 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "int8 KV, fp32 accumulate", "data": "synthetic",
-            "config": res["config"], "gather": res["gather"], "cpu_baseline": None}), flush=True)
+            "config": res["config"], "gather": res["gather"],
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_streaming(args)}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if args.queries > 1:
@@ -657,12 +798,7 @@ def main():
                   "k8v4": "int8 K / q4_0 V, fp32 accumulate", "fp4": "fp4 (e2m1) KV, fp32 accumulate",
                   "fp8": "fp8 (e4m3) KV, fp32 accumulate"}[fmt],
         "data": "synthetic",
-        "config": {"workload": {"c1": "1 layer, 4,096-token q4_0 context",
-                                "c2": "16 layers, 32,768-token int8 context",
-                                "c3": "16 layers, 131,072-token q4_0 context (append 1 token + decode per layer)",
-                                "c4": "16 layers, 4 sequences 262,144/198,000/65,536/8,192 tokens, k8v4",
-                                "c3fp4": "16 layers, 131,072-token fp4 context (append 1 token + decode per layer)",
-                                "c3fp8": "16 layers, 131,072-token fp8 context (append 1 token + decode per layer)"}[args.workload],
+        "config": {"workload": WORKLOAD_TEXT[args.workload],
                    "layers": wl["layers"], "n_q_heads": 24, "n_kv_heads": 4, "head_dim": 256,
                    "page_tokens": 256, "batch": len(wl["lens"]), "context": wl["lens"],
                    "kv_format": fmt, "pages_per_split": args.pages_per_split or "auto",
