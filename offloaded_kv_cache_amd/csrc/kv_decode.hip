@@ -466,7 +466,35 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
     __syncthreads();
   }
   if (item >= n_items) break;
-  const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
+  int split, b, g;
+  if (n_q == 1) {
+    split = item / n_pairs;
+    b = (item - split * n_pairs) / n_kv_heads;
+    g = item % n_kv_heads;
+  } else {
+    // Several query rows per sequence: the n_q rows of one (split, sequence, KV head) read
+    // the same pages. Workgroups go to the eight XCDs round-robin by index, each XCD with its
+    // own L2, so the rows of such a group take indices eight apart (one XCD) and close
+    // together (dispatched about together), and the pages they share are read from HBM once.
+    // Row groups come in chunks of eight: chunk c, XCD x holds group 8c + x, its row j at
+    // index 8 (n_q c + j) + x; a last partial chunk of m < 8 groups is laid out row by row.
+    const int R = n_items / n_q, full = (R / 8) * 8 * n_q;
+    int r, j;
+    if (item < full) {
+      const int sx = item / 8;
+      r = (sx / n_q) * 8 + item % 8;
+      j = sx % n_q;
+    } else {
+      const int m = R % 8, l = item - full;
+      r = (R / 8) * 8 + l % m;
+      j = l / m;
+    }
+    const int n_seq_kv = n_pairs / n_q;  // (sequence, KV head) pairs
+    split = r / n_seq_kv;
+    const int rem = r - split * n_seq_kv;
+    g = rem % n_kv_heads;
+    b = (rem / n_kv_heads) * n_q + j;
+  }
 
   // Issued together before anything waits: the query of the group's heads (element
   // tid; unconditional loads of a clamped head), the context length and the split's

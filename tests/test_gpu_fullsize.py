@@ -1,18 +1,20 @@
 """Parity at full benchmark sizes, in the launch configuration the benchmark uses.
 
-* One layer of 131,072 tokens in q4_0 (24 query / 4 KV heads), and the same in
-  fp4 and fp8, and one layer of 32,768 int8 tokens: the cache is written by the
-  append kernel in 2,048-token chunks through a shuffled block table, decoded
-  with the automatic split count; one KV head's six query heads are checked
-  against the fp64 oracle, and sampled pages of that head are checked byte for
-  byte against the oracle's records.
+* One layer of 131,072 tokens in q4_0 (24 query / 4 KV heads), the same in fp4
+  and fp8, one layer of 32,768 int8 tokens and one of 1,048,576 q4_0 tokens: the
+  cache is written by the append kernel in 2,048-token chunks through a shuffled
+  block table, then the decode step appends the last token inside the split
+  kernel with the automatic split count. Output and pool equal those of the
+  separate append and decode calls bit for bit; every KV head (two at 1,048,576
+  tokens) is checked against the fp64 oracle, and sampled pages of those heads
+  byte for byte against the oracle's records.
 * Four k8v4 sequences of 262,144 / 198,000 / 65,536 / 8,192 tokens in one
   shuffled pool (the 198,000-token one ends in a 112-token page): one KV head
   of every sequence is checked against the oracle.
 
 K and V are drawn on the GPU (seeded, the benchmark's distribution) and appended
-chunk by chunk; the checked head's fp16 K and V are copied back and the oracle
-encodes only that head (its cost is the rotation of every vector of that head).
+chunk by chunk; the checked heads' fp16 K and V are copied back and the oracle
+encodes only those heads (its cost is the rotation of every vector of a head).
 """
 
 import numpy as np
@@ -89,26 +91,61 @@ def head_oracle(q_heads, rec, fmt):
     return attention.decode_attention(q_heads, kh, vh, fmt_id(fmt))
 
 
-LAYERS = [("q4_0", 131072, 3), ("fp4", 131072, 3), ("fp8", 131072, 3), ("int8", 32768, 2)]
+LAYERS = [("q4_0", 131072, 3), ("fp4", 131072, 3), ("fp8", 131072, 3), ("int8", 32768, 2),
+          ("q4_0", 1048576, 3)]   # the top of the 128K-1M context range (32 pages per split)
 
 
 @pytest.mark.parametrize("fmt, T, cfg", LAYERS, ids=[f"{f}_{t}" for f, t, _ in LAYERS])
 def test_one_layer_sampled(gpu, fmt, T, cfg):
-    g = 1
+    """One layer at full size in the benchmark's form: tokens 0 .. T-2 appended in chunks, then
+    the decode step that appends token T-1 inside the split kernel (kv_append_decode, the
+    library's split size). Output and pool equal the separate calls bit for bit; every KV head
+    (two of them at 1,048,576 tokens, to bound the host's oracle time) is checked against the
+    oracle, and sampled pages of those heads byte for byte against the oracle's records."""
+    heads_checked = [0, 1, 2, 3] if T <= 131072 else [0, 3]
     q = kvsynth.q_np(cfg, 0, 1)
-    s, pool, bt, heads = build_pool(gpu, fmt, cfg, [T], seed=31, g=g)
-    got = decode(gpu, s, pool, bt, q, [T])
-    rec = head_records(*heads[0], fmt)
-    want = head_oracle(q[0, 6 * g:6 * g + 6], rec, fmt)
-    assert_close(got[0, 6 * g:6 * g + 6], want, what=f"{fmt} {T}, KV head 1")
-    # sampled pages of the checked head, byte for byte
-    one_head = layout.pack_pages(*rec, fmt_id(fmt))      # pages of a 1-KV-head layout
-    hs = one_head.shape[1]                                # bytes of one head's K + V planes
+    s, pool, bt, heads = build_pool(gpu, fmt, cfg, [T], seed=31, g=None, filled=[T - 1])
+    rng = np.random.default_rng(3131)
+    kn = (rng.standard_normal((1, 4, 256)) * 2).astype(np.float16)
+    vn = (rng.standard_normal((1, 4, 256)) * 2).astype(np.float16)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    btd, ctx, qd = dev(bt), dev(np.array([T], np.int32)), dev(q)
+    before = pool.data.clone()
+    ws = K.paged.DecodeWorkspace(s, 1, T, 0, device=gpu)
+    out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
+    K.append_decode(s, dev(kn), dev(vn), qd, pool.data, btd, ctx, T, out, ws.data)
+    K.append_quantize(s, dev(kn), dev(vn), T - 1, btd[0].contiguous(), before)
+    ws2 = K.paged.DecodeWorkspace(s, 1, T, 0, device=gpu)
+    out2 = torch.empty_like(out)
+    K.decode_attention(s, qd, before, btd, ctx, T, out2, ws2.data)
+    torch.cuda.synchronize()
+    assert ws.status() == 0 and ws2.status() == 0
+    assert torch.equal(pool.data, before), "pool bytes differ from the separate append"
+    got = out.cpu().numpy()
+    assert np.array_equal(got, out2.cpu().numpy()), "output differs from the separate calls"
+    del before
+    kh, vh = heads[0]
     pb = K.page_bytes(s)
-    for p in (0, 1, T // 512, T // 256 - 1):
-        phys = int(bt[0, p])
-        dev = pool.data[phys * pb + g * hs: phys * pb + (g + 1) * hs].cpu().numpy()
-        assert np.array_equal(dev, one_head[p]), f"page {p}"
+
+    def check_head(g):
+        k = np.concatenate([kh[:, g:g + 1], kn[:, g:g + 1]])
+        v = np.concatenate([vh[:, g:g + 1], vn[:, g:g + 1]])
+        rec = head_records(k, v, fmt)
+        return rec, head_oracle(q[0, 6 * g:6 * g + 6], rec, fmt)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(4) as ex:
+        results = list(ex.map(check_head, heads_checked))
+    for g, (rec, want) in zip(heads_checked, results):
+        assert_close(got[0, 6 * g:6 * g + 6], want, what=f"{fmt} {T}, KV head {g}")
+        # sampled pages of the head, byte for byte (first, second, middle and last page);
+        # a page packs on its own, so only the sampled pages are packed
+        for p in (0, 1, T // 512, (T - 1) // 256):
+            one_head = layout.pack_pages(*(r[256 * p:256 * (p + 1)] for r in rec), fmt_id(fmt))[0]
+            hs = one_head.shape[0]                            # bytes of one head's K + V planes
+            phys = int(bt[0, p])
+            dev_bytes = pool.data[phys * pb + g * hs: phys * pb + (g + 1) * hs].cpu().numpy()
+            assert np.array_equal(dev_bytes, one_head), f"KV head {g}, page {p}"
 
 
 def test_k8v4_four_sequences_sampled(gpu):
