@@ -444,9 +444,9 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
   constexpr int TPW = kPageTokens / NW, KT = TPW / 16;  // Q.K: tokens and tiles per wave
   constexpr int EPW = kHeadDim / NW, NTW = EPW / 16;    // P.V: elements and column tiles per wave
   constexpr int HFN = NTW / 2;                           // P.V halves of two column tiles
+  constexpr int kHPW = kMaxGroup / NW;                   // query head slots per wave (prologue)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int elem = tid & (kHeadDim - 1);  // the query element of the thread (prologue)
   const int grp = lane >> 4, col = lane & 15;  // MFMA lane group and column
   const int G = n_q_heads / n_kv_heads;
   const int n_pairs = n_kv_heads * batch, n_items = n_splits * n_pairs;
@@ -499,12 +499,18 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
   // Issued together before anything waits: the query of the group's heads (element
   // tid; unconditional loads of a clamped head), the context length and the split's
   // first block-table entry (index clamped into the table).
-  float qv[kMaxGroup];
+  // Wave w holds head slots HPW w .. HPW w + HPW - 1, lane l elements l + 64k (k = 0..3)
+  // of each: element bits 0-5 are the lane, bits 6-7 the register.
+  float qv[kHPW * 4];
 #pragma unroll
-  for (int hh = 0; hh < kMaxGroup; ++hh) {
-    const int hc = min(hh, G - 1);
-    const float x = (float)__builtin_bit_cast(_Float16, q[((size_t)b * n_q_heads + g * G + hc) * kHeadDim + elem]);
-    qv[hh] = hh < G ? x : 0.f;
+  for (int i = 0; i < kHPW; ++i) {
+    const int hh = kHPW * wave + i, hc = min(hh, G - 1);
+    const uint16_t* qh = q + ((size_t)b * n_q_heads + g * G + hc) * kHeadDim + lane;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float x = (float)__builtin_bit_cast(_Float16, qh[64 * k]);
+      qv[4 * i + k] = hh < G ? x : 0.f;
+    }
   }
   const int p_begin = split * pages_per_split;
   const int bs = n_q == 1 ? b : b / n_q;            // the sequence of query row b
@@ -618,100 +624,100 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
     for (int t = 0; t < KT; ++t) kt[t] = load_ktile<KK>(r0, koff[t], ksoff[t]);
   }
 
-  // (all eight head slots are transformed, unused ones hold zeros, so that each step's
-  // exchanges are in flight together)
+  // The query prepared inside each wave for its head slots: rotation by H (q4 and fp4 K),
+  // block sums for the code offsets (q4, int8), and the fp16 hi + lo A fragments written
+  // straight into their MFMA layout in LDS; one workgroup barrier, then every wave reads
+  // all eight fragments. (All head slots are prepared; unused ones hold zeros.)
   if (four_bit(KK)) {
-    // butterflies inside the wave
+    // element bits 0-5: butterflies between lanes; bits 6-7: a 4-point stage in registers
     butterfly<1>(qv, lane);
     butterfly<2>(qv, lane);
     butterfly<4>(qv, lane);
     butterfly<8>(qv, lane);
     butterfly<16>(qv, lane);
     butterfly<32>(qv, lane);
-    if (tid < kHeadDim) {
 #pragma unroll
-      for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
-    }
-    __syncthreads();
-    const int e0 = tid & 63, k = (tid >> 6) & 3;  // bits 6 and 7: a 4-point transform across waves
-    const float sg1 = (k & 1) ? -1.0f : 1.0f, sg2 = (k & 2) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) {
-      const float x0 = lds.qs[hh][e0], x1 = lds.qs[hh][e0 + 64], x2 = lds.qs[hh][e0 + 128],
-                  x3 = lds.qs[hh][e0 + 192];
-      const float s01 = fmaf(sg1, x1, x0), s23 = fmaf(sg1, x3, x2);
-      qv[hh] = fmaf(sg2, s23, s01) * 0.0625f;
-    }
-    __syncthreads();
-  }
-  if (tid < kHeadDim) {
-#pragma unroll
-    for (int hh = 0; hh < kMaxGroup; ++hh) lds.qs[hh][tid] = qv[hh];
-  }
-  __syncthreads();
-  if (KK == kInt8 || KK == kQ4) {
-    // block sums of the (rotated) query: 8 blocks of 32 elements (q4) or 4 groups of 64 (int8),
-    // for the code offsets (fp4 and fp8 codes carry no offset)
-    constexpr int nb = KK == kQ4 ? 8 : 4, bl = kHeadDim / nb;
-    if (tid < kMaxGroup * nb) {
-      const int hh = tid / nb, j = tid % nb;
-      const f4* src = reinterpret_cast<const f4*>(&lds.qs[hh][j * bl]);
-      f4 acc = src[0];
-#pragma unroll
-      for (int u = 1; u < bl / 4; ++u) acc += src[u];
-      lds.bsum[hh][j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    for (int i = 0; i < kHPW; ++i) {
+      float* x = qv + 4 * i;
+      const float s01p = fmaf(1.0f, x[1], x[0]), s01m = fmaf(-1.0f, x[1], x[0]);
+      const float s23p = fmaf(1.0f, x[3], x[2]), s23m = fmaf(-1.0f, x[3], x[2]);
+      x[0] = fmaf(1.0f, s23p, s01p) * 0.0625f;
+      x[1] = fmaf(1.0f, s23m, s01m) * 0.0625f;
+      x[2] = fmaf(-1.0f, s23p, s01p) * 0.0625f;
+      x[3] = fmaf(-1.0f, s23m, s01m) * 0.0625f;
     }
   }
-  __syncthreads();
-
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) load_vcodes<VK>(vsh, r0, voff[nt], nt);
   load_vscales<VK>(vsh, r0, vsoff);
-
-  // A operands of Q.K: row r = 2*head + part; MFMA j covers block j (elements 32j..32j+31)
-  const int a_head = col >> 1, a_part = col & 1;
-  const bool a_live = a_head < G;
-  const float* qrow = lds.qs[a_head];
-  // The eight fragments are alike in every wave: each wave builds 8 / NW of them into
-  // LDS (the P.V fragment area, unused until the first page's softmax) and all read them.
-  h8 qa[8];
+  // Block sums by lane exchange (xchgf: each value with itself; this compiler folds the
+  // second result of a row or half-wave swap of two different values into the first).
+  if constexpr (KK == kQ4) {
+    // block j = element bits 5-7 = 2k + lane bit 5: sums over lane bits 0-4
+    static_assert(NW == 4, "q4 K: two head slots per wave");
 #pragma unroll
-  for (int jj = 0; jj < 8 / NW; ++jj) {
-    const int j = (8 / NW) * wave + jj;
-    float f[8];
-    if (KK == kFp4) {
-      // slots [e, e+16, e+1, e+17, e+2, e+18, e+3, e+19] with e = 32j + 4grp (byte w of the
-      // lane's dword: low nibble element e + w, high nibble e + 16 + w)
-      const f4 lo4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp);
-      const f4 hi4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp + 16);
-      f[0] = lo4[0]; f[1] = hi4[0]; f[2] = lo4[1]; f[3] = hi4[1];
-      f[4] = lo4[2]; f[5] = hi4[2]; f[6] = lo4[3]; f[7] = hi4[3];
-    } else if (KK == kQ4) {
-      // slots [e, e+2, e+16, e+18, e+1, e+3, e+17, e+19] with e = 32j + 4grp; high-nibble slots hold q/16
-      const f4 lo4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp);
-      const f4 hi4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 4 * grp + 16) * 0.0625f;
-      f[0] = lo4[0]; f[1] = lo4[2]; f[2] = hi4[0]; f[3] = hi4[2];
-      f[4] = lo4[1]; f[5] = lo4[3]; f[6] = hi4[1]; f[7] = hi4[3];
+    for (int u = 0; u < kHPW * 4; ++u) {
+      float sum = half_sum(qv[u], lane);
+      sum += xchgf<16>(sum, lane);
+      if ((lane & 31) == 0) lds.bsum[kHPW * wave + u / 4][2 * (u % 4) + (lane >> 5)] = sum;
+    }
+  } else if constexpr (KK == kInt8) {
+    // group j = element bits 6-7 = k: sums over all 64 lanes
+    static_assert(NW == 8, "int8 K: one head slot per wave");
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float sum = half_sum(qv[u], lane);
+      sum += xchgf<16>(sum, lane);
+      sum += xchgf<32>(sum, lane);
+      if (lane == 0) lds.bsum[wave][u] = sum;
+    }
+  }
+  // A operands of Q.K: row r = 2 head + part (hi, lo) of lane 16 gq + r, fragment j = block j
+  // (elements 32j .. 32j + 31); slot order within a lane's eight halves:
+  //   q4:  [e, e+2, e+16, e+18, e+1, e+3, e+17, e+19], e = 32j + 4gq, high-nibble slots hold q/16
+  //   fp4: [e, e+16, e+1, e+17, e+2, e+18, e+3, e+19], e = 32j + 4gq
+  //   int8, fp8: e .. e + 7, e = 32j + 8gq
+  {
+    _Float16* af = reinterpret_cast<_Float16*>(&lds.afrag[0][0]);
+    const int o = lane & 31;
+    int gq, slot;
+    if (KK == kQ4) {
+      const int w = o & 3;
+      gq = (o & 15) >> 2;
+      slot = ((w & 1) << 2) | (w >> 1) | ((o >> 4) << 1);
+    } else if (KK == kFp4) {
+      gq = (o & 15) >> 2;
+      slot = 2 * (o & 3) + (o >> 4);
     } else {
-      const f4 a4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 8 * grp);
-      const f4 b4 = *reinterpret_cast<const f4*>(qrow + 32 * j + 8 * grp + 4);
-      f[0] = a4[0]; f[1] = a4[1]; f[2] = a4[2]; f[3] = a4[3];
-      f[4] = b4[0]; f[5] = b4[1]; f[6] = b4[2]; f[7] = b4[3];
+      gq = o >> 3;
+      slot = o & 7;
     }
-    // hi = f truncated to fp16, lo = the exact remainder truncated: ~21 bits together
-    u4 w;
+    const float sc = (KK == kQ4 && (o & 16)) ? 0.0625f : 1.0f;
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f[2 * s2], f[2 * s2 + 1]));
-      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f[2 * s2] - (float)hi[0], f[2 * s2 + 1] - (float)hi[1]));
-      w[s2] = a_live ? as_u32(a_part ? lo : hi) : 0u;
+    for (int u = 0; u < kHPW * 4; u += 2) {
+      // hi = the value truncated to fp16, lo = the remainder truncated: ~21 bits together
+      const float f0 = qv[u] * sc, f1 = qv[u + 1] * sc;
+      const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f0, f1));
+      const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(f0 - (float)hi[0], f1 - (float)hi[1]));
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const int hh = kHPW * wave + (u + v) / 4, k = (u + v) % 4;
+        const int j = 2 * k + (lane >> 5);
+        const int at = (j * 64 + 16 * gq + 2 * hh) * 8 + slot;
+        af[at] = hi[v];
+        af[at + 8] = lo[v];
+      }
     }
-    lds.afrag[j][lane] = __builtin_bit_cast(h8, w);
   }
   __syncthreads();
+
+  // A operands of Q.K and of the offset correction (row 2 head + part, k-slot j of lane
+  // group 0 = block sum j)
+  const int a_head = col >> 1, a_part = col & 1;
+  const bool a_live = a_head < G;
+  h8 qa[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) qa[j] = lds.afrag[j][lane];
-  // A operand of the offset correction: row 2*head + part, k-slot j (lane group 0) = block sum j
   h8 qc;
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -732,7 +738,6 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
   f4 oacc[NTW];
 #pragma unroll
   for (int t = 0; t < NTW; ++t) oacc[t] = (f4){0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
   // On a later page the token is written here, once the query is prepared and its inputs
   // (loaded first) have long arrived, and before the loop issues any load of its page.
   if (APPEND && new_pg > p_begin) append_token(new_in);
