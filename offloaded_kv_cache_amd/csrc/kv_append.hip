@@ -7,17 +7,23 @@
 // rotated q4_0 V). The rounding rules are those of include/kvcache.h.
 //
 // One workgroup of 16 waves handles a 32-token group (tokens 32G .. 32G+31, which
-// lie in one page) of one KV head: waves 0-7 encode the group's K vectors, four
-// tokens each; waves 8-15 its V vectors, the token pairs (i, i + 16) that share the
-// bytes of a 4-bit V row, two pairs each (one vector per wave at a time,
-// kv_encode.h). The records are assembled in LDS and then written whole: the
-// group's K rows and scale rows are contiguous in the token-major K plane, and in
-// the element-major V plane each of the 256 element rows receives one 16-byte
-// (4-bit codes) or 32-byte (8-bit codes) segment, instead of one byte per token.
-// Tokens of the group outside the chunk keep their bytes: the segments of a
-// partly covered group are merged with the bytes already in the pool, code by code
-// (a 4-bit V byte holds two tokens), and only the covered tokens' K rows and scales
-// are written. Appends to one page from different calls must be ordered.
+// lie in one page) of one KV head: waves 0-7 encode the group's K vectors, waves 8-15
+// its V vectors, four vectors per wave. Lane l of a wave holds vector l >> 4, elements
+// 16 (l & 15) + i (i = 0..15): the rotation's stages for element bits 0-3 run inside the
+// lane and those for bits 4-7 between the 16 lanes of a row, and a 32-element block is
+// two neighbouring lanes, a 64-element group four. The fp64 rotation is exact for fp16
+// inputs (partial sums are multiples of 2^-24 below 2^24 before the 1/16), so the order
+// of its stages does not change the result; scales and codes follow the rounding rules
+// of include/kvcache.h exactly (kv_encode.h). A V wave holds tokens (i, i + 16) in
+// vectors v and v + 2, whose 4-bit codes share the bytes of the element-major V plane.
+// The records are assembled in LDS and then written whole: the group's K rows and
+// scale rows are contiguous in the token-major K plane, and in the element-major V
+// plane each of the 256 element rows receives one 16-byte (4-bit codes) or 32-byte
+// (8-bit codes) segment, instead of one byte per token. Tokens of the group outside
+// the chunk keep their bytes: the segments of a partly covered group are merged with
+// the bytes already in the pool, code by code (a 4-bit V byte holds two tokens), and
+// only the covered tokens' K rows and scales are written. Appends to one page from
+// different calls must be ordered.
 #include <hip/hip_ext.h>
 
 #include "kv_encode.h"
@@ -26,10 +32,164 @@ namespace kvc {
 namespace {
 
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 32;                // tokens of a work item
 constexpr int kAppendWaves = 16;
 constexpr int kAppendThreads = 64 * kAppendWaves;
+
+// ---- four vectors per wave: lane l holds vector l >> 4, elements 16 (l & 15) + i
+
+// Butterfly stage of element bit log2(M) + 4 (M = 1, 2, 4, 8: lanes s and s ^ M of a row).
+template <int M>
+__device__ inline void mv_lane_stage(double (&y)[16], int lane) {
+  const double sg = (lane & M) ? -1.0 : 1.0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = __builtin_fma(sg, y[i], xchg64<M>(y[i], lane));
+}
+// Exact H x / 16 of the lane's 16 elements.
+__device__ inline void mv_wht(double (&y)[16], int lane) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!(i & h)) {
+        const double a = y[i], b = y[i + h];
+        y[i] = a + b;
+        y[i + h] = a - b;
+      }
+  mv_lane_stage<1>(y, lane);
+  mv_lane_stage<2>(y, lane);
+  mv_lane_stage<4>(y, lane);
+  mv_lane_stage<8>(y, lane);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] *= 0.0625;
+}
+__device__ inline double mv_absmax(const double (&y)[16]) {
+  double m = fabs(y[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) m = fmax(m, fabs(y[i]));
+  return m;
+}
+
+// Codes of the lane's 16 elements and the scale of its block (q4, fp4: the 32 elements
+// of lanes 2b, 2b + 1), group (int8: 64 elements, lanes 4g .. 4g + 3) or vector (fp8).
+template <int KIND>
+__device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane, int (&code)[16]) {
+  double x[16];
+  {
+    const u4* p = reinterpret_cast<const u4*>(src + 16 * (lane & 15));
+    const u4 a = p[0], b = p[1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t wa = a[i >> 1], wb = b[i >> 1];
+      x[i] = f16_to_f64((uint16_t)(wa >> (16 * (i & 1))));
+      x[8 + i] = f16_to_f64((uint16_t)(wb >> (16 * (i & 1))));
+    }
+  }
+  uint16_t scale;
+  if (KIND == kInt8) {
+    double a = mv_absmax(x);
+    a = fmax(a, xchg64<1>(a, lane));
+    a = fmax(a, xchg64<2>(a, lane));
+    scale = enc::f64_to_f16_fast(a / 127.0);
+    const double d = f16_to_f64(scale);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = enc::int8_code_fast(x[i], d);
+  } else if (KIND == kFp8) {
+    double a = mv_absmax(x);
+    a = fmax(a, xchg64<1>(a, lane));
+    a = fmax(a, xchg64<2>(a, lane));
+    a = fmax(a, xchg64<4>(a, lane));
+    a = fmax(a, xchg64<8>(a, lane));
+    scale = enc::f64_to_f16_fast(a / 448.0);
+    const double d = f16_to_f64(scale);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = fp8_code(x[i], d);
+  } else {
+    mv_wht(x, lane);
+    double m = mv_absmax(x);
+    m = fmax(m, xchg64<1>(m, lane));
+    if (KIND == kFp4) {
+      const int e = fp4_block_exp(m);
+      scale = m == 0.0 ? (uint16_t)0 : fp16_pow2_bits(e);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = m == 0.0 ? 0 : fp4_code(x[i], e);
+    } else {
+      // the block's first element holding the largest |y| (the lower lane's elements come
+      // first), then its signed value
+      double first = 0.0;
+      uint32_t hit = 0u;
+#pragma unroll
+      for (int i = 15; i >= 0; --i) {
+        const bool h = fabs(x[i]) == m;
+        first = h ? x[i] : first;
+        hit |= h ? 1u : 0u;
+      }
+      const double pf = xchg64<1>(first, lane);
+      const uint32_t ph = xchg32<1>(hit, lane);
+      const double best = (lane & 1) ? (ph ? pf : first) : (hit ? first : pf);
+      scale = enc::f64_to_f16_fast(-best * 0.125);  // -m/8 exact
+      const double d = f16_to_f64(scale);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) code[i] = enc::q4_code_fast(x[i], d);
+    }
+  }
+  return scale;
+}
+
+// The 16 codes of a lane as nibbles of two dwords (code i at bits 4 (i & 7) of word i >> 3).
+__device__ inline void mv_nibbles(const int (&c)[16], uint32_t& n0, uint32_t& n1) {
+  n0 = 0u;
+  n1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    n0 |= (uint32_t)c[i] << (4 * i);
+    n1 |= (uint32_t)c[8 + i] << (4 * i);
+  }
+}
+
+// Staging of one token's K record: code row (slice-permuted bytes) and scales.
+template <int KIND>
+__device__ inline void mv_stage_k(uint8_t* __restrict__ row, uint16_t* __restrict__ sc, int lane,
+                                  const int (&code)[16], uint16_t scale) {
+  const int s = lane & 15, j = s >> 1;  // elements 16 s .. 16 s + 15 lie in block j
+  if (!four_bit(KIND)) {
+    // byte 64 (r >> 3) + 8 j + (r & 7) = code of element 32 j + r: two runs of 8 bytes
+    u2 w0 = {0u, 0u}, w1 = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      w0[i >> 2] |= ((uint32_t)code[i] & 0xFFu) << (8 * (i & 3));
+      w1[i >> 2] |= ((uint32_t)code[8 + i] & 0xFFu) << (8 * (i & 3));
+    }
+    const int r0 = 16 * (s & 1);
+    *reinterpret_cast<u2*>(row + 64 * (r0 >> 3) + 8 * j) = w0;
+    *reinterpret_cast<u2*>(row + 64 * ((r0 + 8) >> 3) + 8 * j) = w1;
+    if (KIND == kInt8) {
+      if ((s & 3) == 0) sc[s >> 2] = scale;
+    } else if (s == 0) {
+      sc[0] = scale;
+    }
+  } else {
+    // byte 32 sl + 4 j + w = code[32 j + 4 sl + w] | code[32 j + 16 + 4 sl + w] << 4: the
+    // even lane (elements r < 16 of the block) takes the odd lane's codes
+    uint32_t n0, n1;
+    mv_nibbles(code, n0, n1);
+    const uint32_t h0 = xchg32<1>(n0, lane), h1 = xchg32<1>(n1, lane);
+    if (!(s & 1)) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const uint32_t lo = sl < 2 ? n0 >> (16 * sl) : n1 >> (16 * (sl - 2));
+        const uint32_t hi = sl < 2 ? h0 >> (16 * sl) : h1 >> (16 * (sl - 2));
+        uint32_t w = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w |= (((lo >> (4 * q)) & 0xFu) | (((hi >> (4 * q)) & 0xFu) << 4)) << (8 * q);
+        *reinterpret_cast<uint32_t*>(row + 32 * sl + 4 * j) = w;
+      }
+      sc[j] = scale;
+    }
+  }
+}
 
 template <int KK, int VK>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
@@ -62,57 +222,40 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   const size_t stride = (size_t)n_kv_heads * kHeadDim;
   auto src = [&](const uint16_t* x, int i) { return x + (size_t)(t0 + i - start) * stride + (size_t)h * kHeadDim; };
 
+  const int vi = lane >> 4, s = lane & 15;  // the lane's vector and its 16 elements
+  // the wave's four tokens: K waves 4w .. 4w + 3; V waves (i, i + 1, i + 16, i + 17), i = 2 (w - 8)
+  const int ti = wave < 8 ? 4 * wave + vi : 2 * (wave - 8) + (vi & 1) + 16 * (vi >> 1);
+  const int tc = ti < lo ? lo : (ti >= hi ? hi - 1 : ti);  // (tokens outside the chunk read a valid row)
+  int code[16];
   if (wave < 8) {
-    // K: tokens 4 wave .. 4 wave + 3 of the group, each record into its staging row
-#pragma unroll 1
-    for (int u = 0; u < 4; ++u) {
-      const int i = 4 * wave + u;
-      if (i < lo || i >= hi) continue;  // uniform over the wave
-      int code[4];
-      uint16_t scale[4];
-      enc::encode<KK, true>(src(k, i), lane, code, scale);
-      enc::write_k_row_at<KK>(kt + i * KR, ks + i * KS, lane, code, scale);
-    }
+    const uint16_t scale = mv_encode<KK>(src(k, tc), lane, code);
+    mv_stage_k<KK>(kt + ti * KR, ks + ti * KS, lane, code, scale);
   } else {
-    // V: token pairs (i, i + 16), i = 2 (wave - 8) and 2 (wave - 8) + 1
-#pragma unroll 1
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * (wave - 8) + u;
-      int lo_code[4] = {0, 0, 0, 0};
-#pragma unroll 1
-      for (int half = 0; half < 2; ++half) {
-        const int ti = i + 16 * half;
-        if (ti < lo || ti >= hi) continue;  // uniform over the wave
-        int code[4];
-        uint16_t scale[4];
-        enc::encode<VK, true>(src(v, ti), lane, code, scale);
-        // scale rows (one per group or block of elements, one entry per token)
-        if (VK == kFp8) {
-          if (lane == 0) vs[ti] = scale[0];
-        } else if (VK == kInt8) {
-          if (lane == 0) {
+    const uint16_t scale = mv_encode<VK>(src(v, tc), lane, code);
+    // scale rows (one per block, group or vector), one entry per token
+    if (VK == kFp8) {
+      if (s == 0) vs[ti] = scale;
+    } else if (VK == kInt8) {
+      if ((s & 3) == 0) vs[(s >> 2) * kGroup + ti] = scale;
+    } else if (!(s & 1)) {
+      vs[(s >> 1) * kGroup + ti] = scale;
+    }
+    // element rows: 8-bit codes at byte ti; the 4-bit codes of tokens ti (vectors 0, 1) and
+    // ti + 16 (vectors 2, 3, lanes 32 further) share byte ti
+    if (!four_bit(VK)) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) vs[kk * kGroup + ti] = scale[kk];
-          }
-        } else if ((lane & 31) == 0) {
+      for (int i = 0; i < 16; ++i) vt[(16 * s + i) * VB + ti] = (uint8_t)code[i];
+    } else {
+      uint32_t n0, n1;
+      mv_nibbles(code, n0, n1);
+      const uint32_t p0 = xchg32<32>(n0, lane), p1 = xchg32<32>(n1, lane);
+      if (vi < 2) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) vs[((lane >> 5) + 2 * kk) * kGroup + ti] = scale[kk];
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t l4 = ((i < 8 ? n0 : n1) >> (4 * (i & 7))) & 0xFu;
+          const uint32_t h4 = ((i < 8 ? p0 : p1) >> (4 * (i & 7))) & 0xFu;
+          vt[(16 * s + i) * VB + ti] = (uint8_t)(l4 | (h4 << 4));
         }
-        // element rows: 8-bit codes at byte ti; 4-bit codes of the pair share byte i
-        if (!four_bit(VK)) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) vt[(lane + 64 * kk) * VB + ti] = (uint8_t)code[kk];
-        } else if (half == 0) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) lo_code[kk] = code[kk];
-        } else {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) lo_code[kk] |= code[kk] << 4;
-        }
-      }
-      if (four_bit(VK) && i + 16 >= lo && i < hi) {  // (a pair with at least one token in the chunk)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) vt[(lane + 64 * kk) * VB + i] = (uint8_t)lo_code[kk];
       }
     }
   }
