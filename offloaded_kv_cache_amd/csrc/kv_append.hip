@@ -72,6 +72,42 @@ __device__ inline double mv_absmax(const double (&y)[16]) {
   return m;
 }
 
+// Codes from an fp32 quotient, each checked against the rounding threshold nearest to
+// it: y/d is formed as (float)y * rcp(d) (d is an fp16 value, exact in fp32; the estimate
+// is within 2^-19 of y/d for the |y/d| <= 8.01 of q4 and within 2^-15 for the
+// |x/d| <= 127.1 of int8). Where a lane of the wave has a quotient within 2^-16 (q4) or
+// 2^-12 (int8) of a threshold, the whole wave takes the exact decisions of kv_encode.h.
+__device__ inline void mv_q4_codes(const double (&y)[16], double d, int (&code)[16]) {
+  const float rd = d == 0.0 ? 0.0f : __builtin_amdgcn_rcpf((float)d);  // (d = 0: every code 8)
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = fmaf((float)y[i], rd, 0.5f);
+    const float r = __builtin_floorf(q), f = q - r;
+    near |= f < 0x1p-16f || f > 1.0f - 0x1p-16f;
+    code[i] = (int)__builtin_amdgcn_fmed3f(r + 8.0f, 0.0f, 15.0f);
+  }
+  if (__any(near)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = enc::q4_code_fast(y[i], d);
+  }
+}
+__device__ inline void mv_int8_codes(const double (&x)[16], double d, int (&code)[16]) {
+  const float rd = d == 0.0 ? 0.0f : __builtin_amdgcn_rcpf((float)d);  // (d = 0: every code 0)
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = fmaf((float)fabs(x[i]), rd, 0.5f);
+    const float r = __builtin_floorf(q), f = q - r;
+    near |= f < 0x1p-12f || f > 1.0f - 0x1p-12f;
+    const int c = (int)fminf(r, 127.0f);
+    code[i] = x[i] < 0.0 ? -c : c;
+  }
+  if (__any(near)) {
+    mv_int8_codes(x, d, code);
+  }
+}
+
 // Codes of the lane's 16 elements and the scale of its block (q4, fp4: the 32 elements
 // of lanes 2b, 2b + 1), group (int8: 64 elements, lanes 4g .. 4g + 3) or vector (fp8).
 template <int KIND>
@@ -131,8 +167,7 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
       const double best = (lane & 1) ? (ph ? pf : first) : (hit ? first : pf);
       scale = enc::f64_to_f16_fast(-best * 0.125);  // -m/8 exact
       const double d = f16_to_f64(scale);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) code[i] = enc::q4_code_fast(x[i], d);
+      mv_q4_codes(x, d, code);
     }
   }
   return scale;
