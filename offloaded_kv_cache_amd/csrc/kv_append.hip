@@ -42,10 +42,19 @@ constexpr int kAppendThreads = 64 * kAppendWaves;
 
 // Butterfly stage of element bit log2(M) + 4 (M = 1, 2, 4, 8: lanes s and s ^ M of a row).
 template <int M>
+__device__ inline double mv_xchg(double v, int lane) {
+  if (M != 4) return xchg64<M>(v, lane);
+  // lane ^ 4 by the crossbar's swizzle (bit mode: and 0x1F, xor 4)
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)b, 0x101F);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(b >> 32), 0x101F);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+template <int M>
 __device__ inline void mv_lane_stage(double (&y)[16], int lane) {
   const double sg = (lane & M) ? -1.0 : 1.0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] = __builtin_fma(sg, y[i], xchg64<M>(y[i], lane));
+  for (int i = 0; i < 16; ++i) y[i] = __builtin_fma(sg, y[i], mv_xchg<M>(y[i], lane));
 }
 // Exact H x / 16 of the lane's 16 elements.
 __device__ inline void mv_wht(double (&y)[16], int lane) {
@@ -154,17 +163,34 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
     } else {
       // the block's first element holding the largest |y| (the lower lane's elements come
       // first), then its signed value
-      double first = 0.0;
-      uint32_t hit = 0u;
+      double mx = x[0], mn = x[0];
 #pragma unroll
-      for (int i = 15; i >= 0; --i) {
-        const bool h = fabs(x[i]) == m;
-        first = h ? x[i] : first;
-        hit |= h ? 1u : 0u;
+      for (int i = 1; i < 16; ++i) {
+        mx = fmax(mx, x[i]);
+        mn = fmin(mn, x[i]);
       }
-      const double pf = xchg64<1>(first, lane);
-      const uint32_t ph = xchg32<1>(hit, lane);
-      const double best = (lane & 1) ? (ph ? pf : first) : (hit ? first : pf);
+      // pair of lanes: which signs reach m
+      const bool pos_l = mx == m, neg_l = -mn == m;
+      const uint32_t flags = (pos_l ? 1u : 0u) | (neg_l ? 2u : 0u);
+      const uint32_t pflags = xchg32<1>(flags, lane);
+      const uint32_t both = flags | pflags;
+      double best;
+      if (__any(both == 3u)) {
+        // both signs reach m somewhere in a block of the wave: the first element holding it
+        double first = 0.0;
+        uint32_t hit = 0u;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+          const bool h = fabs(x[i]) == m;
+          first = h ? x[i] : first;
+          hit |= h ? 1u : 0u;
+        }
+        const double pf = xchg64<1>(first, lane);
+        const uint32_t ph = xchg32<1>(hit, lane);
+        best = (lane & 1) ? (ph ? pf : first) : (hit ? first : pf);
+      } else {
+        best = (both & 1u) ? m : -m;
+      }
       scale = enc::f64_to_f16_fast(-best * 0.125);  // -m/8 exact
       const double d = f16_to_f64(scale);
       mv_q4_codes(x, d, code);
@@ -173,15 +199,11 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
   return scale;
 }
 
-// The 16 codes of a lane as nibbles of two dwords (code i at bits 4 (i & 7) of word i >> 3).
-__device__ inline void mv_nibbles(const int (&c)[16], uint32_t& n0, uint32_t& n1) {
-  n0 = 0u;
-  n1 = 0u;
+// The 16 codes of a lane as bytes: code 4 q + b in byte b of word q.
+__device__ inline void mv_bytes(const int (&c)[16], uint32_t (&w)[4]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    n0 |= (uint32_t)c[i] << (4 * i);
-    n1 |= (uint32_t)c[8 + i] << (4 * i);
-  }
+  for (int q = 0; q < 4; ++q)
+    w[q] = (uint32_t)c[4 * q] | ((uint32_t)c[4 * q + 1] << 8) | ((uint32_t)c[4 * q + 2] << 16) | ((uint32_t)c[4 * q + 3] << 24);
 }
 
 // Staging of one token's K record: code row (slice-permuted bytes) and scales.
@@ -207,20 +229,16 @@ __device__ inline void mv_stage_k(uint8_t* __restrict__ row, uint16_t* __restric
     }
   } else {
     // byte 32 sl + 4 j + w = code[32 j + 4 sl + w] | code[32 j + 16 + 4 sl + w] << 4: the
-    // even lane (elements r < 16 of the block) takes the odd lane's codes
-    uint32_t n0, n1;
-    mv_nibbles(code, n0, n1);
-    const uint32_t h0 = xchg32<1>(n0, lane), h1 = xchg32<1>(n1, lane);
+    // even lane (elements r < 16 of the block) takes the odd lane's codes; word sl of the
+    // byte-packed codes holds elements 4 sl .. 4 sl + 3 of each lane
+    uint32_t w[4];
+    mv_bytes(code, w);
+    uint32_t h[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = xchg32<1>(w[q], lane);
     if (!(s & 1)) {
 #pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const uint32_t lo = sl < 2 ? n0 >> (16 * sl) : n1 >> (16 * (sl - 2));
-        const uint32_t hi = sl < 2 ? h0 >> (16 * sl) : h1 >> (16 * (sl - 2));
-        uint32_t w = 0u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w |= (((lo >> (4 * q)) & 0xFu) | (((hi >> (4 * q)) & 0xFu) << 4)) << (8 * q);
-        *reinterpret_cast<uint32_t*>(row + 32 * sl + 4 * j) = w;
-      }
+      for (int sl = 0; sl < 4; ++sl) *reinterpret_cast<uint32_t*>(row + 32 * sl + 4 * j) = w[sl] | (h[sl] << 4);
       sc[j] = scale;
     }
   }
@@ -281,15 +299,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) vt[(16 * s + i) * VB + ti] = (uint8_t)code[i];
     } else {
-      uint32_t n0, n1;
-      mv_nibbles(code, n0, n1);
-      const uint32_t p0 = xchg32<32>(n0, lane), p1 = xchg32<32>(n1, lane);
+      uint32_t w[4], p[4];
+      mv_bytes(code, w);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[q] = xchg32<32>(w[q], lane);
       if (vi < 2) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const uint32_t l4 = ((i < 8 ? n0 : n1) >> (4 * (i & 7))) & 0xFu;
-          const uint32_t h4 = ((i < 8 ? p0 : p1) >> (4 * (i & 7))) & 0xFu;
-          vt[(16 * s + i) * VB + ti] = (uint8_t)(l4 | (h4 << 4));
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t b = w[q] | (p[q] << 4);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) vt[(16 * s + 4 * q + t) * VB + ti] = (uint8_t)(b >> (8 * t));
         }
       }
     }
