@@ -600,7 +600,8 @@ def counter_traffic(workload: str):
     The summary records the code hash (kernel_code_hash) of the kernel its counters
     were taken with; a kernel changed since then gives None."""
     name = {"c3": "decode_q4_0_128k_hbm_bytes.txt", "c3fp4": "decode_fp4_128k_hbm_bytes.txt",
-            "c3fp8": "decode_fp8_128k_hbm_bytes.txt"}.get(workload)
+            "c3fp8": "decode_fp8_128k_hbm_bytes.txt", "c2": "decode_int8_32k.txt",
+            "c4": "decode_k8v4_4seq.txt"}.get(workload)
     path = os.path.join(ROOT, "profiles", name) if name else None
     if path is None or not os.path.exists(path):
         return None
