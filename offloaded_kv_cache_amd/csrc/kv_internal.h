@@ -84,6 +84,7 @@ __host__ __device__ inline double f16_to_f64(uint16_t h) {
 __host__ __device__ inline int int8_code(double x, double d) {
   if (d == 0.0) return 0;
   const double q = x / d;
+  if (q != q) return 0;  // (NaN, e.g. inf / inf: code 0, so the conversion below is defined)
   const double a = q < 0 ? -q : q;
   double r = __builtin_floor(a);
   if (a - r >= 0.5) r += 1.0;
@@ -96,6 +97,7 @@ __host__ __device__ inline int int8_code(double x, double d) {
 __host__ __device__ inline int q4_code(double y, double d) {
   if (d == 0.0) return 8;
   const double q = y / d;
+  if (q != q) return 8;  // (NaN, e.g. inf / inf: code 8, so the conversion below is defined)
   double r = __builtin_floor(q);
   if (q - r >= 0.5) r += 1.0;
   double c = r + 8.0;
@@ -142,6 +144,7 @@ __host__ __device__ inline int fp4_code(double y, int e) {
 __host__ __device__ inline int fp8_code(double x, double d) {
   if (d == 0.0) return 0;
   const double v = (x < 0 ? -x : x) / d;
+  if (v != v) return 0;  // (NaN, e.g. inf / inf: code 0, never the NaN code)
   if (v >= 464.0) return x < 0 ? 0xFE : 0x7E;                // at and past the last midpoint
   const int ex = (int)((__builtin_bit_cast(uint64_t, v) >> 52) & 0x7FF) - 1023;  // floor(log2 v)
   const bool sub = v < 0x1p-6;
