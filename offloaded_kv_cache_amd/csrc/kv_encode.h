@@ -1,5 +1,6 @@
-// kv_encode.h - per-wave record encoder shared by the append kernel and the
-// decode kernel's fused single-token append (gfx950).
+// kv_encode.h - per-wave record encoder of the decode kernel's fused single-token
+// append (gfx950); the chunk append kernel (kv_append.hip) uses its scale rounding and
+// exact code decisions.
 //
 // Strata page ("KV 沉进内存、显存减半：Strata 让 12 GB 显卡跑满 262K 上下文"),
 // section "4-bit KV 缓存：先旋转，再压到 4-bit": K and V are rotated by the
@@ -20,56 +21,45 @@
 namespace kvc {
 namespace enc {
 
-// One butterfly stage (bit log2 M) and one max stage on the lane's four values.
-// Two forms of the encoder, with identical results. DPP = true (a lone vector, latency
-// bound): DPP selects and lane swaps, branch-free rounding, division-free codes.
-// DPP = false (many vectors at once, VALU-throughput bound): lane exchanges through the
-// LDS crossbar (no VALU instructions), and the plain rounding and code rules of
-// kv_internal.h (fewer instructions when most lanes take the same branch).
-template <int M, bool DPP>
-__device__ inline double xchg_enc(double v, int lane) {
-  if (DPP) return xchg64<M>(v, lane);
-  return __shfl_xor(v, M);
-}
-
+// One butterfly stage (bit log2 M) and one max stage on the lane's four values. Lane
+// exchanges are DPP selects and lane swaps (a lone vector is latency bound); the
+// rounding is branch-free and the codes are decided without division.
 // (partner + y in the lower lane of a pair, partner - y in the upper one, each as one fma
 // with a sign of +-1: the product is exact, and so is the sum, whose exact value is
 // representable, so the result is the exact butterfly)
-template <int M, bool DPP>
+template <int M>
 __device__ inline void wht_stage(double (&y)[4], int lane) {
   const double sg = (lane & M) ? -1.0 : 1.0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const double o = xchg_enc<M, DPP>(y[k], lane);
+    const double o = xchg64<M>(y[k], lane);
     y[k] = __builtin_fma(sg, y[k], o);
   }
 }
-template <int M, bool DPP>
+template <int M>
 __device__ inline void max_stage(double (&v)[4], int lane) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], xchg_enc<M, DPP>(v[k], lane));
+  for (int k = 0; k < 4; ++k) v[k] = fmax(v[k], xchg64<M>(v[k], lane));
 }
 
 // Maximum over the wave of each of the lane's four values.
-template <bool DPP>
 __device__ inline void wave_max4(double (&v)[4], int lane) {
-  max_stage<1, DPP>(v, lane);
-  max_stage<2, DPP>(v, lane);
-  max_stage<4, DPP>(v, lane);
-  max_stage<8, DPP>(v, lane);
-  max_stage<16, DPP>(v, lane);
-  max_stage<32, DPP>(v, lane);
+  max_stage<1>(v, lane);
+  max_stage<2>(v, lane);
+  max_stage<4>(v, lane);
+  max_stage<8>(v, lane);
+  max_stage<16>(v, lane);
+  max_stage<32>(v, lane);
 }
 
 // Exact y = H x on the lane's four elements.
-template <bool DPP>
 __device__ inline void wht256(double (&y)[4], int lane) {
-  wht_stage<1, DPP>(y, lane);
-  wht_stage<2, DPP>(y, lane);
-  wht_stage<4, DPP>(y, lane);
-  wht_stage<8, DPP>(y, lane);
-  wht_stage<16, DPP>(y, lane);
-  wht_stage<32, DPP>(y, lane);
+  wht_stage<1>(y, lane);
+  wht_stage<2>(y, lane);
+  wht_stage<4>(y, lane);
+  wht_stage<8>(y, lane);
+  wht_stage<16>(y, lane);
+  wht_stage<32>(y, lane);
   const double a0 = y[0] + y[1], a1 = y[0] - y[1];  // bit 6
   const double a2 = y[2] + y[3], a3 = y[2] - y[3];
   y[0] = (a0 + a2) * 0.0625;                          // bit 7, then 1/16
@@ -122,7 +112,7 @@ __device__ inline int q4_code_fast(double y, double d) {
 // fp8: every scale[k] is the vector's one scale.
 // q4, fp4: scale of block (lane >> 5) + 2k lives in register k of every lane of
 // that half-wave.
-template <int KIND, bool DPP = true>
+template <int KIND>
 __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code)[4],
                                    uint16_t (&scale)[4]) {
   double x[4];
@@ -132,21 +122,21 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
     double a[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
-    wave_max4<DPP>(a, lane);
+    wave_max4(a, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      scale[k] = DPP ? f64_to_f16_fast(a[k] / 127.0) : f64_to_f16_rne(a[k] / 127.0);
+      scale[k] = f64_to_f16_fast(a[k] / 127.0);
       const double d = f16_to_f64(scale[k]);
-      code[k] = DPP ? int8_code_fast(x[k], d) : int8_code(x[k], d);
+      code[k] = int8_code_fast(x[k], d);
     }
   } else if (KIND == kFp8) {
     // one scale for the vector: the largest |x| over the wave's four registers
     double a[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) a[k] = fabs(x[k]);
-    wave_max4<DPP>(a, lane);
+    wave_max4(a, lane);
     const double amax = fmax(fmax(a[0], a[1]), fmax(a[2], a[3]));
-    const uint16_t s = DPP ? f64_to_f16_fast(amax / 448.0) : f64_to_f16_rne(amax / 448.0);
+    const uint16_t s = f64_to_f16_fast(amax / 448.0);
     const double d = f16_to_f64(s);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -154,17 +144,17 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
       code[k] = fp8_code(x[k], d);
     }
   } else if (KIND == kFp4) {
-    wht256<DPP>(x, lane);
+    wht256(x, lane);
     // per block (the 32 lanes of a half-wave, register k): largest |y|, its exponent,
     // the power-of-two scale and the grid index of each element (exact comparisons)
     double m[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
-    max_stage<1, DPP>(m, lane);
-    max_stage<2, DPP>(m, lane);
-    max_stage<4, DPP>(m, lane);
-    max_stage<8, DPP>(m, lane);
-    max_stage<16, DPP>(m, lane);
+    max_stage<1>(m, lane);
+    max_stage<2>(m, lane);
+    max_stage<4>(m, lane);
+    max_stage<8>(m, lane);
+    max_stage<16>(m, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = fp4_block_exp(m[k]);
@@ -172,17 +162,17 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
       code[k] = m[k] == 0.0 ? 0 : fp4_code(x[k], e);
     }
   } else {
-    wht256<DPP>(x, lane);
+    wht256(x, lane);
     // per block (the 32 lanes of a half-wave, register k): largest |y|, then the
     // first element holding it, then its signed value
     double m[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) m[k] = fabs(x[k]);
-    max_stage<1, DPP>(m, lane);
-    max_stage<2, DPP>(m, lane);
-    max_stage<4, DPP>(m, lane);
-    max_stage<8, DPP>(m, lane);
-    max_stage<16, DPP>(m, lane);
+    max_stage<1>(m, lane);
+    max_stage<2>(m, lane);
+    max_stage<4>(m, lane);
+    max_stage<8>(m, lane);
+    max_stage<16>(m, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint64_t hit = __ballot(fabs(x[k]) == m[k]);
@@ -196,9 +186,9 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
                      h1 = __builtin_amdgcn_readlane((uint32_t)(xb >> 32), i_hi);
       const uint32_t sel = (lane & 32) ? ~0u : 0u;
       const double best = __builtin_bit_cast(double, ((uint64_t)(h0 ^ ((h0 ^ h1) & sel)) << 32) | (l0 ^ ((l0 ^ l1) & sel)));
-      scale[k] = DPP ? f64_to_f16_fast(-best * 0.125) : f64_to_f16_rne(-best * 0.125);  // -m/8 exact
+      scale[k] = f64_to_f16_fast(-best * 0.125);  // -m/8 exact
       const double d = f16_to_f64(scale[k]);
-      code[k] = DPP ? q4_code_fast(x[k], d) : q4_code(x[k], d);
+      code[k] = q4_code_fast(x[k], d);
     }
   }
 }
@@ -207,14 +197,6 @@ __device__ inline void encode_vals(const uint16_t (&in)[4], int lane, int (&code
 __device__ inline void load_vals(const uint16_t* __restrict__ src, int lane, uint16_t (&in)[4]) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) in[k] = src[lane + 64 * k];
-}
-
-template <int KIND, bool DPP>
-__device__ inline void encode(const uint16_t* __restrict__ src, int lane, int (&code)[4],
-                              uint16_t (&scale)[4]) {
-  uint16_t in[4];
-  load_vals(src, lane, in);
-  encode_vals<KIND, DPP>(in, lane, code, scale);
 }
 
 // K plane row of a token (token-major, slice-permuted code bytes): its code bytes at
