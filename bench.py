@@ -148,6 +148,55 @@ def build_resident(args, wl, dev, per_step=1):
     return s, pools, tables, start_lens, max_pages, append_ev
 
 
+def read_ceiling(args, wl, dev, s, pools, tables, lens_now, max_ctx, pps, per_tok):
+    """The roofline reference of the split kernel: a plain read of exactly the bytes one
+    decode launch streams (every work item's KV-head part of its pages, through the same
+    block tables, split sizes and work-item order; lib/libkvmeasure.so), timed like the
+    split kernel with events recorded at the kernel's own start and end, over the same
+    layers in the same rotation (so its reads come from HBM as the split kernel's do).
+    Returns None when the measurement library is not built."""
+    import ctypes as C
+
+    import torch
+
+    path = os.path.join(ROOT, "offloaded_kv_cache_amd", "lib", "libkvmeasure.so")
+    if not os.path.exists(path):
+        log("read ceiling: lib/libkvmeasure.so not built, skipped")
+        return None
+    lib = C.CDLL(path)
+    fn = lib.kv_measure_read_pages
+    fn.restype = C.c_int
+    fn.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int,
+                   C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+    L, B = wl["layers"], len(lens_now)
+    n_kv = 4
+    head_bytes = per_tok * PAGE // n_kv
+    n_splits = -(-(-(-max_ctx // PAGE)) // pps)
+    ctx = torch.tensor(lens_now, dtype=torch.int32, device=dev)
+    out = torch.empty(n_splits * B * n_kv * 256, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    evs = []
+    for rep in range(args.warmup + args.steps):
+        for layer in range(L):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            b.record(stream)  # (creates the events; the launch records them again)
+            bt = tables[layer]
+            r = fn(pools[layer].data.data_ptr(), pools[layer].n_pages, head_bytes, n_kv, bt.data_ptr(), bt.shape[1],
+                   ctx.data_ptr(), B, pps, n_splits, out.data_ptr(), C.c_void_p(stream.cuda_stream),
+                   C.c_void_p(a.cuda_event), C.c_void_p(b.cuda_event))
+            if r != 0:
+                raise RuntimeError("kv_measure_read_pages rejected its arguments")
+            if rep >= args.warmup:
+                evs.append((a, b))
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e3
+    nbytes = sum(lens_now) * per_tok
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"kernel": "plain read of the launch's pages", "avg_launch_us": round(us, 3),
+            "achieved": round(achieved, 2), "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
 def run_resident(args, wl, dev):
     import torch
 
@@ -222,7 +271,12 @@ def run_resident(args, wl, dev):
     split_ms = [a.elapsed_time(b) for a, b, _ in timed_split]
     split_bytes = [x for _, _, x in timed_split]
     achieved = sum(split_bytes) / (sum(split_ms) * 1e-3) / 1e9
+    # the split size the launches used (the library's own when none was given)
+    pps = args.pages_per_split or K.decode_split_pages(s, B, max_ctx, sum(lens) if B > 1 else 0)
+    ceiling = None if args.no_read_ceiling else read_ceiling(
+        args, wl, dev, s, pools, tables, [start_lens[b] + n_steps for b in range(B)], max_ctx, pps, per_tok)
     res = dict(
+        read_ceiling=ceiling,
         value=kv_bytes / wall / 1e9,
         ms_per_step=wall / args.steps * 1e3,
         split_us=sum(split_ms) / len(split_ms) * 1e3,
@@ -709,6 +763,8 @@ def main():
                     help="N > 1: speculative verification of N new tokens per step and layer (append "
                          "of the N-token chunk, then kv_decode_attention_mq) instead of one decode token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the plain read of the launch's pages (the split kernel's reference)")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--kernel-hash", action="store_true",
@@ -809,6 +865,11 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(res["achieved"] / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic(args.workload), "avg_launch_us": round(res["split_us"], 3),
                      "bytes_per_launch": int(res["split_bytes"])},
+        # a plain read of the same launch's pages on the same GPU, and the split kernel's rate
+        # as a fraction of it
+        "read_ceiling": res.get("read_ceiling"),
+        "frac_of_read_ceiling": (round(res["achieved"] / res["read_ceiling"]["achieved"], 4)
+                                 if res.get("read_ceiling") else None),
         "append_2048_chunk_us": round(res["append_chunk_us"], 3) if res["append_chunk_us"] else None,
         "cpu_baseline": cpu,
     }

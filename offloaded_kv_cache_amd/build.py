@@ -2,6 +2,8 @@
 
 Every source under ``csrc/`` is compiled by hipcc for the MI355X (gfx950)
 only, then linked into one shared library with a C ABI (``include/kvcache.h``).
+The measurement helper under ``measure/`` (a plain read of a decode launch's
+pages, the benchmark's roofline reference) becomes ``lib/libkvmeasure.so``.
 Packed-fp32 VALU instructions are disabled: the kernels rely on ordinary fp32,
 packed fp16 and MFMA arithmetic.
 """
@@ -18,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(LIB_DIR, "libkvcache.so")
+MEASURE_DIR = os.path.join(HERE, "measure")
+MEASURE_LIB_PATH = os.path.join(LIB_DIR, "libkvmeasure.so")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,8 +32,8 @@ CFLAGS = [
 ]
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _run(cmd):
@@ -42,20 +46,23 @@ def _run(cmd):
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
-    objs = []
-    cmds = []
-    for src in sources():
-        obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-        objs.append(obj)
-        cmds.append([HIPCC, *CFLAGS, "-c", src, "-o", obj])
+    libs = [(LIB_PATH, sources(CSRC)), (MEASURE_LIB_PATH, sources(MEASURE_DIR))]
+    cmds, objs = [], {}
+    for lib, srcs in libs:
+        objs[lib] = []
+        for src in srcs:
+            obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
+            objs[lib].append(obj)
+            cmds.append([HIPCC, *CFLAGS, "-c", src, "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for cmd, r in zip(cmds, ex.map(_run, cmds)):
             if verbose:
                 print(" ".join(cmd))
                 sys.stdout.write(r.stderr)
-    tmp = LIB_PATH + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    for lib, _ in libs:
+        tmp = lib + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs[lib]])
+        os.replace(tmp, lib)
     return LIB_PATH
 
 

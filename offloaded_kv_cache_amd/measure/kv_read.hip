@@ -1,0 +1,84 @@
+// kv_read.hip - measurement helper (not part of the decode library's ABI): a plain read
+// of exactly the bytes a decode launch streams, as the roofline reference for the split
+// kernel. It reads, for every work item (split, sequence, KV head) of the decode launch's
+// split-major grid, the KV-head part of each of the item's pages through the same block
+// table, with 16-byte loads, and folds the words into one checksum per thread so that no
+// load can be dropped. No arithmetic beyond the xor, no LDS, no barriers: its duration is
+// what the memory system needs for the launch's pages in the launch's order and grouping.
+// Built into lib/libkvmeasure.so; only the benchmark loads it.
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+constexpr int kThreads = 256;
+constexpr int kMaxPerThread = 36;  // 16-byte words per thread and page: ceil(135,168 / 16 / 256) = 33
+
+__device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const uint8_t* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, 0x00020000);
+}
+
+// One workgroup per work item; an item's pages are read one after the other, each page's
+// loads issued together (words past the head part read an empty range: zeros, no memory).
+template <int PER>
+__global__ __launch_bounds__(kThreads) void read_pages(const uint8_t* __restrict__ pool, int64_t n_pool_pages,
+                                                       int64_t page_bytes, int head_bytes, int n_kv_heads,
+                                                       const int32_t* __restrict__ block_tables, int max_pages,
+                                                       const int32_t* __restrict__ context_lens, int batch,
+                                                       int pages_per_split, uint32_t* __restrict__ out) {
+  const int item = blockIdx.x, n_pairs = batch * n_kv_heads;
+  const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
+  const int T = max(context_lens[b], 0);
+  const int n_pages = (T + 255) / 256;
+  const int p_begin = split * pages_per_split, p_end = min(n_pages, p_begin + pages_per_split);
+  u4 acc = {0u, 0u, 0u, 0u};
+  for (int pg = p_begin; pg < p_end; ++pg) {
+    const int32_t phys = block_tables[(size_t)b * max_pages + pg];
+    if (phys < 0 || phys >= n_pool_pages) continue;
+    const auto r = head_rsrc(pool + phys * page_bytes + (int64_t)g * head_bytes, head_bytes);
+    u4 w[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      w[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + threadIdx.x) * 16, 0, 0));
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc ^= w[j];
+  }
+  out[(size_t)item * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+}  // namespace
+
+// Reads the pages of a decode launch (see above). head_bytes: one KV head's K and V planes
+// of a page (at most 147,456 B and a multiple of 16); page_bytes = n_kv_heads * head_bytes;
+// pages_per_split and n_splits: the decode launch's split size and count; out: device
+// buffer of n_splits * batch * n_kv_heads * 256 words. The launch records start and stop
+// (may be null) at the kernel's own start and end on `stream`. Returns 0, or -1 for
+// arguments outside these limits (nothing is launched then).
+extern "C" int kv_measure_read_pages(const uint8_t* pool, int64_t n_pool_pages, int head_bytes, int n_kv_heads,
+                                     const int32_t* block_tables, int max_pages, const int32_t* context_lens,
+                                     int batch, int pages_per_split, int n_splits, uint32_t* out,
+                                     hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (!pool || !block_tables || !context_lens || !out || head_bytes <= 0 || head_bytes % 16 ||
+      head_bytes > kMaxPerThread * kThreads * 16 || n_kv_heads <= 0 || batch <= 0 || max_pages <= 0 ||
+      pages_per_split <= 0 || n_splits <= 0 || n_pool_pages <= 0)
+    return -1;
+  const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
+  const int per = (head_bytes / 16 + kThreads - 1) / kThreads;
+  const dim3 grid((unsigned)(n_splits * batch * n_kv_heads));
+#define KV_READ_CASE(P)                                                                                   \
+  case P:                                                                                                 \
+    hipExtLaunchKernelGGL(read_pages<P>, grid, dim3(kThreads), 0, stream, start, stop, 0, pool, n_pool_pages, \
+                          page_bytes, head_bytes, n_kv_heads, block_tables, max_pages, context_lens, batch,  \
+                          pages_per_split, out);                                                          \
+    break;
+  switch (per <= 18 ? 18 : (per <= 26 ? 26 : (per <= 33 ? 33 : 36))) {
+    KV_READ_CASE(18)
+    KV_READ_CASE(26)
+    KV_READ_CASE(33)
+    KV_READ_CASE(36)
+  }
+#undef KV_READ_CASE
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
