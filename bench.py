@@ -670,15 +670,15 @@ def counter_traffic(workload: str):
 
 def _short_kernel(name: str) -> str:
     import re
-    m = re.search(r"(decode_split<[^>]*>|append_kernel<[^>]*>|decode_combine|gather\w*|select\w*|key_sums\w*|copyBuffer)",
-                  name)
+    m = re.search(r"(decode_split<[^>]*>|append_kernel<[^>]*>|decode_combine|read_pages<[^>]*>|gather\w*|select\w*|"
+                  r"key_sums\w*|copyBuffer)", name)
     return m.group(1) if m else name[:60]
 
 
 def summarize_trace(root: str, last: int):
     """Kernel durations from a rocprofv3 --kernel-trace -f csv directory: every dispatch of each
-    kernel of this library, then the last `last` dispatches of each decode kernel (the timed
-    steps)."""
+    kernel of this library, then the last `last` dispatches of each decode kernel and of the
+    plain page read (the timed steps)."""
     import csv
     import glob
     import statistics as st
@@ -693,7 +693,7 @@ def summarize_trace(root: str, last: int):
         lines.append(f"  {k:40s} {len(d):6d} {st.mean(d):9.2f} {min(d):9.2f} {max(d):9.2f}")
     lines.append(f"last {last} dispatches of each decode kernel:")
     for k, v in sorted(by.items()):
-        if "decode" in k:
+        if "decode" in k or "read_pages" in k:
             d = [(b - a) / 1000 for a, b in sorted(v)[-last:]]
             lines.append(f"  {k:40s} n={len(d)} mean {st.mean(d):9.2f} us  median {st.median(d):9.2f}  "
                          f"min {min(d):8.2f}  max {max(d):8.2f}")
