@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void read_pages(const uint8_t* __restrict
   const int item = blockIdx.x, n_pairs = batch * n_kv_heads;
   const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
   const int T = max(context_lens[b], 0);
-  const int n_pages = (T + 255) / 256;
+  const int n_pages = min((T + 255) / 256, max_pages);  // (the table's row holds max_pages entries)
   const int p_begin = split * pages_per_split, p_end = min(n_pages, p_begin + pages_per_split);
   u4 acc = {0u, 0u, 0u, 0u};
   for (int pg = p_begin; pg < p_end; ++pg) {
