@@ -56,7 +56,8 @@ __device__ inline void mv_lane_stage(double (&y)[16], int lane) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) y[i] = __builtin_fma(sg, y[i], mv_xchg<M>(y[i], lane));
 }
-// Exact H x / 16 of the lane's 16 elements.
+// Exact H x / 16 of the lane's 16 elements (SCALED = false: H x, 16 times larger).
+template <bool SCALED = true>
 __device__ inline void mv_wht(double (&y)[16], int lane) {
 #pragma unroll
   for (int h = 1; h < 16; h <<= 1)
@@ -71,8 +72,10 @@ __device__ inline void mv_wht(double (&y)[16], int lane) {
   mv_lane_stage<2>(y, lane);
   mv_lane_stage<4>(y, lane);
   mv_lane_stage<8>(y, lane);
+  if (SCALED) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) y[i] *= 0.0625;
+    for (int i = 0; i < 16; ++i) y[i] *= 0.0625;
+  }
 }
 __device__ inline double mv_absmax(const double (&y)[16]) {
   double m = fabs(y[0]);
@@ -84,21 +87,26 @@ __device__ inline double mv_absmax(const double (&y)[16]) {
 // Codes from an fp32 quotient, each checked against the rounding threshold nearest to
 // it: y/d is formed as (float)y * rcp(d) (d is an fp16 value, exact in fp32; the estimate
 // is within 2^-19 of y/d for the |y/d| <= 8.01 of q4 and within 2^-15 for the
-// |x/d| <= 127.1 of int8). Where a lane of the wave has a quotient within 2^-16 (q4) or
-// 2^-12 (int8) of a threshold, the whole wave takes the exact decisions of kv_encode.h.
-__device__ inline void mv_q4_codes(const double (&y)[16], double d, int (&code)[16]) {
-  const float rd = d == 0.0 ? 0.0f : __builtin_amdgcn_rcpf((float)d);  // (d = 0: every code 8)
+// |x/d| <= 127.1 of int8). The code's offset and the rounding half are added in the same
+// fma together with half the window (2^-16 for q4, 2^-12 for int8), so that a quotient
+// within the window of a threshold is one whose shifted value lies less than a whole
+// window above an integer: that is its fraction, and the integer part is the code. The
+// fma's own rounding (at most 2^-20 for q4, 2^-18 for int8) and the estimate's error
+// stay inside the window. Where a lane of the wave has such a quotient, the whole wave
+// takes the exact decisions of kv_encode.h.
+// q4: y16 = 16 y (the rotation without its 1/16): the quotient uses rcp(d) / 16 (exact).
+__device__ inline void mv_q4_codes(const double (&y16)[16], double d, int (&code)[16]) {
+  const float rd = d == 0.0 ? 0.0f : __builtin_amdgcn_rcpf((float)d) * 0.0625f;  // (d = 0: every code 8)
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float q = fmaf((float)y[i], rd, 0.5f);
-    const float r = __builtin_floorf(q), f = q - r;
-    near |= f < 0x1p-16f || f > 1.0f - 0x1p-16f;
-    code[i] = (int)__builtin_amdgcn_fmed3f(r + 8.0f, 0.0f, 15.0f);
+    const float q = fmaf((float)y16[i], rd, 8.5f + 0x1p-16f);  // y/d + 1/2 + 8, shifted by half the window
+    near |= __builtin_amdgcn_fractf(q) < 0x1p-15f;
+    code[i] = (int)__builtin_amdgcn_fmed3f(__builtin_floorf(q), 0.0f, 15.0f);
   }
   if (__any(near)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) code[i] = enc::q4_code_fast(y[i], d);
+    for (int i = 0; i < 16; ++i) code[i] = enc::q4_code_fast(y16[i] * 0.0625, d);
   }
 }
 __device__ inline void mv_int8_codes(const double (&x)[16], double d, int (&code)[16]) {
@@ -106,14 +114,14 @@ __device__ inline void mv_int8_codes(const double (&x)[16], double d, int (&code
   bool near = false;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float q = fmaf((float)fabs(x[i]), rd, 0.5f);
-    const float r = __builtin_floorf(q), f = q - r;
-    near |= f < 0x1p-12f || f > 1.0f - 0x1p-12f;
-    const int c = (int)fminf(r, 127.0f);
+    const float q = fmaf((float)fabs(x[i]), rd, 0.5f + 0x1p-12f);  // |x|/d + 1/2, shifted
+    near |= __builtin_amdgcn_fractf(q) < 0x1p-11f;
+    const int c = (int)fminf(__builtin_floorf(q), 127.0f);
     code[i] = x[i] < 0.0 ? -c : c;
   }
   if (__any(near)) {
-    mv_int8_codes(x, d, code);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) code[i] = enc::int8_code_fast(x[i], d);
   }
 }
 
@@ -138,9 +146,7 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
     a = fmax(a, xchg64<1>(a, lane));
     a = fmax(a, xchg64<2>(a, lane));
     scale = enc::f64_to_f16_fast(a / 127.0);
-    const double d = f16_to_f64(scale);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) code[i] = enc::int8_code_fast(x[i], d);
+    mv_int8_codes(x, f16_to_f64(scale), code);
   } else if (KIND == kFp8) {
     double a = mv_absmax(x);
     a = fmax(a, xchg64<1>(a, lane));
@@ -152,23 +158,27 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
 #pragma unroll
     for (int i = 0; i < 16; ++i) code[i] = fp8_code(x[i], d);
   } else {
-    mv_wht(x, lane);
-    double m = mv_absmax(x);
-    m = fmax(m, xchg64<1>(m, lane));
     if (KIND == kFp4) {
+      mv_wht(x, lane);
+      double m = mv_absmax(x);
+      m = fmax(m, xchg64<1>(m, lane));
       const int e = fp4_block_exp(m);
       scale = m == 0.0 ? (uint16_t)0 : fp16_pow2_bits(e);
 #pragma unroll
       for (int i = 0; i < 16; ++i) code[i] = m == 0.0 ? 0 : fp4_code(x[i], e);
     } else {
-      // the block's first element holding the largest |y| (the lower lane's elements come
-      // first), then its signed value
+      // x = 16 y (the rotation without its 1/16, which the scale and the quotient take);
+      // the block's largest |y| from its largest and smallest values, then the signed value
+      // of the first element holding it (the lower lane's elements come first)
+      mv_wht<false>(x, lane);
       double mx = x[0], mn = x[0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) {
         mx = fmax(mx, x[i]);
         mn = fmin(mn, x[i]);
       }
+      double m = fmax(mx, -mn);
+      m = fmax(m, xchg64<1>(m, lane));
       // pair of lanes: which signs reach m
       const bool pos_l = mx == m, neg_l = -mn == m;
       const uint32_t flags = (pos_l ? 1u : 0u) | (neg_l ? 2u : 0u);
@@ -191,9 +201,8 @@ __device__ inline uint16_t mv_encode(const uint16_t* __restrict__ src, int lane,
       } else {
         best = (both & 1u) ? m : -m;
       }
-      scale = enc::f64_to_f16_fast(-best * 0.125);  // -m/8 exact
-      const double d = f16_to_f64(scale);
-      mv_q4_codes(x, d, code);
+      scale = enc::f64_to_f16_fast(-best * (0.125 * 0.0625));  // -m/8 of y, exact
+      mv_q4_codes(x, f16_to_f64(scale), code);
     }
   }
   return scale;
