@@ -283,6 +283,7 @@ def run_resident(args, wl, dev):
         split_bytes=sum(split_bytes) / len(split_bytes),
         achieved=achieved,
         append_chunk_us=(sum(app_ms) / len(app_ms) * 1e3) if app_ms else None,
+        append_chunk_median_us=(sorted(app_ms)[len(app_ms) // 2] * 1e3) if app_ms else None,
         n_append_chunks=len(app_ms),
         pages_per_split=args.pages_per_split,
     )
@@ -870,7 +871,11 @@ def main():
         "read_ceiling": res.get("read_ceiling"),
         "frac_of_read_ceiling": (round(res["achieved"] / res["read_ceiling"]["achieved"], 4)
                                  if res.get("read_ceiling") else None),
+        # the chunk append kernel over the prefill's chunks: mean (what a kernel trace's average
+        # gives, first chunks of every layer included) and median
         "append_2048_chunk_us": round(res["append_chunk_us"], 3) if res["append_chunk_us"] else None,
+        "append_2048_chunk_median_us": (round(res["append_chunk_median_us"], 3)
+                                        if res.get("append_chunk_median_us") else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
