@@ -85,9 +85,6 @@ constexpr uint32_t kQ4FastMinM1 = 0x13FF;  // fp16 2^-10 minus one: |d| from her
 constexpr uint32_t kI8FastBits = 0x5300;  // fp16 56: |d| below this, -1152 * d_part is exact and finite
 constexpr int kQsStride = kHeadDim + 4;  // padded rows of the query in LDS (bank spread)
 
-__device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
-__device__ inline uint32_t as_u32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
-
 __device__ inline f4 mfma(h8 a, h8 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
