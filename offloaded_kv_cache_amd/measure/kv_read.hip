@@ -3,8 +3,11 @@
 // kernel. It reads, for every work item (split, sequence, KV head) of the decode launch's
 // split-major grid, the KV-head part of each of the item's pages through the same block
 // table, with 16-byte loads, and folds the words into one checksum per thread so that no
-// load can be dropped. No arithmetic beyond the xor, no LDS, no barriers: its duration is
-// what the memory system needs for the launch's pages in the launch's order and grouping.
+// load can be dropped. No arithmetic beyond the xor, no LDS beyond one word, no other
+// barriers: its duration is what the memory system needs for the launch's pages in the
+// launch's order and grouping. Like the split kernel, it runs one workgroup per item when
+// the items fit one round of resident workgroups, and otherwise one round that takes the
+// remaining items from a counter.
 // Built into lib/libkvmeasure.so; only the benchmark loads it.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
@@ -27,51 +30,76 @@ __global__ __launch_bounds__(kThreads) void read_pages(const uint8_t* __restrict
                                                        int64_t page_bytes, int head_bytes, int n_kv_heads,
                                                        const int32_t* __restrict__ block_tables, int max_pages,
                                                        const int32_t* __restrict__ context_lens, int batch,
-                                                       int pages_per_split, uint32_t* __restrict__ out) {
-  const int item = blockIdx.x, n_pairs = batch * n_kv_heads;
-  const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
-  const int T = max(context_lens[b], 0);
-  const int n_pages = min((T + 255) / 256, max_pages);  // (the table's row holds max_pages entries)
-  const int p_begin = split * pages_per_split, p_end = min(n_pages, p_begin + pages_per_split);
-  u4 acc = {0u, 0u, 0u, 0u};
-  for (int pg = p_begin; pg < p_end; ++pg) {
-    const int32_t phys = block_tables[(size_t)b * max_pages + pg];
-    if (phys < 0 || phys >= n_pool_pages) continue;
-    const auto r = head_rsrc(pool + phys * page_bytes + (int64_t)g * head_bytes, head_bytes);
-    u4 w[PER];
+                                                       int pages_per_split, int n_items, uint32_t* __restrict__ counter,
+                                                       uint32_t* __restrict__ out) {
+  __shared__ int next_s;
+  const int n_pairs = batch * n_kv_heads;
+  for (int item = blockIdx.x; item < n_items;) {
+    const int split = item / n_pairs, b = (item - split * n_pairs) / n_kv_heads, g = item % n_kv_heads;
+    const int T = max(context_lens[b], 0);
+    const int n_pages = min((T + 255) / 256, max_pages);  // (the table's row holds max_pages entries)
+    const int p_begin = split * pages_per_split, p_end = min(n_pages, p_begin + pages_per_split);
+    u4 acc = {0u, 0u, 0u, 0u};
+    for (int pg = p_begin; pg < p_end; ++pg) {
+      const int32_t phys = block_tables[(size_t)b * max_pages + pg];
+      if (phys < 0 || phys >= n_pool_pages) continue;
+      const auto r = head_rsrc(pool + phys * page_bytes + (int64_t)g * head_bytes, head_bytes);
+      u4 w[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      w[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + threadIdx.x) * 16, 0, 0));
+      for (int j = 0; j < PER; ++j)
+        w[j] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, (j * kThreads + threadIdx.x) * 16, 0, 0));
 #pragma unroll
-    for (int j = 0; j < PER; ++j) acc ^= w[j];
+      for (int j = 0; j < PER; ++j) acc ^= w[j];
+    }
+    out[(size_t)item * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if (!counter) break;  // one workgroup per item
+    // the next item past the first round, from the counter (every thread reads it after the barrier)
+    if (threadIdx.x == 0) next_s = (int)gridDim.x + (int)atomicAdd(&counter[0], 1u);
+    __syncthreads();
+    item = next_s;
+    __syncthreads();
   }
-  out[(size_t)item * kThreads + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  // the last workgroup to finish leaves the counters at zero for the next launch
+  if (counter && threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(&counter[1], 1u) == gridDim.x - 1) {
+      atomicExch(&counter[0], 0u);
+      atomicExch(&counter[1], 0u);
+    }
+  }
 }
 
 }  // namespace
 
 // Reads the pages of a decode launch (see above). head_bytes: one KV head's K and V planes
 // of a page (at most 147,456 B and a multiple of 16); page_bytes = n_kv_heads * head_bytes;
-// pages_per_split and n_splits: the decode launch's split size and count; out: device
-// buffer of n_splits * batch * n_kv_heads * 256 words. The launch records start and stop
-// (may be null) at the kernel's own start and end on `stream`. Returns 0, or -1 for
-// arguments outside these limits (nothing is launched then).
+// pages_per_split and n_splits: the decode launch's split size and count; n_resident: the
+// decode launch's round of resident workgroups (more items than that are taken from
+// `counter`, two device words that are zero before the first such launch and are left at
+// zero by each; 0 or a null counter: one workgroup per item); out: device buffer of
+// n_splits * batch * n_kv_heads * 256 words. The launch records start and stop (may be
+// null) at the kernel's own start and end on `stream`. Returns 0, or -1 for arguments
+// outside these limits (nothing is launched then).
 extern "C" int kv_measure_read_pages(const uint8_t* pool, int64_t n_pool_pages, int head_bytes, int n_kv_heads,
                                      const int32_t* block_tables, int max_pages, const int32_t* context_lens,
-                                     int batch, int pages_per_split, int n_splits, uint32_t* out,
-                                     hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                                     int batch, int pages_per_split, int n_splits, int n_resident,
+                                     uint32_t* counter, uint32_t* out, hipStream_t stream, hipEvent_t start,
+                                     hipEvent_t stop) {
   if (!pool || !block_tables || !context_lens || !out || head_bytes <= 0 || head_bytes % 16 ||
       head_bytes > kMaxPerThread * kThreads * 16 || n_kv_heads <= 0 || batch <= 0 || max_pages <= 0 ||
-      pages_per_split <= 0 || n_splits <= 0 || n_pool_pages <= 0)
+      pages_per_split <= 0 || n_splits <= 0 || n_pool_pages <= 0 || n_resident < 0)
     return -1;
   const int64_t page_bytes = (int64_t)n_kv_heads * head_bytes;
   const int per = (head_bytes / 16 + kThreads - 1) / kThreads;
-  const dim3 grid((unsigned)(n_splits * batch * n_kv_heads));
+  const int n_items = n_splits * batch * n_kv_heads;
+  const bool counted = counter && n_resident > 0 && n_items > n_resident;
+  if (!counted) counter = nullptr;
+  const dim3 grid((unsigned)(counted ? n_resident : n_items));
 #define KV_READ_CASE(P)                                                                                   \
   case P:                                                                                                 \
     hipExtLaunchKernelGGL(read_pages<P>, grid, dim3(kThreads), 0, stream, start, stop, 0, pool, n_pool_pages, \
                           page_bytes, head_bytes, n_kv_heads, block_tables, max_pages, context_lens, batch,  \
-                          pages_per_split, out);                                                          \
+                          pages_per_split, n_items, counter, out);                                        \
     break;
   switch (per <= 18 ? 18 : (per <= 26 ? 26 : (per <= 33 ? 33 : 36))) {
     KV_READ_CASE(18)

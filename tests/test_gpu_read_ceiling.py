@@ -28,7 +28,7 @@ def _fn():
     fn = C.CDLL(LIB).kv_measure_read_pages
     fn.restype = C.c_int
     fn.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int,
-                   C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+                   C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     return fn
 
 
@@ -55,7 +55,8 @@ def expected(pool, head_bytes, n_kv, bt, lens, pps, n_splits):
 
 
 @pytest.mark.parametrize("fmt", ["q4_0", "int8", "k8v4", "fp8"])
-def test_read_pages_reads_exactly_the_launch_bytes(gpu, fmt):
+@pytest.mark.parametrize("n_resident", [0, 7])
+def test_read_pages_reads_exactly_the_launch_bytes(gpu, fmt, n_resident):
     if not os.path.exists(LIB):
         pytest.fail("lib/libkvmeasure.so is not built (offloaded_kv_cache_amd/build.py builds it)")
     s = K.shape(fmt)
@@ -75,12 +76,17 @@ def test_read_pages_reads_exactly_the_launch_bytes(gpu, fmt):
     dev_pool = torch.from_numpy(pool).to(gpu)
     dev_bt = torch.from_numpy(bt).to(gpu)
     dev_lens = torch.from_numpy(lens).to(gpu)
-    out = torch.full((n_splits * 4 * n_kv * 256,), -1, dtype=torch.int32, device=gpu)
     stream = torch.cuda.current_stream()
-    r = _fn()(dev_pool.data_ptr(), n_pool, head_bytes, n_kv, dev_bt.data_ptr(), max_pages, dev_lens.data_ptr(),
-              4, pps, n_splits, out.data_ptr(), C.c_void_p(stream.cuda_stream), None, None)
-    assert r == 0
-    torch.cuda.synchronize()
-    got = out.cpu().numpy().view(np.uint32).reshape(-1, 256)
+    counter = torch.zeros(2, dtype=torch.int32, device=gpu)
     want = expected(pool, head_bytes, n_kv, bt, lens, pps, n_splits)
-    assert np.array_equal(got, want)
+    # n_resident 7: 64 items through 7 workgroups and the counter, twice on one counter
+    for _ in range(2):
+        out = torch.full((n_splits * 4 * n_kv * 256,), -1, dtype=torch.int32, device=gpu)
+        r = _fn()(dev_pool.data_ptr(), n_pool, head_bytes, n_kv, dev_bt.data_ptr(), max_pages, dev_lens.data_ptr(),
+                  4, pps, n_splits, n_resident, counter.data_ptr(), out.data_ptr(), C.c_void_p(stream.cuda_stream),
+                  None, None)
+        assert r == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint32).reshape(-1, 256)
+        assert np.array_equal(got, want)
+        assert counter.cpu().tolist() == [0, 0]  # left at zero for the next launch
