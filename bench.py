@@ -237,7 +237,8 @@ def run_resident(args, wl, dev):
         for e in pair:
             e.record(stream)  # creates the events before the timed region
 
-    def step(st, timing):
+    def step(st, timing, strm=None):
+        strm = stream if strm is None else strm
         for layer in range(L):
             # the split kernel's own start and end are recorded on its stream (kernel duration
             # without the queueing gap in front of it)
@@ -249,15 +250,15 @@ def run_resident(args, wl, dev):
                                         tables[layer][b].contiguous() if B > 1 else tables[layer][0])
                 K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
                                    out, ws.data, pages_per_split=args.pages_per_split, phase="split",
-                                   stream=stream, events=evs)
+                                   stream=strm, events=evs)
                 K.decode_attention(s, q_all[st, layer], pools[layer].data, tables[layer], ctx[st], max_ctx,
                                    out, ws.data, pages_per_split=args.pages_per_split, phase="combine",
-                                   stream=stream)
+                                   stream=strm)
             else:
                 # one layer's decode step: the token's append runs inside the split kernel
                 K.append_decode(s, knew[st, layer], vnew[st, layer], q_all[st, layer], pools[layer].data,
                                 tables[layer], ctx[st], max_ctx, out, ws.data,
-                                pages_per_split=args.pages_per_split, stream=stream, events=evs)
+                                pages_per_split=args.pages_per_split, stream=strm, events=evs)
             if evs is not None:
                 timed_split.append((evs[0], evs[1], sum(start_lens[b] + st + 1 for b in range(B)) * per_tok))
 
@@ -280,7 +281,35 @@ def run_resident(args, wl, dev):
     pps = args.pages_per_split or K.decode_split_pages(s, B, max_ctx, sum(lens) if B > 1 else 0)
     ceiling = None if args.no_read_ceiling else read_ceiling(
         args, wl, dev, s, pools, tables, [start_lens[b] + n_steps for b in range(B)], max_ctx, pps, per_tok)
+    # The same timed steps again, each captured once as a HIP graph and replayed (as a serving
+    # loop would run a decode step): the appends write the same tokens to the same rows again
+    # and the attention reads the same pages. Kernel events cannot be read inside a graph, so
+    # the roofline above comes from the eager steps; this is the step time without launch gaps.
+    graph = None
+    if not args.no_graph and not args.separate_append:
+        try:
+            cap = torch.cuda.Stream()
+            graphs = []
+            for st in range(args.warmup, n_steps):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step(st, False, cap)
+                graphs.append(g)
+            graphs[0].replay()
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            wall_g = time.perf_counter() - t1
+            if ws.status() != 0:
+                raise RuntimeError(f"decode status word {ws.status()} after the graph replays")
+            graph = {"ms_per_step": round(wall_g / args.steps * 1e3, 4), "value": round(kv_bytes / wall_g / 1e9, 2),
+                     "unit": "GB/s"}
+        except Exception as ex:  # the eager figures stand on their own
+            log(f"graph replay skipped: {ex!r}"[:300])
     res = dict(
+        graph=graph,
         read_ceiling=ceiling,
         value=kv_bytes / wall / 1e9,
         ms_per_step=wall / args.steps * 1e3,
@@ -769,6 +798,8 @@ def main():
                     help="N > 1: speculative verification of N new tokens per step and layer (append "
                          "of the N-token chunk, then kv_decode_attention_mq) instead of one decode token")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the replay of the timed steps as HIP graphs")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the plain read of the launch's pages (the split kernel's reference)")
     ap.add_argument("--cpu-tokens", type=int, default=131072)
@@ -874,6 +905,8 @@ def main():
         # a plain read of the same launch's pages on the same GPU, and the split kernel's rate
         # as a fraction of it
         "read_ceiling": res.get("read_ceiling"),
+        # the same steps captured as HIP graphs and replayed (no launch gaps; not `value`)
+        "graph_replay": res.get("graph"),
         "frac_of_read_ceiling": (round(res["achieved"] / res["read_ceiling"]["achieved"], 4)
                                  if res.get("read_ceiling") else None),
         # the chunk append kernel over the prefill's chunks: mean (what a kernel trace's average
