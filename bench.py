@@ -151,8 +151,9 @@ def build_resident(args, wl, dev, per_step=1):
 def read_ceiling(args, wl, dev, s, pools, tables, lens_now, max_ctx, pps, per_tok):
     """The roofline reference of the split kernel: a plain read of exactly the bytes one
     decode launch streams (every work item's KV-head part of its pages, through the same
-    block tables, split sizes and work-item order, with the split kernel's grid policy: one
-    workgroup per item within one round of resident workgroups, a counter beyond it;
+    block tables, split sizes and work-item order, with the split kernel's workgroup size and
+    grid policy: one workgroup per item within one round of resident workgroups, a counter
+    beyond it;
     lib/libkvmeasure.so), timed like the split kernel with events recorded at the kernel's
     own start and end, over the same layers in the same rotation (so its reads come from
     HBM as the split kernel's do). Returns None when the measurement library is not built."""
@@ -168,17 +169,19 @@ def read_ceiling(args, wl, dev, s, pools, tables, lens_now, max_ctx, pps, per_to
     fn = lib.kv_measure_read_pages
     fn.restype = C.c_int
     fn.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int,
-                   C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+                   C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     L, B = wl["layers"], len(lens_now)
-    # the split kernel's round of resident workgroups: two per CU for 4-bit K (four waves),
-    # one per CU for 8-bit K (eight waves)
-    n_resident = (2 if wl["fmt"] in ("q4_0", "fp4") else 1) * torch.cuda.get_device_properties(dev).multi_processor_count
+    # the split kernel's workgroups and their round of residents: four waves, two per CU, for
+    # 4-bit K; eight waves, one per CU, for 8-bit K
+    four_bit_k = wl["fmt"] in ("q4_0", "fp4")
+    threads = 256 if four_bit_k else 512
+    n_resident = (2 if four_bit_k else 1) * torch.cuda.get_device_properties(dev).multi_processor_count
     counter = torch.zeros(2, dtype=torch.int32, device=dev)
     n_kv = 4
     head_bytes = per_tok * PAGE // n_kv
     n_splits = -(-(-(-max_ctx // PAGE)) // pps)
     ctx = torch.tensor(lens_now, dtype=torch.int32, device=dev)
-    out = torch.empty(n_splits * B * n_kv * 256, dtype=torch.int32, device=dev)
+    out = torch.empty(n_splits * B * n_kv * threads, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     evs = []
     for rep in range(args.warmup + args.steps):
@@ -188,7 +191,7 @@ def read_ceiling(args, wl, dev, s, pools, tables, lens_now, max_ctx, pps, per_to
             b.record(stream)  # (creates the events; the launch records them again)
             bt = tables[layer]
             r = fn(pools[layer].data.data_ptr(), pools[layer].n_pages, head_bytes, n_kv, bt.data_ptr(), bt.shape[1],
-                   ctx.data_ptr(), B, pps, n_splits, n_resident, counter.data_ptr(), out.data_ptr(),
+                   ctx.data_ptr(), B, pps, n_splits, threads, n_resident, counter.data_ptr(), out.data_ptr(),
                    C.c_void_p(stream.cuda_stream), C.c_void_p(a.cuda_event), C.c_void_p(b.cuda_event))
             if r != 0:
                 raise RuntimeError("kv_measure_read_pages rejected its arguments")

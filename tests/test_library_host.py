@@ -297,14 +297,14 @@ def test_measurement_library_loads_and_rejects_bad_arguments():
     fn = C.CDLL(path).kv_measure_read_pages
     fn.restype = C.c_int
     fn.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int,
-                   C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+                   C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
     dummy = C.c_void_p(16)  # never dereferenced: every call below is rejected first
-    ok = dict(pool=dummy, n=8, hb=73728, nkv=4, bt=dummy, mp=8, ctx=dummy, b=1, pps=2, ns=4, nr=0, out=dummy)
+    ok = dict(pool=dummy, n=8, hb=73728, nkv=4, bt=dummy, mp=8, ctx=dummy, b=1, pps=2, ns=4, th=256, nr=0, out=dummy)
     def call(**kw):
         a = dict(ok, **kw)
         return fn(a["pool"], a["n"], a["hb"], a["nkv"], a["bt"], a["mp"], a["ctx"], a["b"], a["pps"], a["ns"],
-                  a["nr"], None, a["out"], None, None, None)
+                  a["th"], a["nr"], None, a["out"], None, None, None)
     for bad in (dict(pool=None), dict(bt=None), dict(ctx=None), dict(out=None), dict(hb=0), dict(hb=73720),
                 dict(hb=147456 + 16), dict(nkv=0), dict(b=0), dict(mp=0), dict(pps=0), dict(ns=0), dict(n=0),
-                dict(nr=-1)):
+                dict(nr=-1), dict(th=128), dict(th=1024)):
         assert call(**bad) == -1, bad
