@@ -55,7 +55,7 @@
 //   partial is rotated back by H first (H is linear, so merging rotated-back
 //   partials equals rotating the merged output back).
 //
-// Kernel 2 (decode_combine): per (query head, sequence, 64-element chunk), the
+// Kernel 2 (decode_combine): per (query head, sequence, 32-element chunk), the
 // log-sum-exp merge of the partials.
 //
 // Tokens past the context length are masked (score -inf, scale 0), so stale
@@ -1149,15 +1149,17 @@ __global__ __launch_bounds__(64 * NW, (NW == 4 && !(DYN && KK == kQ4)) ? 2 : 1) 
 }
 
 // Log-sum-exp merge of the partials of one (query head, sequence) for one chunk of
-// 64 head elements (partials of rotated V were rotated back by the split kernel).
-// 256 threads: four groups of 64 (one thread per element) each merge a quarter of
-// the splits; a thread's 32 partial values of a pass are loaded together with the
+// 32 head elements (partials of rotated V were rotated back by the split kernel).
+// 256 threads: eight groups of 32 (one thread per element) each merge an eighth of
+// the splits; a thread's 16 partial values of a pass are loaded together with the
 // split maxima, before the weights are known; the group sums are added in a fixed
-// order. Every chunk's workgroup forms the (cheap) maximum and weights itself.
+// order. Every chunk's workgroup forms the (cheap) maximum and weights itself. The
+// merge is latency-bound: 32-element chunks give twice the workgroups of 64-element
+// ones, each with half the loads per thread, and finish sooner.
 constexpr int kCombineThreads = 256;
-constexpr int kCombineElems = 64;                              // head elements per workgroup
+constexpr int kCombineElems = 32;                              // head elements per workgroup
 constexpr int kCombineGroups = kCombineThreads / kCombineElems;
-constexpr int kCombineRun = 32;                                // splits per thread per pass
+constexpr int kCombineRun = 16;                                // splits per thread per pass
 constexpr int kCombinePass = kCombineGroups * kCombineRun;     // splits per pass
 constexpr int kCombineChunk = 1024;                            // split weights held in LDS
 
