@@ -10,17 +10,20 @@ written out step by step:
    element e: S[p][g][e] = sum over the page's tokens of k[t][g][e] * 2^24. fp16
    values are integer multiples of 2^-24 below 2^16, so every term and the sum
    (at most 256 terms, below 2^48) are exact integers.
-2. Query sums. Q[g][e] = sum over the query heads h of KV head g's group of
+2. Page representatives. R[p][g][e] = S[p][g][e] / 2^32 (the exact key sum
+   divided by 256, the mean key of a full page) rounded once to fp16, nearest
+   with ties to even. Scores read these 2-byte values instead of the 8-byte sums.
+3. Query sums. Q[g][e] = sum over the query heads h of KV head g's group of
    q[h][e] * 2^24 (exact integers below 2^43).
-3. Score. score[p] = sum over g and e of Q[g][e] * S[p][g][e]: the summed
-   query-key products of the group's heads with the page's keys, up to the
-   positive factor 2^48; an exact integer (Python int).
-4. Selection of k pages out of n: if n <= k, every page; otherwise the last
+4. Score. score[p] = sum over g and e of Q[g][e] * R[p][g][e] * 2^24: the summed
+   query-key products of the group's heads with the page's representative keys,
+   up to the positive factor 2^48; an exact integer (Python int).
+5. Selection of k pages out of n: if n <= k, every page; otherwise the last
    page (the one holding the newest tokens) and the k - 1 other pages of
    largest score, ties to the lower page index. Returned in ascending order.
 
-Every step is integer arithmetic, so the selection is exact and does not depend
-on any summation order.
+Steps 1, 3 and 4 are integer arithmetic and step 2 one rounding of an exact
+value, so the selection is exact and does not depend on any summation order.
 """
 
 from __future__ import annotations
@@ -50,22 +53,33 @@ def key_sums(k, n_pages: int | None = None) -> np.ndarray:
     return S
 
 
+def key_reps(S) -> np.ndarray:
+    """S int64 [..., D] -> R fp16 (step 2): S / 2^32 rounded once to fp16, nearest-even.
+    |S| < 2^48, so S / 2^32 is exact in float64 and the cast rounds it once."""
+    S = np.asarray(S, np.int64)
+    x = S.astype(np.float64)
+    assert np.array_equal(x.astype(np.int64), S), "key sums must be exact in float64"
+    return (x / 4294967296.0).astype(np.float16)
+
+
 def query_sums(q, n_kv_heads: int) -> np.ndarray:
-    """q: fp16 [Hq, D] -> Q int64 [Hkv, D] (step 2; groups of Hq / Hkv consecutive heads)."""
+    """q: fp16 [Hq, D] -> Q int64 [Hkv, D] (step 3; groups of Hq / Hkv consecutive heads)."""
     qi = fp16_to_int(q)
     hq, d = qi.shape
     G = hq // n_kv_heads
     return qi.reshape(n_kv_heads, G, d).sum(axis=1)
 
 
-def page_scores(q, S) -> list:
-    """Exact scores (Python ints) of every page (step 3)."""
-    Q = query_sums(q, S.shape[1]).astype(object)
-    return [int((Q * S[p].astype(object)).sum()) for p in range(S.shape[0])]
+def page_scores(q, R) -> list:
+    """Exact scores (Python ints) of every page from its representatives R fp16
+    [n_pages, Hkv, D] (step 4)."""
+    Q = query_sums(q, R.shape[1]).astype(object)
+    Ri = fp16_to_int(R)
+    return [int((Q * Ri[p].astype(object)).sum()) for p in range(R.shape[0])]
 
 
 def select_pages(scores, k_sel: int) -> list:
-    """Step 4: the last page plus the k_sel - 1 best others (ties: lower index), ascending."""
+    """Step 5: the last page plus the k_sel - 1 best others (ties: lower index), ascending."""
     n = len(scores)
     if n <= k_sel:
         return list(range(n))
@@ -76,5 +90,4 @@ def select_pages(scores, k_sel: int) -> list:
 
 def select(q, k, k_sel: int) -> list:
     """Selection for query q [Hq, D] over keys k [T, Hkv, D] (all steps)."""
-    S = key_sums(k)
-    return select_pages(page_scores(q, S), k_sel)
+    return select_pages(page_scores(q, key_reps(key_sums(k))), k_sel)
