@@ -531,6 +531,7 @@ def run_streaming(args, dev):
     if qsa and args.gather_mode != "layers":
         raise SystemExit("--selection qsa chooses every layer's pages at once: use --gather-mode layers")
     key_sums = torch.zeros((L, n_pages, 4, 256), dtype=torch.int64, device=dev) if qsa else None
+    key_reps = torch.zeros((L, n_pages, 4, 256), dtype=torch.float16, device=dev) if qsa else None
     for layer in range(L):
         gen = torch.Generator(device=dev)
         gen.manual_seed(kvsynth.torch_seed(cfg, layer))
@@ -539,7 +540,7 @@ def run_streaming(args, dev):
             k, v = kvsynth.kv_tokens_torch(gen, 2048, gain, dev)
             staging.append(k, v, t0, ident)
             if qsa:
-                K.page_key_sums(s, k, t0, key_sums[layer])
+                K.page_key_sums(s, k, t0, key_sums[layer], key_reps[layer])
         host[layer * layer_bytes:(layer + 1) * layer_bytes].copy_(staging.data)
         torch.cuda.synchronize()
     del staging
@@ -585,8 +586,8 @@ def run_streaming(args, dev):
         if timing:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        # one call selects for all 16 layers (each from its own query and key sums)
-        K.select_pages(s, q_all[st, :, 0], key_sums, n_pages, c["n_sel"], sel_dev, sel_ws, stream=stream)
+        # one call selects for all 16 layers (each from its own query and page representatives)
+        K.select_pages(s, q_all[st, :, 0], key_reps, n_pages, c["n_sel"], sel_dev, sel_ws, stream=stream)
         if timing:
             e1.record(stream)
             select_ev.append((e0, e1))
@@ -796,7 +797,7 @@ def main():
                          "per layer before its attention, or per-layer gathers on a copy stream")
     ap.add_argument("--selection", choices=["random", "qsa"], default="random",
                     help="streaming workload: pages drawn at random with the set miss rate, or chosen on "
-                         "the GPU from each layer's query and per-page key sums (kv_select_pages)")
+                         "the GPU from each layer's query and per-page key representatives (kv_select_pages)")
     ap.add_argument("--queries", type=int, default=1, metavar="N",
                     help="N > 1: speculative verification of N new tokens per step and layer (append "
                          "of the N-token chunk, then kv_decode_attention_mq) instead of one decode token")

@@ -470,36 +470,46 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
  * Page selection for streaming mode (KV-offload news page, section
  * "新招不是全搬，而是分层放": attention over a fixed budget of selected tokens,
  * whose selection rule the page does not give; this library declares the
- * plain rule below). All arithmetic is on exact integers, so the result does
- * not depend on summation order and is the same on every call.
+ * plain rule below). The key sums are exact integers and each page
+ * representative one rounding of an exact value, so the result does not
+ * depend on summation order and is the same on every call.
  *
  * kv_page_key_sums - adds tokens [start_pos, start_pos + n_tokens) of one
- * sequence to its per-page key sums:
+ * sequence to its per-page key sums and rounds the page representatives:
  *   sums[p][g][e] += k[t][g][e] * 2^24 for every token t of logical page p
+ *   reps[p][g][e]  = sums[p][g][e] / 2^32 rounded once to fp16 (nearest, ties
+ *                    to even): the page's key sum over 256, for every page p
+ *                    the call adds tokens to
  * (fp16 keys are integer multiples of 2^-24, so each term is an exact integer;
- * a page's sum stays below 2^48).
+ * a page's sum stays below 2^48 and its representative within fp16 range).
  *   k       device fp16 [n_tokens][n_kv_heads][256] (the keys as appended).
  *   sums    device int64 [n_pages_cap][n_kv_heads][256], zero before the
- *           first token of each page is added. Atomic adds: calls may overlap.
+ *           first token of each page is added. Atomic adds: the sums of calls
+ *           that overlap are exact.
+ *   reps    device fp16 [n_pages_cap][n_kv_heads][256]; each element is
+ *           rounded from the sum the call's own add produced, so calls that
+ *           add to the same page must be ordered (one stream) for the
+ *           representatives to be those of the final sums.
  *
  * kv_select_pages - the pages one step attends, for n_sets independent sets
  * (layers, or sequences of equal page count) in one call. For set i:
  *   score[p] = sum over KV heads g and elements e of
- *              (sum over g's query heads h of q[i][h][e] * 2^24) * sums[i][p][g][e]
+ *              (sum over g's query heads h of q[i][h][e] * 2^24) * reps[i][p][g][e] * 2^24
  * (an exact 128-bit integer); the selection is the last page (p = n_pages - 1,
  * the newest tokens) and the k_sel - 1 other pages of largest score, ties to
  * the lower page index, written in ascending order to out_selection[i] (device
  * int32 [n_sets][k_sel]; the first min(k_sel, n_pages) entries); with
- * n_pages <= k_sel, every page.
+ * n_pages <= k_sel, every page. It reads 512 B per page and KV head.
  *   q          device fp16 [n_sets][n_q_heads][256] (each set's query).
- *   sums       device int64 [n_sets][sums_pages][n_kv_heads][256], sums_pages >= n_pages.
+ *   reps       device fp16 [n_sets][reps_pages][n_kv_heads][256], 16-B aligned,
+ *              reps_pages >= n_pages (as kv_page_key_sums writes them).
  *   n_pages    pages of the context (<= 32768); k_sel in 1..256; at most 8 KV heads.
  *   workspace  device, >= kv_select_workspace_bytes(n_pages, n_sets) bytes, 16-B aligned.
  */
 int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,
-                     int64_t* sums, int64_t n_pages_cap, void* stream);
+                     int64_t* sums, void* reps, int64_t n_pages_cap, void* stream);
 size_t kv_select_workspace_bytes(int64_t n_pages, int32_t n_sets);
-int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t sums_pages,
+int kv_select_pages(const kv_shape* shape, const void* q, const void* reps, int64_t reps_pages,
                     int64_t n_pages, int32_t k_sel, int32_t n_sets, int32_t* out_selection,
                     void* workspace, size_t workspace_bytes, void* stream);
 

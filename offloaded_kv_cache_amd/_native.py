@@ -89,7 +89,7 @@ def _load():
                                       P, P]),
         "kv_gather_pages_layers": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
                                              P, P, P, P, P]),
-        "kv_page_key_sums": (C.c_int, [C.POINTER(KVShape), P, I64, I64, P, I64, P]),
+        "kv_page_key_sums": (C.c_int, [C.POINTER(KVShape), P, I64, I64, P, P, I64, P]),
         "kv_select_workspace_bytes": (SZ, [I64, I32]),
         "kv_select_pages": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, I32, I32, P, P, SZ, P]),
         "kv_host_f64_to_f16": (C.c_uint16, [C.c_double]),
@@ -420,16 +420,20 @@ def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, 
     return nm
 
 
-def page_key_sums(s: KVShape, k, start_pos: int, sums, stream=None):
+def page_key_sums(s: KVShape, k, start_pos: int, sums, reps, stream=None):
     """kv_page_key_sums: add keys k (fp16 [n, n_kv_heads, 256]) of tokens start_pos.. to
-    sums (device int64 [n_pages_cap, n_kv_heads, 256])."""
+    sums (device int64 [n_pages_cap, n_kv_heads, 256]) and round the touched pages'
+    representatives into reps (device fp16, same shape)."""
     torch = _torch()
     if k.dim() != 3 or k.shape[1:] != (s.n_kv_heads, s.head_dim):
         raise ValueError("k must be [n_tokens, n_kv_heads, head_dim]")
     if sums.dim() != 3 or sums.shape[1:] != (s.n_kv_heads, s.head_dim):
         raise ValueError("sums must be [n_pages_cap, n_kv_heads, head_dim]")
+    if reps.shape != sums.shape:
+        raise ValueError("reps must have the shape of sums")
     _check(lib.kv_page_key_sums(C.byref(s), _ptr(k, torch.float16, name="k"), k.shape[0], start_pos,
-                                _ptr(sums, torch.int64, name="sums"), sums.shape[0], _stream(stream)))
+                                _ptr(sums, torch.int64, name="sums"), _ptr(reps, torch.float16, name="reps"),
+                                sums.shape[0], _stream(stream)))
 
 
 def select_workspace_bytes(n_pages: int, n_sets: int = 1) -> int:
@@ -439,21 +443,21 @@ def select_workspace_bytes(n_pages: int, n_sets: int = 1) -> int:
     return nb
 
 
-def select_pages(s: KVShape, q, sums, n_pages: int, k_sel: int, out_selection, workspace, stream=None):
+def select_pages(s: KVShape, q, reps, n_pages: int, k_sel: int, out_selection, workspace, stream=None):
     """kv_select_pages over the leading dimension of q ([n_sets, Hq, 256], or [Hq, 256] for
-    one set), sums ([n_sets, sums_pages, Hkv, 256] or [sums_pages, Hkv, 256]) and
+    one set), reps (fp16 [n_sets, reps_pages, Hkv, 256] or [reps_pages, Hkv, 256]) and
     out_selection ([n_sets, k_sel] or [k_sel]); each set's pages in ascending order."""
     torch = _torch()
     one = q.dim() == 2
     n_sets = 1 if one else q.shape[0]
-    if q.shape[-2:] != (s.n_q_heads, s.head_dim) or sums.dim() != (3 if one else 4):
-        raise ValueError("q must be [n_sets, n_q_heads, head_dim] and sums [n_sets, pages, n_kv_heads, head_dim]")
-    if not one and (sums.shape[0] != n_sets or out_selection.dim() != 2 or out_selection.shape[0] != n_sets):
-        raise ValueError("one sums block and one selection row per set")
+    if q.shape[-2:] != (s.n_q_heads, s.head_dim) or reps.dim() != (3 if one else 4):
+        raise ValueError("q must be [n_sets, n_q_heads, head_dim] and reps [n_sets, pages, n_kv_heads, head_dim]")
+    if not one and (reps.shape[0] != n_sets or out_selection.dim() != 2 or out_selection.shape[0] != n_sets):
+        raise ValueError("one reps block and one selection row per set")
     if out_selection.shape[-1] != k_sel:
         raise ValueError("out_selection rows must hold k_sel entries")
-    _check(lib.kv_select_pages(C.byref(s), _ptr(q, torch.float16, name="q"), _ptr(sums, torch.int64, name="sums"),
-                               sums.shape[-3], n_pages, k_sel, n_sets,
+    _check(lib.kv_select_pages(C.byref(s), _ptr(q, torch.float16, name="q"), _ptr(reps, torch.float16, name="reps"),
+                               reps.shape[-3], n_pages, k_sel, n_sets,
                                _ptr(out_selection, torch.int32, name="out_selection"),
                                _buf(workspace, "workspace"), workspace.numel(),
                                _stream(stream)))

@@ -585,17 +585,18 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
 }
 
 int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,
-                     int64_t* sums, int64_t n_pages_cap, void* stream) {
+                     int64_t* sums, void* reps, int64_t n_pages_cap, void* stream) {
   if (int r = check_shape(shape)) return r;
   if (n_tokens < 0 || start_pos < 0) return fail(KV_EINVAL, "negative token count or position");
   if (n_tokens == 0) return ok();
-  if (!k || !sums) return fail(KV_EINVAL, "NULL buffer");
-  if (!aligned(k, 2) || !aligned(sums, 8)) return fail(KV_EALIGN, "misaligned buffer (k: 2 B, sums: 8 B)");
+  if (!k || !sums || !reps) return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(k, 2) || !aligned(sums, 8) || !aligned(reps, 2))
+    return fail(KV_EALIGN, "misaligned buffer (k: 2 B, sums: 8 B, reps: 2 B)");
   if ((start_pos + n_tokens - 1) / kPageTokens >= n_pages_cap)
     return fail(KV_EINVAL, "tokens up to position %lld need more than %lld pages of sums",
                 (long long)(start_pos + n_tokens - 1), (long long)n_pages_cap);
   hipError_t e = launch_key_sums(shape->n_kv_heads, (const uint16_t*)k, n_tokens, start_pos, sums,
-                                 (hipStream_t)stream);
+                                 (uint16_t*)reps, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "key-sum launch");
   return ok();
 }
@@ -610,7 +611,7 @@ size_t kv_select_workspace_bytes(int64_t n_pages, int32_t n_sets) {
   return (size_t)(n > 0 ? n : 1) * 16;
 }
 
-int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, int64_t sums_pages,
+int kv_select_pages(const kv_shape* shape, const void* q, const void* reps, int64_t reps_pages,
                     int64_t n_pages, int32_t k_sel, int32_t n_sets, int32_t* out_selection,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (int r = check_shape(shape)) return r;
@@ -620,16 +621,16 @@ int kv_select_pages(const kv_shape* shape, const void* q, const int64_t* sums, i
   if (shape->n_kv_heads > select_max_kv_heads())
     return fail(KV_EUNSUPPORTED, "page selection takes at most %d KV heads", select_max_kv_heads());
   if (n_sets < 0 || n_sets > 65535) return fail(KV_EINVAL, "n_sets out of range (0..65535)");
-  if (sums_pages < n_pages) return fail(KV_EINVAL, "sums_pages (%lld) below n_pages (%lld)",
-                                        (long long)sums_pages, (long long)n_pages);
+  if (reps_pages < n_pages) return fail(KV_EINVAL, "reps_pages (%lld) below n_pages (%lld)",
+                                        (long long)reps_pages, (long long)n_pages);
   if (n_pages == 0 || n_sets == 0) return ok();
-  if (!q || !sums || !out_selection || !workspace) return fail(KV_EINVAL, "NULL buffer");
-  if (!aligned(q, 2) || !aligned(sums, 8) || !aligned(out_selection, 4) || !aligned(workspace, 16))
-    return fail(KV_EALIGN, "misaligned buffer (q: 2 B, sums: 8 B, selection: 4 B, workspace: 16 B)");
+  if (!q || !reps || !out_selection || !workspace) return fail(KV_EINVAL, "NULL buffer");
+  if (!aligned(q, 2) || !aligned(reps, 16) || !aligned(out_selection, 4) || !aligned(workspace, 16))
+    return fail(KV_EALIGN, "misaligned buffer (q: 2 B, reps: 16 B, selection: 4 B, workspace: 16 B)");
   const size_t need = (size_t)n_pages * n_sets * 16;
   if (workspace_bytes < need)
     return fail(KV_ESMALL, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
-  hipError_t e = launch_select(shape->n_q_heads, shape->n_kv_heads, (const uint16_t*)q, sums, sums_pages,
+  hipError_t e = launch_select(shape->n_q_heads, shape->n_kv_heads, (const uint16_t*)q, (const uint16_t*)reps, reps_pages,
                                (int)n_pages, k_sel, n_sets, out_selection, workspace, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "selection launch");
   return ok();

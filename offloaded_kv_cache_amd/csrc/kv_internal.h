@@ -198,9 +198,9 @@ hipError_t launch_zero_words(uint32_t* p, int n_words, hipStream_t stream);
 
 // Page selection (kv_select.hip).
 hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
-                           int64_t* sums, hipStream_t stream);
-hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const int64_t* sums,
-                         int64_t sums_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
+                           int64_t* sums, uint16_t* reps, hipStream_t stream);
+hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const uint16_t* reps,
+                         int64_t reps_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
                          hipStream_t stream);
 int select_max_pages();
 int select_max_k();

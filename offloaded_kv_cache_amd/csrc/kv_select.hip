@@ -4,13 +4,15 @@
 // offload), section "新招不是全搬，而是分层放": attention over a fixed budget of
 // selected tokens, with most of the cache in system memory; the page's account of
 // the selection rule breaks off. The rule implemented (declared, see
-// include/kvcache.h) works on exact integers:
+// include/kvcache.h) works on exact integers and one rounding:
 //   S[p][g][e] = sum over page p's tokens of k * 2^24     (key sums, int64)
+//   R[p][g][e] = S[p][g][e] / 2^32 rounded once to fp16   (page representatives)
 //   Q[g][e]    = sum over KV head g's query heads of q * 2^24
-//   score[p]   = sum over g, e of Q[g][e] * S[p][g][e]    (128-bit integer)
+//   score[p]   = sum over g, e of Q[g][e] * R[p][g][e] * 2^24   (128-bit integer)
 // then the last page plus the k - 1 other pages of largest score (ties to the lower
 // page index), in ascending order. Integer sums do not depend on their order, so
-// the key sums can be accumulated with atomics and every selection is exact.
+// the key sums can be accumulated with atomics and every selection is exact; the
+// scores read the 2-byte representatives, a quarter of the sums' bytes.
 #include "kv_internal.h"
 
 namespace kvc {
@@ -26,17 +28,33 @@ __device__ inline int64_t f16_to_int(uint16_t h) {  // exact: |h| * 2^24 < 2^40
 }
 
 // Key sums of the tokens [start, start + n) that fall in logical page `first_page +
-// blockIdx.x`, KV head blockIdx.y; thread e owns element e.
+// blockIdx.x`, KV head blockIdx.y; thread e owns element e. The representative is
+// rounded from the sum the thread's own atomic add produced (its old value plus the
+// addend), so within one call it is that of the complete sum.
 __global__ __launch_bounds__(kThreads) void key_sums_kernel(const uint16_t* __restrict__ k, int64_t n,
                                                            int64_t start, int64_t first_page,
-                                                           int n_kv_heads, int64_t* __restrict__ sums) {
+                                                           int n_kv_heads, int64_t* __restrict__ sums,
+                                                           uint16_t* __restrict__ reps) {
   const int e = threadIdx.x, g = blockIdx.y;
   const int64_t page = first_page + blockIdx.x;
   const int64_t t0 = max(start, page * kPageTokens), t1 = min(start + n, (page + 1) * kPageTokens);
   int64_t acc = 0;
   for (int64_t t = t0; t < t1; ++t) acc += f16_to_int(k[((t - start) * n_kv_heads + g) * kHeadDim + e]);
-  atomicAdd(reinterpret_cast<unsigned long long*>(&sums[(page * n_kv_heads + g) * kHeadDim + e]),
-            (unsigned long long)acc);
+  const int64_t at = (page * n_kv_heads + g) * kHeadDim + e;
+  const unsigned long long old =
+      atomicAdd(reinterpret_cast<unsigned long long*>(&sums[at]), (unsigned long long)acc);
+  const int64_t now = (int64_t)(old + (unsigned long long)acc);  // |now| < 2^48: exact in fp64
+  reps[at] = f64_to_f16_rne((double)now * 0x1p-32);
+}
+
+// An fp16 value times 2^24 as an integer, from its bits: magnitude m * 2^(max(E, 1) - 1)
+// with m the significand (implicit bit included for E > 0), as |Q| * m < 2^54 fits int64
+// the product with a query sum is formed before the shift.
+__device__ inline i128 times_rep(int64_t qs, uint16_t h) {
+  const int E = (h >> 10) & 31;
+  const int64_t m = (int64_t)((h & 0x3FF) | (E ? 0x400 : 0));
+  const i128 v = (i128)(qs * m) << (E ? E - 1 : 0);
+  return (h & 0x8000) ? -v : v;
 }
 
 // Scores of a tile of kTilePages pages of selection set blockIdx.y (a layer or a
@@ -49,15 +67,15 @@ constexpr int kSlice = kHeadDim / kParts;                // 16 elements per thre
 constexpr int kMaxKvHeads = 8;
 
 __global__ __launch_bounds__(kThreads) void page_score_kernel(const uint16_t* __restrict__ q,
-                                                             const int64_t* __restrict__ sums,
-                                                             int64_t sums_pages, int n_pages,
+                                                             const uint16_t* __restrict__ reps,
+                                                             int64_t reps_pages, int n_pages,
                                                              int n_q_heads, int n_kv_heads,
                                                              i128* __restrict__ scores) {
   __shared__ int64_t qsum[kMaxKvHeads][kHeadDim];
   __shared__ i128 part[kTilePages][kParts];
   const int tid = threadIdx.x;
   q += (size_t)blockIdx.y * n_q_heads * kHeadDim;
-  sums += (size_t)blockIdx.y * sums_pages * n_kv_heads * kHeadDim;
+  reps += (size_t)blockIdx.y * reps_pages * n_kv_heads * kHeadDim;
   scores += (size_t)blockIdx.y * n_pages;
   const int G = n_q_heads / n_kv_heads;
   for (int g = 0; g < n_kv_heads; ++g) {  // Q[g][e] for e = tid
@@ -71,9 +89,14 @@ __global__ __launch_bounds__(kThreads) void page_score_kernel(const uint16_t* __
   i128 acc = 0;
   if (page < n_pages) {
     for (int g = 0; g < n_kv_heads; ++g) {
-      const int64_t* sp = sums + (page * n_kv_heads + g) * kHeadDim + i * kSlice;
+      // the thread's 16 representatives: two 16-byte loads
+      const uint4* rp = reinterpret_cast<const uint4*>(reps + (page * n_kv_heads + g) * kHeadDim + i * kSlice);
+      const uint4 w[2] = {rp[0], rp[1]};
 #pragma unroll
-      for (int u = 0; u < kSlice; ++u) acc += (i128)qsum[g][i * kSlice + u] * (i128)sp[u];
+      for (int u = 0; u < kSlice; ++u) {
+        const uint32_t word = (&w[u >> 3].x)[(u >> 1) & 3];
+        acc += times_rep(qsum[g][i * kSlice + u], (uint16_t)(u & 1 ? word >> 16 : word & 0xFFFFu));
+      }
     }
   }
   part[j][i] = acc;
@@ -163,21 +186,21 @@ int select_max_k() { return kMaxSelect; }
 int select_max_kv_heads() { return kMaxKvHeads; }
 
 hipError_t launch_key_sums(int n_kv_heads, const uint16_t* k, int64_t n_tokens, int64_t start_pos,
-                           int64_t* sums, hipStream_t stream) {
+                           int64_t* sums, uint16_t* reps, hipStream_t stream) {
   if (n_tokens <= 0) return hipSuccess;
   const int64_t p0 = start_pos / kPageTokens, p1 = (start_pos + n_tokens - 1) / kPageTokens;
   dim3 grid((unsigned)(p1 - p0 + 1), (unsigned)n_kv_heads), block(kThreads);
-  hipLaunchKernelGGL(key_sums_kernel, grid, block, 0, stream, k, n_tokens, start_pos, p0, n_kv_heads, sums);
+  hipLaunchKernelGGL(key_sums_kernel, grid, block, 0, stream, k, n_tokens, start_pos, p0, n_kv_heads, sums, reps);
   return hipGetLastError();
 }
 
-hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const int64_t* sums,
-                         int64_t sums_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
+hipError_t launch_select(int n_q_heads, int n_kv_heads, const uint16_t* q, const uint16_t* reps,
+                         int64_t reps_pages, int n_pages, int k_sel, int n_sets, int32_t* out, void* scores,
                          hipStream_t stream) {
   if (n_pages <= 0 || n_sets <= 0) return hipSuccess;
   const unsigned tiles = (unsigned)((n_pages + kTilePages - 1) / kTilePages);
-  hipLaunchKernelGGL(page_score_kernel, dim3(tiles, (unsigned)n_sets), dim3(kThreads), 0, stream, q, sums,
-                     sums_pages, n_pages, n_q_heads, n_kv_heads, (i128*)scores);
+  hipLaunchKernelGGL(page_score_kernel, dim3(tiles, (unsigned)n_sets), dim3(kThreads), 0, stream, q, reps,
+                     reps_pages, n_pages, n_q_heads, n_kv_heads, (i128*)scores);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(top_pages_kernel, dim3((unsigned)n_sets), dim3(kThreads), 0, stream, (const i128*)scores,

@@ -286,11 +286,13 @@ static void argument_checks() {
   CHECK(tb.same(saved));
 
   int64_t* sums = reinterpret_cast<int64_t*>(a);
-  CHECK(kv_page_key_sums(&s, a, -1, 0, sums, 4, nullptr) < 0);
-  CHECK(kv_page_key_sums(&s, a, 10, 2000, sums, 4, nullptr) < 0);  // pages beyond the capacity
-  CHECK(kv_select_pages(&s, a, sums, 4, 8, 2, 1, reinterpret_cast<int32_t*>(a), a, 16, nullptr) < 0);  // sums_pages < n_pages
-  CHECK(kv_select_pages(&s, a, sums, 8, 8, 0, 1, reinterpret_cast<int32_t*>(a), a, 4096, nullptr) < 0);
-  CHECK(kv_select_pages(&s, a, sums, 8, 8, 300, 1, reinterpret_cast<int32_t*>(a), a, 4096, nullptr) < 0);
+  CHECK(kv_page_key_sums(&s, a, -1, 0, sums, a, 4, nullptr) < 0);
+  CHECK(kv_page_key_sums(&s, a, 10, 2000, sums, a, 4, nullptr) < 0);  // pages beyond the capacity
+  CHECK(kv_page_key_sums(&s, a, 10, 0, sums, nullptr, 4, nullptr) < 0);  // no representatives
+  CHECK(kv_select_pages(&s, a, a, 4, 8, 2, 1, reinterpret_cast<int32_t*>(a), a, 16, nullptr) < 0);  // reps_pages < n_pages
+  CHECK(kv_select_pages(&s, a, a, 8, 8, 0, 1, reinterpret_cast<int32_t*>(a), a, 4096, nullptr) < 0);
+  CHECK(kv_select_pages(&s, a, a, 8, 8, 300, 1, reinterpret_cast<int32_t*>(a), a, 4096, nullptr) < 0);
+  CHECK(kv_select_pages(&s, a, static_cast<char*>(a) + 2, 8, 8, 2, 1, reinterpret_cast<int32_t*>(a), a, 4096, nullptr) < 0);  // reps not 16-B aligned
 
   // every rejected call left a message
   CHECK(kv_last_error() != nullptr && std::strlen(kv_last_error()) > 0);
