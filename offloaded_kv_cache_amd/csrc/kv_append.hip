@@ -38,6 +38,13 @@ constexpr int kGroup = 32;                // tokens of a work item
 constexpr int kAppendWaves = 16;
 constexpr int kAppendThreads = 64 * kAppendWaves;
 
+// Row of V element e in the LDS staging of the element-major V plane. A staging store
+// has the 16 lanes of a row write elements 16 s + c (s = 0..15) of one token, rows 16 or
+// 32 bytes apart, which would all fall in one LDS bank; xoring the row's low four bits
+// with s puts them in different banks. A bijection of 0..255; the writer to global
+// memory reads row e at the same place.
+__device__ inline int vrow(int e) { return e ^ ((e >> 4) & 15); }
+
 // ---- four vectors per wave: lane l holds vector l >> 4, elements 16 (l & 15) + i
 
 // Butterfly stage of element bit log2(M) + 4 (M = 1, 2, 4, 8: lanes s and s ^ M of a row).
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     // ti + 16 (vectors 2, 3, lanes 32 further) share byte ti
     if (!four_bit(VK)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) vt[(16 * s + i) * VB + ti] = (uint8_t)code[i];
+      for (int i = 0; i < 16; ++i) vt[vrow(16 * s + i) * VB + ti] = (uint8_t)code[i];
     } else {
       uint32_t w[4], p[4];
       mv_bytes(code, w);
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
         for (int q = 0; q < 4; ++q) {
           const uint32_t b = w[q] | (p[q] << 4);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) vt[(16 * s + 4 * q + t) * VB + ti] = (uint8_t)(b >> (8 * t));
+          for (int t = 0; t < 4; ++t) vt[vrow(16 * s + 4 * q + t) * VB + ti] = (uint8_t)(b >> (8 * t));
         }
       }
     }
@@ -341,7 +348,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     for (int c = tid; c < kHeadDim * kPieces; c += kAppendThreads) {
       const int e = c / kPieces, p = c % kPieces;
       u4* dst = reinterpret_cast<u4*>(vplane + (size_t)e * code_row_bytes(VK) + (row0 % kPageTokens / kGroup) * VB + 16 * p);
-      u4 val = *reinterpret_cast<const u4*>(vt + e * VB + 16 * p);
+      u4 val = *reinterpret_cast<const u4*>(vt + vrow(e) * VB + 16 * p);
       if (!whole) {
         const u4 old = *dst;
         u4 keep;  // bits of the stored segment that belong to tokens outside the chunk
