@@ -13,7 +13,7 @@
 // page index), in ascending order. Integer sums do not depend on their order, so
 // the key sums can be accumulated with atomics and every selection is exact; the
 // scores read the 2-byte representatives, a quarter of the sums' bytes.
-#include "kv_internal.h"
+#include "kv_lanes.h"
 
 namespace kvc {
 namespace {
@@ -108,62 +108,134 @@ __global__ __launch_bounds__(kThreads) void page_score_kernel(const uint16_t* __
   }
 }
 
-// The selection: the last page, then k - 1 rounds of "best page not yet taken".
+// The selection: the last page, then k - 1 rounds of "best page not yet taken". Thread t
+// owns pages t, t + 256, ... (the last page excepted) and keeps the best and second best
+// of its pages not yet taken (a bit per page in LDS marks those taken); a round takes the
+// best over the threads (equal scores: the lower page). The owner of the page taken moves
+// its second best up, and looks at its pages again only when it wins a second time
+// (its second best is then unknown). The round's arg-max runs inside each wave by lane
+// exchanges, then over the four waves' results in LDS (double-buffered by round parity,
+// so one barrier a round).
 constexpr int kMaxSelect = 256;
 constexpr int kMaxPages = 32768;
+constexpr int kOwnWords = kMaxPages / kThreads / 32;  // taken bits of a thread's pages
+
+__device__ inline bool better(i128 s, int p, i128 bs, int bp) {  // (s, p) ahead of (bs, bp)?
+  return p >= 0 && (bp < 0 || s > bs || (s == bs && p < bp));
+}
+
+// (score, page) of lane ^ M
+template <int M>
+__device__ inline void xchg_pair(i128& s, int& p, int lane) {
+  const unsigned __int128 u = (unsigned __int128)s;
+  const uint32_t w0 = xchg32<M>((uint32_t)u, lane), w1 = xchg32<M>((uint32_t)(u >> 32), lane);
+  const uint32_t w2 = xchg32<M>((uint32_t)(u >> 64), lane), w3 = xchg32<M>((uint32_t)(u >> 96), lane);
+  s = (i128)(((unsigned __int128)w3 << 96) | ((unsigned __int128)w2 << 64) | ((unsigned __int128)w1 << 32) | w0);
+  p = (int)xchg32<M>((uint32_t)p, lane);
+}
+template <int M>
+__device__ inline void argmax_step(i128& s, int& p, int lane) {
+  i128 os = s;
+  int op = p;
+  xchg_pair<M>(os, op, lane);
+  if (better(os, op, s, p)) {
+    s = os;
+    p = op;
+  }
+}
+
+// The best and second best of thread tid's pages not taken (page -1: none); the scores
+// of 16 pages are loaded together, so that their latencies overlap.
+struct Best2 {
+  i128 s, s2;
+  int p, p2;
+};
+__device__ inline Best2 own_best(const i128* __restrict__ scores, int last, int tid,
+                                 const uint32_t (*taken)[kThreads]) {
+  Best2 b = {0, 0, -1, -1};
+  for (int j0 = 0; tid + kThreads * j0 < last; j0 += 16) {
+    i128 sc[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int p = tid + kThreads * (j0 + u);
+      sc[u] = p < last ? scores[p] : (i128)0;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + u, p = tid + kThreads * j;
+      const bool free = p < last && !((taken[j >> 5][tid] >> (j & 31)) & 1u);
+      if (!free) continue;
+      if (better(sc[u], p, b.s, b.p)) {  // pages visited in increasing order
+        b.s2 = b.s;
+        b.p2 = b.p;
+        b.s = sc[u];
+        b.p = p;
+      } else if (better(sc[u], p, b.s2, b.p2)) {
+        b.s2 = sc[u];
+        b.p2 = p;
+      }
+    }
+  }
+  return b;
+}
 
 __global__ __launch_bounds__(kThreads) void top_pages_kernel(const i128* __restrict__ scores, int n_pages,
                                                             int k_sel, int32_t* __restrict__ out) {
-  __shared__ uint8_t taken[kMaxPages];
   scores += (size_t)blockIdx.x * n_pages;  // selection set blockIdx.x
   out += (size_t)blockIdx.x * k_sel;
-  __shared__ i128 best_s[kThreads];
-  __shared__ int best_p[kThreads];
+  __shared__ i128 wbest_s[2][kThreads / 64];
+  __shared__ int wbest_p[2][kThreads / 64];
   __shared__ int chosen[kMaxSelect];
-  const int tid = threadIdx.x;
+  __shared__ uint32_t taken[kOwnWords][kThreads];  // column t: thread t's pages
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (n_pages <= k_sel) {
     for (int p = tid; p < n_pages; p += kThreads) out[p] = p;
     return;
   }
-  for (int p = tid; p < n_pages; p += kThreads) taken[p] = 0;
-  __syncthreads();
-  if (tid == 0) {
-    taken[n_pages - 1] = 1;
-    chosen[0] = n_pages - 1;
-  }
-  __syncthreads();
+  const int last = n_pages - 1;
+#pragma unroll
+  for (int w = 0; w < kOwnWords; ++w) taken[w][tid] = 0u;
+  Best2 b = own_best(scores, last, tid, taken);
+  if (tid == 0) chosen[0] = last;
   for (int r = 1; r < k_sel; ++r) {
-    i128 bs = 0;
-    int bp = -1;
-    for (int p = tid; p < n_pages - 1; p += kThreads) {
-      if (taken[p]) continue;
-      const i128 s = scores[p];
-      if (bp < 0 || s > bs) {  // pages visited in increasing order: equal scores keep the lower
-        bs = s;
-        bp = p;
-      }
-    }
-    best_s[tid] = bs;
-    best_p[tid] = bp;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-      if (tid < s) {
-        const int po = best_p[tid + s];
-        const i128 so = best_s[tid + s];
-        const int pm = best_p[tid];
-        if (po >= 0 && (pm < 0 || so > best_s[tid] || (so == best_s[tid] && po < pm))) {
-          best_s[tid] = so;
-          best_p[tid] = po;
-        }
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      taken[best_p[0]] = 1;
-      chosen[r] = best_p[0];
+    // arg-max inside the wave
+    i128 ws = b.s;
+    int wp = b.p;
+    argmax_step<1>(ws, wp, lane);
+    argmax_step<2>(ws, wp, lane);
+    argmax_step<4>(ws, wp, lane);
+    argmax_step<8>(ws, wp, lane);
+    argmax_step<16>(ws, wp, lane);
+    argmax_step<32>(ws, wp, lane);
+    const int buf = r & 1;
+    if (lane == 0) {
+      wbest_s[buf][wave] = ws;
+      wbest_p[buf][wave] = wp;
     }
     __syncthreads();
+    // over the waves (every thread, the same answer)
+    i128 gs = wbest_s[buf][0];
+    int gp = wbest_p[buf][0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w)
+      if (better(wbest_s[buf][w], wbest_p[buf][w], gs, gp)) {
+        gs = wbest_s[buf][w];
+        gp = wbest_p[buf][w];
+      }
+    if (tid == 0) chosen[r] = gp;
+    if (gp % kThreads == tid) {  // the owner: mark it taken, move its second best up
+      const int j = gp / kThreads;
+      taken[j >> 5][tid] |= 1u << (j & 31);
+      if (b.p2 != -2) {
+        b.s = b.s2;
+        b.p = b.p2;
+        b.p2 = -2;  // unknown
+      } else {
+        b = own_best(scores, last, tid, taken);
+      }
+    }
   }
+  __syncthreads();
   if (tid == 0) {  // ascending order (k is small)
     for (int i = 1; i < k_sel; ++i) {
       const int v = chosen[i];
