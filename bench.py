@@ -515,6 +515,7 @@ def run_streaming(args, dev):
 
     import kvsynth
     import offloaded_kv_cache_amd as K
+    from offloaded_kv_cache_amd import _native as N
 
     c = dict(C5)
     c["host_tokens"] = args.host_tokens
@@ -576,13 +577,35 @@ def run_streaming(args, dev):
     sel_dev = torch.empty((L, c["n_sel"]), dtype=torch.int32, device=dev)
     sel_ws = torch.empty(K.select_workspace_bytes(n_pages, L), dtype=torch.uint8, device=dev)
     select_ev = []
+    # The random draw stands in for the page selection and is input generation, not part of
+    # the step: every step's selections are drawn before the timed region, each against a
+    # shadow copy of its layer's table that the library's host CLOCK (kv_residency_select,
+    # the code the gather calls run) advances step by step, so the real tables later see
+    # the same selections and end in the same state.
+    drawn = None
+    if not qsa:
+        shadow = [N.Residency(c["slots"], n_pages) for _ in range(L)]
+        for sh, t in zip(shadow, tables):
+            sh.slot_page[:], sh.page_slot[:], sh.ref[:] = t.slot_page, t.page_slot, t.ref
+            sh.c.hand = t.hand
+        drawn = []
+        for _ in range(n_steps):
+            rows = [streaming_selection(rng, shadow[layer], n_pages, c["n_sel"], c["miss"]) for layer in range(L)]
+            for sh, sel in zip(shadow, rows):
+                sh.select(sel)
+            drawn.append(np.stack(rows))
+    # the timed steps' event pairs, created before the timed region
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    for pair in step_ev:
+        for e in pair:
+            e.record(stream)
 
     def choose(st, timing):
-        """Every layer's selection for step st: random with the workload's miss rate, or the
-        GPU page selection from each layer's query (copied to the host for the CLOCK step)."""
+        """Every layer's selection for step st: the random draw made above, or the GPU page
+        selection from each layer's query (copied to the host for the CLOCK step)."""
         if not qsa:
-            return np.stack([streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
-                             for layer in range(L)])
+            return drawn[st]
         if timing:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -597,19 +620,17 @@ def run_streaming(args, dev):
         nonlocal misses
         if args.gather_mode == "layers":
             sels = choose(st, timing)
+            # events recorded by the copy kernel's launch: the time of the copies on the GPU
+            ev = step_ev[st - args.warmup] if timing else None
+            m = int(sl.gather_layers(sels, host_layers, stream, events=ev).sum())
             if timing:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            m = int(sl.gather_layers(sels, host_layers, stream).sum())
-            if timing:
-                e1.record(stream)
-                gather_ev.append((e0, e1, m))
+                gather_ev.append((ev[0], ev[1], m))
                 misses += m
             for layer in range(L):
                 sl.attend(layer, q_all[st, layer], ctx, ctx_tok, out, ws.data, stream)
             return
         for layer in range(L):
-            sel = streaming_selection(rng, tables[layer], n_pages, c["n_sel"], c["miss"])
+            sel = drawn[st][layer]
             if timing:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 if sl.overlap:
@@ -632,6 +653,11 @@ def run_streaming(args, dev):
     wall = time.perf_counter() - t0
     if ws.status() != 0:
         raise RuntimeError(f"decode status word {ws.status()}")
+    if drawn is not None:  # the real tables ended where the shadow tables did
+        for sh, t in zip(shadow, tables):
+            if not (np.array_equal(sh.slot_page, t.slot_page) and np.array_equal(sh.ref, t.ref)
+                    and sh.hand == t.hand):
+                raise RuntimeError("residency tables diverged from the drawn selections' shadow tables")
     g_ms = sum(a.elapsed_time(b) for a, b, _ in gather_ev)
     copied = sum(m for _, _, m in gather_ev) * pb
     # pinned host -> device peak on this machine: one large plain copy
@@ -653,6 +679,8 @@ def run_streaming(args, dev):
                         "miss_rate": round(misses / (args.steps * L * c["n_sel"]), 4),
                         "pages_copied": int(misses), "bytes_copied": int(copied),
                         "gather_ms_per_step": round(g_ms / args.steps, 4),
+                        "gather_timing": "copy kernel (events recorded by its launch)" if args.gather_mode == "layers"
+                        else "events around each host call (CLOCK step, launch and copy)",
                         "schedule": args.gather_mode,
                         "selection": args.selection,
                         "selection_ms_per_step": round(sum(a.elapsed_time(b) for a, b in select_ev) / args.steps, 4)

@@ -467,6 +467,22 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
                            int32_t* out_block_tables, int32_t* out_n_miss, void* stream);
 
 /*
+ * kv_gather_pages_layers_timed - kv_gather_pages_layers, with `start_event` and
+ * `stop_event` (hipEvent_t, each may be NULL) recorded by the copy launches
+ * themselves: the start event at the start of the first copy kernel, the stop
+ * event at the end of the last one. Their elapsed time is the time the copies
+ * take on the GPU, without the host's CLOCK step or the launch in front of them
+ * (a PCIe rate, as a kernel trace reports it). Nothing is recorded when
+ * n_layers or n_sel is 0. Every other argument and all behaviour are those of
+ * kv_gather_pages_layers.
+ */
+int kv_gather_pages_layers_timed(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
+                                 const int32_t* selections, int32_t n_sel,
+                                 const void* const* host_pools, void* const* slot_pools,
+                                 int32_t* out_block_tables, int32_t* out_n_miss, void* stream,
+                                 void* start_event, void* stop_event);
+
+/*
  * Page selection for streaming mode (KV-offload news page, section
  * "新招不是全搬，而是分层放": attention over a fixed budget of selected tokens,
  * whose selection rule the page does not give; this library declares the

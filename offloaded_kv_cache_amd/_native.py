@@ -26,7 +26,8 @@ EXPORTED_SYMBOLS = (
     "kv_last_error", "kv_version", "kv_page_bytes", "kv_append_quantize", "kv_append_quantize_timed",
     "kv_decode_workspace_bytes", "kv_decode_split_pages", "kv_decode_attention", "kv_decode_split",
     "kv_decode_split_timed", "kv_decode_attention_noalloc",
-    "kv_decode_combine", "kv_decode_attention_mq", "kv_decode_mq_workspace_bytes", "kv_append_decode", "kv_gather_pages_layers", "kv_page_key_sums",
+    "kv_decode_combine", "kv_decode_attention_mq", "kv_decode_mq_workspace_bytes", "kv_append_decode", "kv_gather_pages_layers",
+    "kv_gather_pages_layers_timed", "kv_page_key_sums",
     "kv_select_workspace_bytes", "kv_select_pages",
     "kv_residency_reset",
     "kv_residency_select", "kv_gather_pages", "kv_host_f64_to_f16", "kv_host_encode_vector",
@@ -89,6 +90,8 @@ def _load():
                                       P, P]),
         "kv_gather_pages_layers": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
                                              P, P, P, P, P]),
+        "kv_gather_pages_layers_timed": (C.c_int, [C.POINTER(KVShape), I32, C.POINTER(KVResidency), P, I32,
+                                                   P, P, P, P, P, P, P]),
         "kv_page_key_sums": (C.c_int, [C.POINTER(KVShape), P, I64, I64, P, P, I64, P]),
         "kv_select_workspace_bytes": (SZ, [I64, I32]),
         "kv_select_pages": (C.c_int, [C.POINTER(KVShape), P, P, I64, I64, I32, I32, P, P, SZ, P]),
@@ -393,10 +396,12 @@ def gather_pages(s: KVShape, table: Residency, selection, host_pool, slot_pool, 
 
 
 def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, out_block_tables,
-                        stream=None):
+                        stream=None, events=None):
     """kv_gather_pages_layers: CLOCK step of every layer, then one page-in launch for all
     of them. selections int32 [L, n_sel]; out_block_tables device int32 [L, n_sel].
-    Returns the misses per layer (numpy int32 [L])."""
+    Returns the misses per layer (numpy int32 [L]). ``events`` = (start, stop)
+    torch.cuda.Event pair: recorded at the copy kernel's own start and end
+    (kv_gather_pages_layers_timed)."""
     torch = _torch()
     sel = np.ascontiguousarray(selections, dtype=np.int32)
     L = len(tables)
@@ -411,10 +416,13 @@ def gather_pages_layers(s: KVShape, tables, selections, host_pools, slot_pools, 
     hp = (C.c_void_p * L)(*[_buf(h, "host pool", pinned_ok=True).value for h in host_pools])
     sp = (C.c_void_p * L)(*[_buf(p, "slot pool").value for p in slot_pools])
     nm = np.zeros(L, np.int32)
-    _check(lib.kv_gather_pages_layers(C.byref(s), L, arr, sel.ctypes.data_as(C.c_void_p), sel.shape[1],
-                                      C.cast(hp, C.c_void_p), C.cast(sp, C.c_void_p),
-                                      _ptr(out_block_tables, torch.int32, name="out_block_tables"),
-                                      nm.ctypes.data_as(C.c_void_p), _stream(stream)))
+    fn, ev = lib.kv_gather_pages_layers, _event_ptrs(events)
+    if ev:
+        fn = lib.kv_gather_pages_layers_timed
+    _check(fn(C.byref(s), L, arr, sel.ctypes.data_as(C.c_void_p), sel.shape[1],
+              C.cast(hp, C.c_void_p), C.cast(sp, C.c_void_p),
+              _ptr(out_block_tables, torch.int32, name="out_block_tables"),
+              nm.ctypes.data_as(C.c_void_p), _stream(stream), *ev))
     for t, a in zip(tables, arr):  # the tables' arrays are shared; the hand is copied back
         t.c.hand = a.hand
     return nm

@@ -14,6 +14,7 @@
 #include <string>
 #include <vector>
 
+#include "kv_gather.h"
 #include "kv_internal.h"
 
 using namespace kvc;
@@ -521,10 +522,16 @@ int kv_gather_pages(const kv_shape* shape, kv_residency* t, const int32_t* selec
   return ok();
 }
 
-int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
-                           const int32_t* selections, int32_t n_sel, const void* const* host_pools,
-                           void* const* slot_pools, int32_t* out_block_tables, int32_t* out_n_miss,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kv_gather_pages_layers with optional events: `start` is recorded at the start of the
+// first copy kernel, `stop` at the end of the last one (none when there is nothing to do).
+int gather_layers(const kv_shape* shape, int32_t n_layers, kv_residency* tables, const int32_t* selections,
+                  int32_t n_sel, const void* const* host_pools, void* const* slot_pools,
+                  int32_t* out_block_tables, int32_t* out_n_miss, void* stream, void* start_event,
+                  void* stop_event) {
   if (int r = check_shape(shape)) return r;
   if (n_layers < 0 || n_sel < 0) return fail(KV_EINVAL, "negative size");
   if (n_layers == 0 || n_sel == 0) return ok();
@@ -576,12 +583,35 @@ int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency
       gb.src[i] = src[done_c + i];
       gb.dst[i] = dst[done_c + i];
     }
-    hipError_t e = launch_gather_multi(gb, pb, (hipStream_t)stream);
+    const bool first = done_e == 0 && done_c == 0;
+    const bool last = done_e + ne == total && done_c + nc == src.size();
+    hipError_t e = launch_gather_multi_timed(gb, pb, (hipStream_t)stream, first ? (hipEvent_t)start_event : nullptr,
+                                             last ? (hipEvent_t)stop_event : nullptr);
     if (e != hipSuccess) return hip_fail(e, "gather launch (the residency tables were already updated)");
     done_e += ne;
     done_c += nc;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_gather_pages_layers(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
+                           const int32_t* selections, int32_t n_sel, const void* const* host_pools,
+                           void* const* slot_pools, int32_t* out_block_tables, int32_t* out_n_miss,
+                           void* stream) {
+  return gather_layers(shape, n_layers, tables, selections, n_sel, host_pools, slot_pools, out_block_tables,
+                       out_n_miss, stream, nullptr, nullptr);
+}
+
+int kv_gather_pages_layers_timed(const kv_shape* shape, int32_t n_layers, kv_residency* tables,
+                                 const int32_t* selections, int32_t n_sel, const void* const* host_pools,
+                                 void* const* slot_pools, int32_t* out_block_tables, int32_t* out_n_miss,
+                                 void* stream, void* start_event, void* stop_event) {
+  return gather_layers(shape, n_layers, tables, selections, n_sel, host_pools, slot_pools, out_block_tables,
+                       out_n_miss, stream, start_event, stop_event);
 }
 
 int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int64_t start_pos,

@@ -11,7 +11,9 @@
 // arguments, so the host needs no device-side buffer for them. Each workgroup
 // moves one 64 KiB chunk of one page with 16-byte loads, eight in flight per
 // thread, enough to keep many PCIe read requests outstanding.
-#include "kv_internal.h"
+#include <hip/hip_ext.h>
+
+#include "kv_gather.h"
 
 namespace kvc {
 namespace {
@@ -74,11 +76,17 @@ __global__ __launch_bounds__(kThreads) void gather_multi_kernel(MultiGatherBatch
 
 }  // namespace
 
-hipError_t launch_gather_multi(const MultiGatherBatch& batch, int64_t page_bytes, hipStream_t stream) {
+hipError_t launch_gather_multi_timed(const MultiGatherBatch& batch, int64_t page_bytes, hipStream_t stream,
+                                     hipEvent_t start, hipEvent_t stop) {
   const unsigned chunks = (unsigned)((page_bytes + kChunk - 1) / kChunk);
   dim3 grid(chunks, (unsigned)(batch.n_copies > 0 ? batch.n_copies : 1)), block(kThreads);
-  hipLaunchKernelGGL(gather_multi_kernel, grid, block, 0, stream, batch, page_bytes);
+  // events (or NULL) recorded at the kernel's own start and end
+  hipExtLaunchKernelGGL(gather_multi_kernel, grid, block, 0, stream, start, stop, 0, batch, page_bytes);
   return hipGetLastError();
+}
+
+hipError_t launch_gather_multi(const MultiGatherBatch& batch, int64_t page_bytes, hipStream_t stream) {
+  return launch_gather_multi_timed(batch, page_bytes, stream, nullptr, nullptr);
 }
 
 hipError_t launch_gather(const GatherBatch& batch, int64_t page_bytes, const uint8_t* host_pool,

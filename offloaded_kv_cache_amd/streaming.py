@@ -44,11 +44,12 @@ class StreamedLayers:
         for e in self.gathered + self.attended:
             e.record(cur)  # every event starts out complete
 
-    def gather_layers(self, selections, host_pools, stream):
+    def gather_layers(self, selections, host_pools, stream, events=None):
         """Page in every layer's selection ([n_layers, n_sel]) with one launch on `stream`;
-        returns the misses per layer."""
+        returns the misses per layer. `events` = (start, stop): recorded at the copy
+        kernel's own start and end."""
         return N.gather_pages_layers(self.s, self.tables, selections, host_pools, self.slots,
-                                     self.block_table_all, stream=stream)
+                                     self.block_table_all, stream=stream, events=events)
 
     def gather(self, layer: int, selection, host_pool, stream) -> int:
         """Page in layer `layer`'s selection (CLOCK on the host, copy kernel on the GPU);

@@ -125,7 +125,8 @@ def draw_selections(L, n_pages, n_slots, n_sel, steps, seed):
 @pytest.mark.parametrize("fmt", ["int8", "k8v4", "fp8"])
 def test_gather_layers_equals_per_layer_gathers(gpu, fmt):
     """kv_gather_pages_layers (one launch for every layer) leaves the same tables, slots
-    and block tables as kv_gather_pages per layer, and attention over them is identical."""
+    and block tables as kv_gather_pages per layer, and attention over them is identical;
+    so does kv_gather_pages_layers_timed, whose events span the copy kernel."""
     L, n_pages, n_slots, n_sel, steps = 4, 30, 10, 8, 4
     s = K.shape(fmt)
     seqs = [Sequence(35, layer, 0, n_pages * 256, fmt) for layer in range(L)]
@@ -134,16 +135,20 @@ def test_gather_layers_equals_per_layer_gathers(gpu, fmt):
     q = to_dev(kvsynth.q_np(35, 0, steps * L).reshape(steps, L, 1, 24, 256), gpu)
     ctx = to_dev(np.array([n_sel * 256], np.int32), gpu)
     runs = []
-    for batched in (False, True):
+    for mode in ("per_layer", "layers", "layers_timed"):
         sl = K.streaming.StreamedLayers(s, L, n_slots, n_pages, n_sel, gpu)
         stream = torch.cuda.current_stream()
         ws = K.paged.DecodeWorkspace(s, 1, n_sel * 256, 0, device=gpu)
         out = torch.empty((1, 24, 256), dtype=torch.float32, device=gpu)
         keep = torch.empty((steps, L, 24, 256), dtype=torch.float32, device=gpu)
-        bts, miss = [], []
+        bts, miss, evs = [], [], []
         for st in range(steps):
-            if batched:
-                miss.append(list(sl.gather_layers(np.stack(sels[st]), host, stream)))
+            if mode != "per_layer":
+                ev = None
+                if mode == "layers_timed":
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    evs.append(ev)
+                miss.append(list(sl.gather_layers(np.stack(sels[st]), host, stream, events=ev)))
             else:
                 miss.append([sl.gather(layer, sels[st][layer], host[layer], stream) for layer in range(L)])
             bts.append(sl.block_table_all.cpu().numpy().copy())
@@ -152,14 +157,17 @@ def test_gather_layers_equals_per_layer_gathers(gpu, fmt):
                 keep[st, layer].copy_(out[0])
         torch.cuda.synchronize()
         assert ws.status() == 0
+        for (e0, e1), m in zip(evs, miss):  # a copy kernel ran between the events of each step
+            assert e0.elapsed_time(e1) > 0.0 or sum(m) == 0
         runs.append((keep.cpu().numpy(), bts, miss, [t.slot_page.copy() for t in sl.tables],
                      [t.hand for t in sl.tables], [x.cpu().numpy() for x in sl.slots]))
-    a, b = runs
-    assert a[2] == b[2], "misses per layer"
-    assert all(np.array_equal(x, y) for x, y in zip(a[1], b[1])), "block tables"
-    assert all(np.array_equal(x, y) for x, y in zip(a[3], b[3])) and a[4] == b[4], "residency tables"
-    assert all(np.array_equal(x, y) for x, y in zip(a[5], b[5])), "slot contents"
-    assert np.array_equal(a[0], b[0]), "attention outputs"
+    a = runs[0]
+    for b in runs[1:]:
+        assert a[2] == b[2], "misses per layer"
+        assert all(np.array_equal(x, y) for x, y in zip(a[1], b[1])), "block tables"
+        assert all(np.array_equal(x, y) for x, y in zip(a[3], b[3])) and a[4] == b[4], "residency tables"
+        assert all(np.array_equal(x, y) for x, y in zip(a[5], b[5])), "slot contents"
+        assert np.array_equal(a[0], b[0]), "attention outputs"
     assert sum(sum(m) for m in a[2]) > 0
 
 
