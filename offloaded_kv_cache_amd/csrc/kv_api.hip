@@ -8,6 +8,7 @@
 // the step rules (hits pinned first, misses placed in selection order, ref set
 // on insert) are the textbook algorithm and are documented in kvcache.h.
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -173,6 +174,8 @@ int kv_append_quantize_timed(const kv_shape* shape, const void* k, const void* v
   if (n_tokens < 0 || start_pos < 0) return fail(KV_EINVAL, "negative n_tokens or start_pos");
   if (n_tokens == 0) return ok();
   if (!k || !v || !block_table || !pool) return fail(KV_EINVAL, "NULL buffer");
+  if (n_tokens > INT64_MAX - start_pos)  // (so that start_pos + n_tokens below cannot overflow)
+    return fail(KV_EINVAL, "start_pos + n_tokens overflows");
   if (n_table < 1 || start_pos + n_tokens > (int64_t)n_table * kPageTokens)
     return fail(KV_EINVAL, "tokens [%lld, %lld) do not fit %d pages of 256", (long long)start_pos,
                 (long long)(start_pos + n_tokens), n_table);
@@ -622,6 +625,8 @@ int kv_page_key_sums(const kv_shape* shape, const void* k, int64_t n_tokens, int
   if (!k || !sums || !reps) return fail(KV_EINVAL, "NULL buffer");
   if (!aligned(k, 2) || !aligned(sums, 8) || !aligned(reps, 2))
     return fail(KV_EALIGN, "misaligned buffer (k: 2 B, sums: 8 B, reps: 2 B)");
+  if (n_tokens > INT64_MAX - start_pos)  // (so that start_pos + n_tokens below cannot overflow)
+    return fail(KV_EINVAL, "start_pos + n_tokens overflows");
   if ((start_pos + n_tokens - 1) / kPageTokens >= n_pages_cap)
     return fail(KV_EINVAL, "tokens up to position %lld need more than %lld pages of sums",
                 (long long)(start_pos + n_tokens - 1), (long long)n_pages_cap);

@@ -146,6 +146,18 @@ def test_abi_argument_errors_enqueue_nothing():
     # a token range past the block table
     r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), 300, 0, P(16), 1, P(256), 4, None, None)
     assert r == N.KV_EINVAL and "do not fit" in N.last_error()
+    # a start position so large that start_pos + n_tokens would wrap past INT64_MAX (a wrapped
+    # sum would pass the range check and send the kernel far outside the block table)
+    big = (1 << 63) - 1
+    for n in (1, 2, 300):
+        r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), n, big, P(16), 1, P(256), 4, None, None)
+        assert r == N.KV_EINVAL and "overflows" in N.last_error()
+        r = N.lib.kv_page_key_sums(C.byref(s), P(16), n, big, P(256), P(256), 1 << 40, None)
+        assert r == N.KV_EINVAL and "overflows" in N.last_error()
+    r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), 1, big - 1, P(16), 1, P(256), 4, None, None)
+    assert r == N.KV_EINVAL and "do not fit" in N.last_error()
+    r = N.lib.kv_page_key_sums(C.byref(s), P(16), 300, 256 * 4 - 299, P(256), P(256), 4, None)
+    assert r == N.KV_EINVAL and "pages of sums" in N.last_error()
     # misaligned pool
     r = N.lib.kv_append_quantize(C.byref(s), P(16), P(16), 10, 0, P(16), 1, P(258), 4, None, None)
     assert r == N.KV_EALIGN
