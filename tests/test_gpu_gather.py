@@ -208,3 +208,43 @@ def test_overlapped_streaming_equals_serial(gpu, fmt):
             sub = Sequence(34, layer, 0, n_sel * 256, fmt, k=k, v=v)
             assert_close(results[1][st, layer][None], oracle_out(q[st, layer].cpu().numpy(), [sub], fmt),
                          what=f"step {st} layer {layer}")
+
+
+def test_gather_layers_beyond_one_launch(gpu):
+    """A kv_gather_pages_layers call with more copies (96) and block-table entries (256) than
+    one launch carries is split into several launches; it leaves the same tables, slots and
+    block tables as kv_gather_pages per layer, and the timed form's events span all of its
+    launches. Pages are random bytes (the copy is verbatim)."""
+    s = K.shape("int8")
+    pb = K.page_bytes(s)
+    L, n_pages, n_slots, n_sel = 5, 80, 64, 64  # 320 entries, 320 copies at the first step
+    rng = np.random.default_rng(71)
+    host = [torch.from_numpy(rng.integers(0, 256, n_pages * pb, dtype=np.uint8)).pin_memory() for _ in range(L)]
+    sels = [np.stack([rng.permutation(n_pages)[:n_sel].astype(np.int32) for _ in range(L)]) for _ in range(3)]
+    stream = torch.cuda.current_stream()
+    runs = []
+    for timed in (False, True):
+        sl = K.streaming.StreamedLayers(s, L, n_slots, n_pages, n_sel, gpu)
+        miss, bts = [], []
+        for st in range(3):
+            if timed:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                m = sl.gather_layers(sels[st], host, stream, events=ev)
+                torch.cuda.synchronize()
+                assert ev[0].elapsed_time(ev[1]) > 0.0
+            else:
+                m = np.array([sl.gather(layer, sels[st][layer], host[layer], stream) for layer in range(L)])
+            miss.append(m.tolist())
+            bts.append(sl.block_table_all.cpu().numpy().copy())
+        torch.cuda.synchronize()
+        runs.append((miss, bts, [t.slot_page.copy() for t in sl.tables], [x.cpu() for x in sl.slots]))
+        # every selected page of the last step sits in its slot
+        for layer in range(L):
+            for i in range(0, n_sel, 7):
+                slot, page = int(bts[-1][layer, i]), int(sels[-1][layer, i])
+                assert torch.equal(runs[-1][3][layer][slot * pb:(slot + 1) * pb], host[layer][page * pb:(page + 1) * pb])
+    a, b = runs
+    assert a[0] == b[0] and sum(a[0][0]) == L * n_sel, "misses per layer"
+    assert all(np.array_equal(x, y) for x, y in zip(a[1], b[1])), "block tables"
+    assert all(np.array_equal(x, y) for x, y in zip(a[2], b[2])), "residency tables"
+    assert all(torch.equal(x, y) for x, y in zip(a[3], b[3])), "slot contents"
