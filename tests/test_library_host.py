@@ -166,6 +166,17 @@ def test_abi_argument_errors_enqueue_nothing():
     r = N.lib.kv_decode_attention(C.byref(s), P(256), 1, P(256), 16, P(256), 16, P(256), 4096, 0.0625,
                                   P(256), P(256), need - 1, 0, None)
     assert r == N.KV_ESMALL
+    # the timed multi-layer gather: nothing to do records nothing and succeeds; its
+    # arguments are checked as the untimed call's are
+    t1 = K.Residency(4, 10)
+    tabs = (N.KVResidency * 1)(t1.c)
+    one = np.array([1], np.int32)
+    r = N.lib.kv_gather_pages_layers_timed(C.byref(s), 1, tabs, one.ctypes.data_as(P), 0, None, None,
+                                           None, None, None, None, None)
+    assert r == 0
+    r = N.lib.kv_gather_pages_layers_timed(C.byref(s), 1, tabs, one.ctypes.data_as(P), 1, None, None,
+                                           P(256), None, None, None, None)
+    assert r == N.KV_EINVAL and t1.slot_page.tolist() == [-1] * 4
     # a gather selection larger than the slot pool
     t = K.Residency(2, 10)
     sel = np.array([1, 2, 3], np.int32)
